@@ -1,0 +1,425 @@
+"""CPU oracle for CRISP sparse-prefill attention.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product path (the HIP library and its
+Python binding) never calls it and shares no code with it.
+
+Everything here is plain NumPy in float64 on the exact values of the inputs
+(bf16 inputs are upcast exactly), written to be checked by eye against the
+pages it follows:
+
+* [CRISP §2]   CRISP paper, "problem" paragraph: sparse attention restricted to
+               an index set S through a mask M_S (0 on S, -inf elsewhere), and
+               FlexPrefill's background (proxy attention on a representative
+               query subset, vertical = column, slash = diagonal scores, PE
+               "flattened, sorted, accumulated" until mass >= gamma).
+* [CRISP §3.2] C_struct: proxy mass on the sink window (first w_sink keys) and
+               the recency window (last w_local keys); route to Vertical-Slash
+               iff C_struct >= tau.
+* [CRISP §4]   noise floor: the first and last blocks are always kept, mu is
+               the mean residual mass over the other N_b - 2 blocks, a block is
+               kept iff its mass exceeds alpha * mu; both directions (vertical
+               = column means, slash = diagonal means) are thresholded
+               separately and unioned.
+* [rcap.io summary, per-head pseudo-code] the explicit formulas:
+               A_hat = softmax(Q_lastblock K^T / sqrt(d));
+               C_struct = A_hat[:, sink + recency].sum() / b;
+               p = block_pool(colmean), block_pool(diagmean);
+               mu = max(1 - p[0] - p[-1], 0) / (N_blocks - 2);
+               S = {j : p_j > alpha mu};  PE: gamma_cumsum(pool(Q), pool(K), 0.95).
+
+Readings where the pages are silent (each is repeated in the design notes):
+causal mask inside the proxy; C_struct over the union of the two windows;
+column/diagonal means divide by b (all b proxy rows, masked entries count 0);
+diagonal offset o = q_r - j at token level, bin k = offsets [kb, (k+1)b);
+slash bin k selects key block qb - k for query block qb; every list holds the
+anchor blocks 0 and qb; PE pools every query block, softmaxes each pooled row
+over its causal key blocks and cuts the flattened causal matrix globally
+against gamma * sum(P), ties broken by lower flat (row-major) index, plus the
+two anchors per row; the min-budget top-up takes the largest remaining score,
+ties to the lower index.
+
+Decision arithmetic (route, mu, threshold) is spelled out in float32 in a
+fixed order so that, given the GPU's float32 scores, the oracle's decisions are
+the exact ones the GPU must reproduce.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+FLT_MIN = np.float32(np.finfo(np.float32).tiny)
+TIE_REL = 1e-6
+
+
+# =============================================================== stage 1: proxy attention
+
+def proxy_attention(q_last: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """A_hat = causal softmax(Q_last K^T / sqrt(d)) for the last query block.
+
+    [rcap.io pseudo-code, first line; CRISP §2 "representative query subset"].
+    q_last: [b, d] (rows are the queries at positions n-b .. n-1), k: [n, d].
+    Returns A_hat [b, n] in float64; row r is a softmax over keys j <= n-b+r.
+    """
+    b, d = q_last.shape
+    n = k.shape[0]
+    s = (q_last.astype(np.float64) @ k.astype(np.float64).T) / math.sqrt(d)
+    pos = n - b + np.arange(b)
+    s[np.arange(n)[None, :] > pos[:, None]] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def vertical_scores(A: np.ndarray, blk: int) -> np.ndarray:
+    """p^v: column means of A_hat, pooled into key blocks by summation [CRISP §4]."""
+    b, n = A.shape
+    a_v = A.sum(axis=0) / b
+    return a_v.reshape(n // blk, blk).sum(axis=1)
+
+
+def slash_scores(A: np.ndarray, blk: int) -> np.ndarray:
+    """p^s: diagonal means of A_hat, pooled into offset bins by summation [CRISP §4].
+
+    Diagonal o holds the entries (r, q_r - o), q_r = n - b + r; a_s[o] is their
+    sum divided by b; bin k gathers offsets [k*blk, (k+1)*blk).
+    """
+    b, n = A.shape
+    a_s = np.zeros(n)
+    for r in range(b):
+        q = n - b + r
+        a_s[:q + 1] += A[r, q::-1]          # A[r, q - o] for o = 0..q
+    a_s /= b
+    return a_s.reshape(n // blk, blk).sum(axis=1)
+
+
+def c_struct(A: np.ndarray, w_sink: int, w_local: int) -> float:
+    """Structural mass on the sink and recency windows [CRISP §3.2; rcap.io pseudo-code].
+
+    Sum of A_hat over the union of columns [0, w_sink) and [n - w_local, n),
+    divided by the number of proxy rows b.
+    """
+    b, n = A.shape
+    cols = np.zeros(n, bool)
+    cols[:min(w_sink, n)] = True
+    cols[max(n - w_local, 0):] = True
+    return float(A[:, cols].sum() / b)
+
+
+def proxy_literal(q_last, k, blk, w_sink, w_local):
+    """The same three quantities by explicit loops over every (r, j); tiny n only.
+
+    A second, independent transcription used to pin the vectorised version.
+    """
+    b, d = q_last.shape
+    n = k.shape[0]
+    A = np.zeros((b, n))
+    for r in range(b):
+        q = n - b + r
+        logits = [sum(float(q_last[r, t]) * float(k[j, t]) for t in range(d)) / math.sqrt(d) for j in range(q + 1)]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        z = sum(w)
+        for j in range(q + 1):
+            A[r, j] = w[j] / z
+    pv = [0.0] * (n // blk)
+    ps = [0.0] * (n // blk)
+    cs = 0.0
+    for r in range(b):
+        q = n - b + r
+        for j in range(q + 1):
+            pv[j // blk] += A[r, j] / b
+            ps[(q - j) // blk] += A[r, j] / b
+            if j < w_sink or j >= n - w_local:
+                cs += A[r, j] / b
+    return A, np.array(pv), np.array(ps), cs
+
+
+# =============================================================== stage 2: routing
+
+def route_decision(c: np.float32, tau: float) -> bool:
+    """Vertical-Slash iff C_struct >= tau, compared in float32 [CRISP §3.2]."""
+    return bool(np.float32(c) >= np.float32(tau))
+
+
+def route_tie(c: float, tau: float) -> bool:
+    return abs(float(c) - float(tau)) <= TIE_REL * abs(float(tau))
+
+
+# =============================================================== stage 3a: Vertical-Slash selection
+
+def noise_floor_f32(p: np.ndarray) -> np.float32:
+    """mu = max(1 - p_0 - p_last, 0) / (N_b - 2) in float32, left to right [CRISP §4]."""
+    p = np.asarray(p, np.float32)
+    nb = p.shape[0]
+    t = np.float32(1.0) - p[0]
+    t = np.float32(t - p[nb - 1])
+    t = np.float32(max(t, np.float32(0.0)))
+    return np.float32(t / np.float32(nb - 2))
+
+
+def threshold_f32(p: np.ndarray, alpha: float) -> np.float32:
+    return np.float32(np.float32(alpha) * noise_floor_f32(p))
+
+
+def vs_select_direction(p: np.ndarray, alpha: float, min_blocks: int = 0) -> np.ndarray:
+    """S_d = {k : p_k > alpha mu_d} plus the anchors 0 and N_b - 1 [CRISP §4].
+
+    With min_blocks > |S_d|, the set is topped up with the largest remaining
+    p_k (ties to the lower k) until it holds min_blocks indices.
+    Returns the sorted int array of selected indices.
+    """
+    p = np.asarray(p, np.float32)
+    nb = p.shape[0]
+    thr = threshold_f32(p, alpha)
+    sel = p > thr
+    sel[0] = True
+    sel[nb - 1] = True
+    need = min(min_blocks, nb) - int(sel.sum())
+    if need > 0:
+        rest = np.flatnonzero(~sel)
+        order = sorted(rest, key=lambda i: (-float(p[i]), int(i)))
+        sel[np.array(order[:need], dtype=int)] = True
+    return np.flatnonzero(sel)
+
+
+def vs_ties(p: np.ndarray, alpha: float) -> np.ndarray:
+    """Indices whose score lies within 1e-6 relative of the threshold."""
+    p = np.asarray(p, np.float32)
+    thr = float(threshold_f32(p, alpha))
+    band = TIE_REL * max(thr, float(FLT_MIN))
+    return np.flatnonzero(np.abs(p.astype(np.float64) - thr) <= band)
+
+
+def vs_block_lists(sv: np.ndarray, ss: np.ndarray, nb: int) -> list:
+    """Key-block list of every query block for a Vertical-Slash head.
+
+    list(qb) = sorted unique ({kb in S_v : kb <= qb} U {qb - k : k in S_s, k <= qb} U {0, qb})
+    [CRISP §2: "S_v U S_s plus the first and last blocks"; §4: union of the two
+    directions].
+    """
+    out = []
+    sv = np.asarray(sv)
+    ss = np.asarray(ss)
+    for qb in range(nb):
+        s = set(int(x) for x in sv[sv <= qb])
+        s |= set(int(qb - x) for x in ss[ss <= qb])
+        s |= {0, qb}
+        out.append(np.array(sorted(s), dtype=np.int64))
+    return out
+
+
+# =============================================================== stage 3b: Pooled-Estimation selection
+
+def block_means(x: np.ndarray, blk: int) -> np.ndarray:
+    """Mean of every block of blk consecutive rows."""
+    n, d = x.shape
+    return x.astype(np.float64).reshape(n // blk, blk, d).mean(axis=1)
+
+
+def pe_probabilities(q: np.ndarray, k: np.ndarray, blk: int) -> np.ndarray:
+    """Pooled estimate: causal row softmax of pool(Q) pool(K)^T / sqrt(d).
+
+    [rcap.io pseudo-code gamma_cumsum(pool(Q), pool(K)); CRISP §2 "applying
+    softmax after pooling both queries and keys"].  Returns P [N_b, N_b] with
+    zeros above the diagonal.
+    """
+    d = q.shape[1]
+    qm = block_means(q, blk)
+    km = block_means(k, blk)
+    L = (qm @ km.T) / math.sqrt(d)
+    nb = L.shape[0]
+    L[np.triu(np.ones((nb, nb), bool), 1)] = -np.inf
+    L -= L.max(axis=1, keepdims=True)
+    e = np.exp(L)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def pe_cut(P: np.ndarray, gamma: float):
+    """Global gamma-cumsum over the flattened causal pooled matrix [CRISP §2, PE path].
+
+    Entries (qb, kb <= qb) are ordered by descending P, ties by ascending
+    row-major flat index; the shortest prefix whose float64 sum reaches
+    gamma * sum(P) is kept; gamma >= 1 keeps everything.  The anchors (qb, 0)
+    and (qb, qb) of every row are then added.
+    Returns (mask [N_b, N_b] bool, info dict with the cut position and mass).
+    """
+    P = np.asarray(P, np.float64)
+    nb = P.shape[0]
+    qi, ki = np.tril_indices(nb)
+    vals = P[qi, ki]
+    flat = qi * nb + ki
+    total = float(vals.sum())
+    order = np.lexsort((flat, -vals))
+    mask = np.zeros((nb, nb), bool)
+    if gamma >= 1.0:
+        kstar = vals.size
+        target = total
+        csum = np.cumsum(vals[order])
+    else:
+        target = gamma * total
+        csum = np.cumsum(vals[order])
+        kstar = int(np.searchsorted(csum, target, side="left")) + 1
+        kstar = min(kstar, vals.size)
+    take = order[:kstar]
+    mask[qi[take], ki[take]] = True
+    mask[np.arange(nb), 0] = True
+    mask[np.arange(nb), np.arange(nb)] = True
+    info = dict(kstar=kstar, target=target, total=total,
+                prefix=float(csum[kstar - 1]) if kstar > 0 else 0.0,
+                prefix_before=float(csum[kstar - 2]) if kstar > 1 else 0.0,
+                cut_value=float(vals[order[kstar - 1]]) if kstar > 0 else 0.0,
+                next_value=float(vals[order[kstar]]) if kstar < vals.size else -1.0)
+    return mask, info
+
+
+def pe_tie(info: dict) -> bool:
+    """True when the cut sits within 1e-6 relative of gamma*T, or the value at
+    the cut equals its neighbour to 1e-6 relative (so the order of equal
+    values decides)."""
+    t = info["target"]
+    if t <= 0:
+        return False
+    near = abs(info["prefix"] - t) <= TIE_REL * t or abs(info["prefix_before"] - t) <= TIE_REL * t
+    cv, nv = info["cut_value"], info["next_value"]
+    same = nv >= 0 and abs(cv - nv) <= TIE_REL * max(cv, 1e-300)
+    return bool(near or same)
+
+
+def mask_to_lists(mask: np.ndarray) -> list:
+    return [np.flatnonzero(mask[qb, :qb + 1]).astype(np.int64) for qb in range(mask.shape[0])]
+
+
+def lists_to_csr(per_head_lists: list):
+    """[[list per qb] per head] -> (row_ptr [H*N_b + 1], col_idx) in head-major order."""
+    counts = [len(l) for lists in per_head_lists for l in lists]
+    row_ptr = np.zeros(len(counts) + 1, np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col = np.concatenate([l for lists in per_head_lists for l in lists]) if counts else np.zeros(0, np.int64)
+    return row_ptr, col
+
+
+def dense_lists(nb: int) -> list:
+    return [np.arange(qb + 1, dtype=np.int64) for qb in range(nb)]
+
+
+# =============================================================== stage 4: attention
+
+def attention_block_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, qb: int, kblocks, blk: int) -> np.ndarray:
+    """Rows of query block qb attending causally to the listed key blocks.
+
+    O_i = sum_{j in J_i} softmax_j(q_i . k_j / sqrt(d)) v_j with
+    J_i = {j <= i : block(j) in list}  [CRISP §2, mask M_S; exact softmax on
+    the selected blocks].  An empty J_i gives a zero row.
+    """
+    d = q.shape[1]
+    rows = np.arange(qb * blk, (qb + 1) * blk)
+    kb = np.asarray(sorted(int(x) for x in kblocks), dtype=np.int64)
+    if kb.size == 0:
+        return np.zeros((blk, v.shape[1]))
+    cols = (kb[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+    s = (q[rows].astype(np.float64) @ k[cols].astype(np.float64).T) / math.sqrt(d)
+    s[cols[None, :] > rows[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    out = np.zeros((blk, v.shape[1]))
+    ok = np.isfinite(m[:, 0])
+    e = np.exp(s[ok] - m[ok])
+    out[ok] = (e @ v[cols].astype(np.float64)) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def block_sparse_attention(q, k, v, lists, blk):
+    """Whole-head block-sparse causal attention, one query block at a time."""
+    return np.concatenate([attention_block_rows(q, k, v, qb, lists[qb], blk) for qb in range(len(lists))])
+
+
+def dense_causal_attention(q, k, v):
+    """softmax(q k^T / sqrt(d) + causal mask) v, the all-blocks special case."""
+    n, d = q.shape
+    s = (q.astype(np.float64) @ k.astype(np.float64).T) / math.sqrt(d)
+    s[np.triu(np.ones((n, n), bool), 1)] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e @ v.astype(np.float64)) / e.sum(axis=1, keepdims=True)
+
+
+def masked_attention_literal(q, k, v, M):
+    """softmax(q k^T / sqrt(d) + M) v with an explicit n x n mask matrix M
+    (0 where allowed, -inf elsewhere) [CRISP §2 problem statement]; tiny n."""
+    d = q.shape[1]
+    s = (q.astype(np.float64) @ k.astype(np.float64).T) / math.sqrt(d) + M
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for i in range(q.shape[0]):
+        if np.isfinite(s[i]).any():
+            e = np.exp(s[i] - s[i].max())
+            out[i] = e @ v.astype(np.float64) / e.sum()
+    return out
+
+
+def mask_matrix(lists, n, blk):
+    """M_S: 0 on allowed (i, j) (j <= i and block(j) listed for block(i)), -inf elsewhere."""
+    M = np.full((n, n), -np.inf)
+    for qb, kbs in enumerate(lists):
+        for kb in kbs:
+            for i in range(qb * blk, (qb + 1) * blk):
+                for j in range(kb * blk, (kb + 1) * blk):
+                    if j <= i:
+                        M[i, j] = 0.0
+    return M
+
+
+# =============================================================== per-head pipeline
+
+def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, dense_below_n=0):
+    """Stages 1-3 for one query head from its own Q [n, d] and its KV head's K.
+
+    Returns a dict with the float64 scores, the decisions and the per-block
+    lists.  route is 1 (VS), 0 (PE) or -1 (dense fallback: N_b <= 2, or n below
+    the length gate, where mu is undefined or sparsity does not pay).
+    """
+    n = k.shape[0]
+    nb = n // blk
+    out = dict(nb=nb)
+    if nb <= 2 or n < dense_below_n:
+        out.update(route=-1, lists=dense_lists(nb))
+        return out
+    A = proxy_attention(q[n - blk:], k)
+    pv, ps = vertical_scores(A, blk), slash_scores(A, blk)
+    cs = c_struct(A, w_sink, w_local)
+    out.update(pv=pv, ps=ps, c_struct=cs)
+    vs = route_decision(np.float32(cs), tau)
+    out["route"] = 1 if vs else 0
+    if vs:
+        sv = vs_select_direction(pv.astype(np.float32), alpha, min_blocks)
+        ss = vs_select_direction(ps.astype(np.float32), alpha, min_blocks)
+        out.update(sv=sv, ss=ss, lists=vs_block_lists(sv, ss, nb))
+    else:
+        P = pe_probabilities(q, k, blk)
+        mask, info = pe_cut(P, gamma)
+        out.update(P=P, pe_info=info, lists=mask_to_lists(mask))
+    return out
+
+
+def decide_from_scores(route_in, c, pv, ps, P, nb, tau, alpha, gamma, min_blocks=0):
+    """Stages 2-3 given float32 scores computed elsewhere (the GPU's).
+
+    route_in == -1 marks the dense fallback.  Returns (route, sv, ss, lists,
+    info); P is only read for Pooled-Estimation heads.
+    """
+    if route_in == -1:
+        return -1, None, None, dense_lists(nb), None
+    vs = route_decision(np.float32(c), tau)
+    if vs:
+        sv = vs_select_direction(np.asarray(pv, np.float32), alpha, min_blocks)
+        ss = vs_select_direction(np.asarray(ps, np.float32), alpha, min_blocks)
+        return 1, sv, ss, vs_block_lists(sv, ss, nb), None
+    mask, info = pe_cut(np.asarray(P, np.float32).astype(np.float64), gamma)
+    return 0, None, None, mask_to_lists(mask), info
+
+
+def prefill_head(q, k, v, blk=128, w_sink=128, w_local=128, tau=0.3, alpha=1.0, gamma=0.95,
+                 min_blocks=0, dense_below_n=0):
+    """All four stages for one head: selection then block-sparse attention."""
+    sel = select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks, dense_below_n)
+    sel["O"] = block_sparse_attention(q, k, v, sel["lists"], blk)
+    return sel

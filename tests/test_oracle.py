@@ -1,0 +1,331 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- hand-worked cases, closed forms of special cases, invariants that the
+definitions force, brute force on tiny inputs, or a library routine."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import crisp_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ------------------------------------------------------------------ noise floor (hand-worked)
+
+def test_noise_floor_golden_cases():
+    g = json.load(open(os.path.join(GOLD, "noise_floor_cases.json")))
+    for c in g["cases"]:
+        p = np.array(c["p"], np.float32)
+        mu = float(O.noise_floor_f32(p))
+        assert abs(mu - c["mu"]) <= 1e-7, c
+        sel = O.vs_select_direction(p, c["alpha"])
+        assert sel.tolist() == c["selected"], c
+    for c in g["min_blocks_cases"]:
+        p = np.array(c["p"], np.float32)
+        sel = O.vs_select_direction(p, c["alpha"], c["min_blocks"])
+        assert sel.tolist() == c["selected"], c
+
+
+def test_threshold_monotone_in_alpha():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        p = rng.dirichlet(np.full(40, 0.3)).astype(np.float32)
+        prev = None
+        for a in [0.25, 0.5, 1.0, 1.25, 1.5, 2.0, 4.0]:
+            s = set(O.vs_select_direction(p, a).tolist())
+            if prev is not None:
+                assert s <= prev
+            prev = s
+
+
+def test_residual_rescale_keeps_selection_and_lowers_mu():
+    """Moving mass from the non-anchor blocks onto the sink block scales every
+    residual score and mu by the same factor: mu drops and the selected set is
+    unchanged (the floor follows the sink, CRISP §4)."""
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        nb = 50
+        p = rng.dirichlet(np.full(nb, 0.5))
+        p[0] += 0.2
+        p /= p.sum()
+        resid = 1 - p[0] - p[-1]
+        f = 0.5                                   # half of the residual moves to the sink
+        q = p.copy()
+        q[1:-1] *= f
+        q[0] += resid * (1 - f)
+        mu_p = O.noise_floor_f32(p.astype(np.float32))
+        mu_q = O.noise_floor_f32(q.astype(np.float32))
+        assert mu_q < mu_p
+        # away from float32 rounding at the threshold the sets agree
+        thr = float(O.threshold_f32(p.astype(np.float32), 1.0))
+        if np.min(np.abs(p[1:-1] - thr)) > 1e-5 * thr:
+            assert O.vs_select_direction(p.astype(np.float32), 1.0).tolist() == \
+                O.vs_select_direction(q.astype(np.float32), 1.0).tolist()
+
+
+def test_vs_lists_golden():
+    g = json.load(open(os.path.join(GOLD, "vs_lists_case.json")))
+    lists = O.vs_block_lists(np.array(g["sv"]), np.array(g["ss"]), g["nb"])
+    assert [l.tolist() for l in lists] == g["lists"]
+
+
+def test_vs_lists_properties():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        nb = int(rng.integers(3, 60))
+        sv = np.sort(rng.choice(nb, size=int(rng.integers(0, nb)), replace=False))
+        ss = np.sort(rng.choice(nb, size=int(rng.integers(0, nb)), replace=False))
+        lists = O.vs_block_lists(sv, ss, nb)
+        for qb, l in enumerate(lists):
+            assert l[0] == 0 and l[-1] == qb and np.all(np.diff(l) > 0)
+            # membership by brute force over every key block
+            for kb in range(qb + 1):
+                want = kb in (0, qb) or kb in set(sv.tolist()) or (qb - kb) in set(ss.tolist())
+                assert (kb in set(l.tolist())) == want
+
+
+# ------------------------------------------------------------------ proxy attention
+
+def test_proxy_rows_are_softmax_and_scores_sum_to_one():
+    n, b, d = 1024, 128, 64
+    q, k = _rand((b, d), 1), _rand((n, d), 2)
+    A = O.proxy_attention(q, k)
+    assert np.allclose(A.sum(1), 1.0, atol=1e-12)
+    pos = n - b + np.arange(b)
+    assert np.all(A[np.arange(n)[None, :] > pos[:, None]] == 0)
+    assert abs(O.vertical_scores(A, b).sum() - 1) < 1e-12
+    assert abs(O.slash_scores(A, b).sum() - 1) < 1e-12
+
+
+def test_proxy_matches_literal_loops():
+    n, b, d = 24, 4, 8
+    q, k = _rand((b, d), 11), _rand((n, d), 12)
+    A0, pv0, ps0, cs0 = O.proxy_literal(q, k, blk=4, w_sink=4, w_local=4)
+    A = O.proxy_attention(q, k)
+    assert np.allclose(A, A0, atol=1e-13)
+    assert np.allclose(O.vertical_scores(A, 4), pv0, atol=1e-13)
+    assert np.allclose(O.slash_scores(A, 4), ps0, atol=1e-13)
+    assert abs(O.c_struct(A, 4, 4) - cs0) < 1e-13
+    # uneven windows (not multiples of the block) through the same literal definition
+    _, _, _, cs1 = O.proxy_literal(q, k, blk=4, w_sink=3, w_local=6)
+    assert abs(O.c_struct(A, 3, 6) - cs1) < 1e-13
+
+
+def test_proxy_zero_query_closed_form():
+    """Q = 0: every proxy row is uniform over its q_r + 1 causal keys."""
+    n, b, d = 1024, 128, 32
+    A = O.proxy_attention(np.zeros((b, d)), _rand((n, d), 4))
+    nb = n // b
+    q = n - b + np.arange(b)
+    pv_want = np.array([sum(max(0, min(q[r], (kb + 1) * b - 1) - kb * b + 1) / (q[r] + 1) for r in range(b)) / b
+                        for kb in range(nb)])
+    assert np.allclose(O.vertical_scores(A, b), pv_want, atol=1e-13)
+    # diagonal o is present on row r iff o <= q_r, each with weight 1/(q_r+1)
+    a_s = np.array([sum(1.0 / (q[r] + 1) for r in range(b) if o <= q[r]) / b for o in range(n)])
+    assert np.allclose(O.slash_scores(A, b), a_s.reshape(nb, b).sum(1), atol=1e-13)
+    cs_want = sum((b + r + 1) / (q[r] + 1) for r in range(b)) / b
+    assert abs(O.c_struct(A, b, b) - cs_want) < 1e-13
+
+
+def test_proxy_one_hot_limit():
+    """A single overwhelming key takes all the mass: p^v and C_struct become indicators."""
+    n, b, d = 1024, 128, 16
+    q = np.zeros((b, d)); q[:, 0] = 1.0
+    k = np.zeros((n, d))
+    j = 300
+    k[j, 0] = 1e4
+    A = O.proxy_attention(q, k)
+    pv = O.vertical_scores(A, b)
+    want = np.zeros(n // b); want[j // b] = 1.0
+    assert np.allclose(pv, want, atol=1e-12)
+    ps = O.slash_scores(A, b)
+    # row r puts its mass on offset q_r - j
+    a_s = np.zeros(n)
+    for r in range(b):
+        a_s[n - b + r - j] += 1.0 / b
+    assert np.allclose(ps, a_s.reshape(-1, b).sum(1), atol=1e-12)
+    assert O.c_struct(A, b, b) < 1e-12
+
+
+def test_c_struct_equals_anchor_blocks_of_vertical_score():
+    """With w_sink = w_local = b the anchor windows are exactly the first and last block (CRISP §4)."""
+    n, b, d = 2048, 128, 64
+    A = O.proxy_attention(_rand((b, d), 8), _rand((n, d), 9))
+    pv = O.vertical_scores(A, b)
+    assert abs(O.c_struct(A, b, b) - (pv[0] + pv[-1])) < 1e-13
+
+
+def test_route_rule_and_monotone_in_tau():
+    assert O.route_decision(np.float32(0.3), 0.3)            # ">=": equality routes to VS
+    assert not O.route_decision(np.nextafter(np.float32(0.3), np.float32(0)), 0.3)
+    cs = np.random.default_rng(2).uniform(0, 1, 100).astype(np.float32)
+    prev = None
+    for tau in [0.1, 0.2, 0.3, 0.5, 0.8]:
+        s = {i for i, c in enumerate(cs) if O.route_decision(c, tau)}
+        if prev is not None:
+            assert s <= prev
+        prev = s
+
+
+# ------------------------------------------------------------------ pooled estimation
+
+def test_pe_probabilities_block_constant_inputs():
+    """Inputs constant within each block pool to those constants, so P is the
+    causal row softmax of the small constant matrix (scipy)."""
+    from scipy.special import softmax
+    nb, blk, d = 5, 4, 8
+    qc, kc = _rand((nb, d), 21), _rand((nb, d), 22)
+    q = np.repeat(qc, blk, axis=0)
+    k = np.repeat(kc, blk, axis=0)
+    P = O.pe_probabilities(q, k, blk)
+    L = qc @ kc.T / math.sqrt(d)
+    for qb in range(nb):
+        assert np.allclose(P[qb, :qb + 1], softmax(L[qb, :qb + 1]), atol=1e-14)
+        assert np.all(P[qb, qb + 1:] == 0)
+
+
+def test_pe_cut_brute_force_minimum_cardinality():
+    """The gamma-cumsum prefix solves FlexPrefill's dual problem (CRISP §2):
+    among all subsets of causal entries whose mass reaches gamma*T it has the
+    fewest elements, and no subset of that size carries more mass."""
+    rng = np.random.default_rng(13)
+    for trial in range(40):
+        nb = int(rng.integers(2, 5))                       # at most 10 causal entries
+        P = O.pe_probabilities(rng.standard_normal((nb * 2, 4)) * 3, rng.standard_normal((nb * 2, 4)) * 3, 2)
+        gamma = float(rng.uniform(0.3, 0.99))
+        qi, ki = np.tril_indices(nb)
+        vals = P[qi, ki]
+        T = vals.sum()
+        best = None
+        for r in range(1, vals.size + 1):
+            masses = [sum(vals[list(c)]) for c in itertools.combinations(range(vals.size), r)]
+            ok = [m for m in masses if m >= gamma * T]
+            if ok:
+                best = (r, max(ok))
+                break
+        _, info = O.pe_cut(P, gamma)
+        assert info["kstar"] == best[0]
+        assert abs(info["prefix"] - best[1]) < 1e-12
+
+
+def test_pe_cut_gamma_limits_and_monotone():
+    rng = np.random.default_rng(17)
+    nb = 12
+    P = O.pe_probabilities(rng.standard_normal((nb * 4, 8)), rng.standard_normal((nb * 4, 8)), 4)
+    full, _ = O.pe_cut(P, 1.0)
+    assert np.array_equal(full, np.tril(np.ones((nb, nb), bool)))
+    prev = None
+    for gamma in [0.1, 0.5, 0.8, 0.9, 0.95, 0.99, 1.0]:
+        m, _ = O.pe_cut(P, gamma)
+        assert np.all(m[np.arange(nb), 0]) and np.all(m[np.arange(nb), np.arange(nb)])
+        assert not np.any(np.triu(m, 1))
+        if prev is not None:
+            assert np.all(m[prev])
+        prev = m
+
+
+def test_pe_cut_ties_go_to_lower_flat_index():
+    """Two equal non-anchor entries (3,1) and (3,2) straddle the cut: the one
+    with the lower row-major flat index is taken.  Sorted masses by hand:
+    1, .5, .5, .4, .4, .4, .3, .2, .15, .15 (T = 4); gamma*T = 3.8 is first
+    reached by the ninth entry."""
+    P = np.array([[1.0, 0, 0, 0],
+                  [0.5, 0.5, 0, 0],
+                  [0.4, 0.2, 0.4, 0],
+                  [0.3, 0.15, 0.15, 0.4]])
+    m, info = O.pe_cut(P, 0.95)
+    assert info["kstar"] == 9
+    assert m[3, 1] and not m[3, 2]
+    assert O.pe_tie(info)            # the cut value equals its neighbour: reported as a tie
+    m2, info2 = O.pe_cut(P, 0.9)     # 3.6 reached by the eighth entry (0.2 at (2,1))
+    assert info2["kstar"] == 8 and m2[2, 1] and not m2[3, 1] and not m2[3, 2]
+
+
+# ------------------------------------------------------------------ attention
+
+def _sdpa(q, k, v):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True)[0, 0].numpy()
+
+
+def test_dense_attention_matches_library_sdpa():
+    n, d = 256, 32
+    q, k, v = _rand((n, d), 31), _rand((n, d), 32), _rand((n, d), 33)
+    assert np.allclose(O.dense_causal_attention(q, k, v), _sdpa(q, k, v), atol=1e-12)
+
+
+def test_all_blocks_selected_is_dense_attention():
+    n, d, blk = 512, 32, 64
+    q, k, v = _rand((n, d), 41), _rand((n, d), 42), _rand((n, d), 43)
+    o = O.block_sparse_attention(q, k, v, O.dense_lists(n // blk), blk)
+    assert np.allclose(o, _sdpa(q, k, v), atol=1e-12)
+
+
+def test_block_sparse_matches_explicit_mask_matrix():
+    n, d, blk = 96, 8, 8
+    rng = np.random.default_rng(44)
+    q, k, v = _rand((n, d), 45), _rand((n, d), 46), _rand((n, d), 47)
+    nb = n // blk
+    lists = []
+    for qb in range(nb):
+        s = {kb for kb in range(qb + 1) if rng.random() < 0.4}
+        if qb % 3:                       # some rows without the diagonal block, one empty row
+            s |= {qb}
+        lists.append(sorted(s))
+    lists[2] = []
+    o = O.block_sparse_attention(q, k, v, lists, blk)
+    M = O.mask_matrix(lists, n, blk)
+    assert np.allclose(o, O.masked_attention_literal(q, k, v, M), atol=1e-12)
+
+
+def test_attention_is_causal():
+    n, d, blk = 256, 16, 32
+    q, k, v = _rand((n, d), 51), _rand((n, d), 52), _rand((n, d), 53)
+    lists = O.dense_lists(n // blk)
+    o = O.block_sparse_attention(q, k, v, lists, blk)
+    i = 150
+    k2, v2 = k.copy(), v.copy()
+    k2[i + 1:] += 5.0
+    v2[i + 1:] -= 3.0
+    o2 = O.block_sparse_attention(q, k2, v2, lists, blk)
+    assert np.allclose(o[:i + 1], o2[:i + 1], atol=1e-14)
+    assert not np.allclose(o[i + 1:], o2[i + 1:])
+
+
+# ------------------------------------------------------------------ whole head on generated inputs
+
+def test_select_head_on_tiny_generated_layer():
+    """Tiny fp32 case: head 0 (sink + recency + 3 needles) routes to VS and keeps
+    its needle blocks; head 1 (diffuse) routes to PE."""
+    from workloads import synth
+    spec = synth.make_spec(synth.CONFIGS[0])
+    cfg = spec.cfg
+    Q, K, V = synth.generate(spec)
+    r0 = O.select_head(Q[0].astype(np.float64), K[0].astype(np.float64), 128, 128, 128, cfg.tau, cfg.alpha, cfg.gamma)
+    assert r0["route"] == 1 and r0["c_struct"] >= cfg.tau
+    for nb_id in spec.needle_blocks[0]:
+        assert nb_id in set(r0["sv"].tolist())
+    r1 = O.select_head(Q[1].astype(np.float64), K[1].astype(np.float64), 128, 128, 128, cfg.tau, cfg.alpha, cfg.gamma)
+    assert r1["route"] == 0
+    # decisions recomputed from float32-rounded scores agree with the float64 run
+    rt, sv, ss, lists, _ = O.decide_from_scores(1, np.float32(r0["c_struct"]), r0["pv"], r0["ps"], None,
+                                                cfg.nb, cfg.tau, cfg.alpha, cfg.gamma)
+    assert rt == 1 and np.array_equal(sv, r0["sv"]) and np.array_equal(ss, r0["ss"])
+
+
+def test_dense_fallback_cases():
+    q, k = _rand((256, 16), 61), _rand((256, 16), 62)
+    r = O.select_head(q, k, 128, 128, 128, 0.3, 1.0, 0.95)
+    assert r["route"] == -1 and [l.tolist() for l in r["lists"]] == [[0], [0, 1]]
+    q, k = _rand((512, 16), 63), _rand((512, 16), 64)
+    r = O.select_head(q, k, 128, 128, 128, 0.3, 1.0, 0.95, dense_below_n=1024)
+    assert r["route"] == -1
