@@ -1,0 +1,12 @@
+"""CRISP sparse-prefill attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in libcrisp.so (hand-written HIP kernels behind the C
+ABI in include/crisp.h); this package only marshals PyTorch tensors into it.
+"""
+from .api import (BLOCK, CrispError, CrispParams, Selection, attn_workspace_bytes, col_capacity,
+                  crisp_dense_attn, crisp_prefill, crisp_select, crisp_sparse_attn, lib, make_shape,
+                  new_selection, select_workspace_bytes, workspace_bytes)
+
+__all__ = ["BLOCK", "CrispError", "CrispParams", "Selection", "attn_workspace_bytes", "col_capacity",
+           "crisp_dense_attn", "crisp_prefill", "crisp_select", "crisp_sparse_attn", "lib", "make_shape",
+           "new_selection", "select_workspace_bytes", "workspace_bytes"]

@@ -1,0 +1,46 @@
+// Shared device-side definitions for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crisp {
+
+constexpr int BLK = 128;    // block size b (tokens per block), also the attention tile edge
+constexpr int HD = 128;     // head dim d
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// log2(e): softmax is evaluated as exp2(x * log2(e)) on the hardware exp unit.
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// 32x32 MFMA output layout (v_mfma_f32_32x32x{16 bf16, 2 f32}): lane l, register i
+// holds row 8*(i/4) + 4*(l/32) + (i%4), column l%32.
+__device__ __forceinline__ int mfma32_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+}  // namespace crisp

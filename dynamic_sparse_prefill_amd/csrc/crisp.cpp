@@ -1,0 +1,263 @@
+// C ABI of libcrisp: argument validation, workspace planning and launch
+// sequencing.  Everything here runs on the host; nothing allocates, nothing
+// synchronises, and every check happens before the first launch.
+#include "../../include/crisp.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "launch.h"
+
+using namespace crisp;
+
+namespace {
+constexpr int BLK = 128;   // block size b: pooling, selection and attention tile edge
+constexpr int HD = 128;    // head dim d
+}  // namespace
+
+namespace {
+
+constexpr int64_t MAX_NB = 32768;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_shape(const crisp_shape* s) {
+  if (!s) return CRISP_E_ARG;
+  if (s->dtype != CRISP_BF16 && s->dtype != CRISP_FP32) return CRISP_E_UNSUPPORTED;
+  if (s->d != HD) return CRISP_E_UNSUPPORTED;
+  if (s->n <= 0 || s->n % BLK) return CRISP_E_ARG;
+  if (s->n / BLK > MAX_NB) return CRISP_E_UNSUPPORTED;
+  if (s->hq <= 0 || s->hkv <= 0 || s->hq % s->hkv) return CRISP_E_ARG;
+  const int64_t st[8] = {s->sq_h, s->sq_n, s->sk_h, s->sk_n, s->sv_h, s->sv_n, s->so_h, s->so_n};
+  for (int64_t x : st)
+    if (x < 0 || x % 8) return CRISP_E_ARG;
+  if (s->sq_n < HD || s->sk_n < HD || s->sv_n < HD || s->so_n < HD) return CRISP_E_ARG;
+  // worst-case list size must fit int32 row pointers
+  const int64_t nb = s->n / BLK;
+  if ((int64_t)s->hq * nb * (nb + 1) / 2 > 0x7fffffffLL) return CRISP_E_UNSUPPORTED;
+  return CRISP_OK;
+}
+
+int check_params(const crisp_shape* s, const crisp_params* p) {
+  if (!p) return CRISP_E_ARG;
+  if (p->block != BLK) return CRISP_E_UNSUPPORTED;
+  if (p->sink < 0 || p->local < 0 || p->sink > s->n || p->local > s->n) return CRISP_E_ARG;
+  if (!(p->tau >= 0.f) || !(p->alpha >= 0.f) || !isfinite(p->tau) || !isfinite(p->alpha)) return CRISP_E_ARG;
+  if (!(p->gamma > 0.f) || !(p->gamma <= 1.f)) return CRISP_E_ARG;
+  if (p->min_blocks < 0 || p->dense_below_n < 0 || p->flags != 0) return CRISP_E_ARG;
+  return CRISP_OK;
+}
+
+Strides strides(const crisp_shape* s) {
+  return Strides{s->sq_h, s->sq_n, s->sk_h, s->sk_n, s->sv_h, s->sv_n, s->so_h, s->so_n};
+}
+
+int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
+
+// Selection workspace layout (every region 256-byte aligned).
+struct SelectLayout {
+  size_t stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, total;
+};
+
+SelectLayout select_layout(const crisp_shape* s) {
+  const int64_t nb = s->n / BLK, hq = s->hq, hkv = s->hkv, nch = proxy_chunks((int)nb);
+  SelectLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.stats = take(hq * nch * BLK * 8);
+  L.rowstat = take(hq * BLK * 8);
+  L.tiles = take(hq * nb * 16);
+  L.pv = take(hq * nb * 4);
+  L.ps = take(hq * nb * 4);
+  L.sv = take(hq * nb * 4);
+  L.ss = take(hq * nb * 4);
+  L.nv = take(hq * 4);
+  L.ns = take(hq * 4);
+  L.kbar = take(hkv * nb * HD * 4);
+  L.qbar = take(hq * nb * HD * 4);
+  L.P = take(hq * tri(nb) * 4);
+  L.hcnt = take(hq * 3 * PE_BUCKETS * 4);
+  L.hmass = take(hq * 3 * PE_BUCKETS * 8);
+  L.cut = take(hq * pe_cut_state_bytes());
+  L.eqrow = take(hq * nb * 4);
+  L.counts = take(hq * nb * 4);
+  L.total = o;
+  return L;
+}
+
+size_t attn_ws(const crisp_shape* s) {
+  const size_t esz = s->dtype == CRISP_FP32 ? 4 : 2;
+  return align256((size_t)s->hkv * (size_t)s->n * HD * esz);
+}
+
+bool dense_path(const crisp_shape* s, const crisp_params* p) {
+  const int64_t nb = s->n / BLK;
+  return nb <= 2 || (p->dense_below_n > 0 && s->n < p->dense_below_n);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_E_HIP; }
+
+int check_qkv(const crisp_shape* s, const void* q, const void* k, const void* v, const void* o) {
+  if (!q || !k || !aligned16(q) || !aligned16(k)) return CRISP_E_ARG;
+  if (v && !aligned16(v)) return CRISP_E_ARG;
+  if (o && !aligned16(o)) return CRISP_E_ARG;
+  (void)s;
+  return CRISP_OK;
+}
+
+int validate_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p,
+                    const crisp_selection* out, const void* ws, size_t ws_bytes) {
+  int st = check_shape(s);
+  if (st) return st;
+  if ((st = check_params(s, p))) return st;
+  if ((st = check_qkv(s, q, k, nullptr, nullptr))) return st;
+  if (!out || !out->route || !out->c_struct || !out->row_ptr || !out->col_idx) return CRISP_E_ARG;
+  if (out->col_capacity < crisp_col_capacity(s)) return CRISP_E_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255)) return CRISP_E_ARG;
+  if (ws_bytes < select_layout(s).total) return CRISP_E_WORKSPACE;
+  return CRISP_OK;
+}
+
+int validate_attn(const crisp_shape* s, const void* q, const void* k, const void* v, void* o, const void* ws,
+                  size_t ws_bytes) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!v || !o) return CRISP_E_ARG;
+  if ((st = check_qkv(s, q, k, v, o))) return st;
+  if (!ws || ((uintptr_t)ws & 255)) return CRISP_E_ARG;
+  if (ws_bytes < attn_ws(s)) return CRISP_E_WORKSPACE;
+  return CRISP_OK;
+}
+
+int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
+               void* ws, hipStream_t stream) {
+  const SelectLayout L = select_layout(s);
+  char* w = (char*)ws;
+  const int nb = (int)(s->n / BLK);
+  const int fp32 = s->dtype == CRISP_FP32;
+  const bool dense = dense_path(s, p);
+  const Strides st = strides(s);
+  if (!dense) {
+    hipError_t e = launch_proxy(fp32, q, k, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, w + L.stats,
+                                w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
+    if (e != hipSuccess) return CRISP_E_HIP;
+  }
+  SelectBufs b;
+  b.tiles = w + L.tiles;
+  b.kbar = (const float*)(w + L.kbar);
+  b.pv = (float*)(w + L.pv);
+  b.ps = (float*)(w + L.ps);
+  b.qbar = (float*)(w + L.qbar);
+  b.P = out->pe_prob ? out->pe_prob : (float*)(w + L.P);
+  b.sv = (int32_t*)(w + L.sv);
+  b.nv = (int32_t*)(w + L.nv);
+  b.ss = (int32_t*)(w + L.ss);
+  b.ns = (int32_t*)(w + L.ns);
+  b.hcnt = (uint32_t*)(w + L.hcnt);
+  b.hmass = (unsigned long long*)(w + L.hmass);
+  b.cut = w + L.cut;
+  b.eqrow = (int32_t*)(w + L.eqrow);
+  b.counts = (int32_t*)(w + L.counts);
+  b.route = out->route;
+  b.c_struct = out->c_struct;
+  b.row_ptr = out->row_ptr;
+  b.col_idx = out->col_idx;
+  b.pv_out = out->pv;
+  b.ps_out = out->ps;
+  b.sv_out = out->sv;
+  b.nv_out = out->nv;
+  b.ss_out = out->ss;
+  b.ns_out = out->ns;
+  return status_of(launch_select(fp32, dense, q, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, p->tau,
+                                 p->alpha, p->gamma, p->min_blocks, b, stream));
+}
+
+int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
+             const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream) {
+  const int nb = (int)(s->n / BLK);
+  const int fp32 = s->dtype == CRISP_FP32;
+  hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, stream);
+  if (e != hipSuccess) return CRISP_E_HIP;
+  return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, nb, s->hq, s->hkv, strides(s),
+                                    stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t crisp_select_workspace_bytes(const crisp_shape* shape, const crisp_params* params) {
+  if (check_shape(shape) || check_params(shape, params)) return 0;
+  return select_layout(shape).total;
+}
+
+size_t crisp_attn_workspace_bytes(const crisp_shape* shape) {
+  if (check_shape(shape)) return 0;
+  return attn_ws(shape);
+}
+
+size_t crisp_workspace_bytes(const crisp_shape* shape, const crisp_params* params) {
+  if (check_shape(shape) || check_params(shape, params)) return 0;
+  return select_layout(shape).total + attn_ws(shape);
+}
+
+int64_t crisp_col_capacity(const crisp_shape* shape) {
+  if (check_shape(shape)) return 0;
+  return (int64_t)shape->hq * tri(shape->n / BLK);
+}
+
+int crisp_select(const crisp_shape* shape, const void* q, const void* k, const crisp_params* params,
+                 crisp_selection* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_select(shape, q, k, params, out, workspace, workspace_bytes);
+  if (st) return st;
+  return run_select(shape, q, k, params, out, workspace, stream);
+}
+
+int crisp_sparse_attn(const crisp_shape* shape, const void* q, const void* k, const void* v,
+                      const crisp_selection* sel, void* o, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const int st = validate_attn(shape, q, k, v, o, workspace, workspace_bytes);
+  if (st) return st;
+  if (!sel || !sel->row_ptr || !sel->col_idx) return CRISP_E_ARG;
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, workspace, stream);
+}
+
+int crisp_dense_attn(const crisp_shape* shape, const void* q, const void* k, const void* v, void* o,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_attn(shape, q, k, v, o, workspace, workspace_bytes);
+  if (st) return st;
+  return run_attn(shape, q, k, v, nullptr, nullptr, true, o, workspace, stream);
+}
+
+int crisp_prefill(const crisp_shape* shape, const void* q, const void* k, const void* v,
+                  const crisp_params* params, crisp_selection* sel, void* o, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const size_t sel_bytes = crisp_select_workspace_bytes(shape, params);
+  if (!sel_bytes) return check_params(shape, params) ? check_params(shape, params) : CRISP_E_ARG;
+  if (workspace_bytes < sel_bytes + attn_ws(shape)) return CRISP_E_WORKSPACE;
+  st = validate_select(shape, q, k, params, sel, workspace, sel_bytes);
+  if (st) return st;
+  char* attn_ws_ptr = (char*)workspace + sel_bytes;
+  st = validate_attn(shape, q, k, v, o, attn_ws_ptr, workspace_bytes - sel_bytes);
+  if (st) return st;
+  st = run_select(shape, q, k, params, sel, workspace, stream);
+  if (st) return st;
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream);
+}
+
+const char* crisp_status_string(int status) {
+  switch (status) {
+    case CRISP_OK: return "ok";
+    case CRISP_E_ARG: return "invalid argument";
+    case CRISP_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case CRISP_E_WORKSPACE: return "workspace or list capacity too small";
+    case CRISP_E_HIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal launchers (C++ linkage) called by the C-ABI layer in crisp.cpp.
+// Every launcher only enqueues work on `s` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crisp {
+
+struct Strides { int64_t q_h, q_n, k_h, k_n, v_h, v_n, o_h, o_n; };
+
+// ---- attention (attn.hip)
+hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv,
+                              int64_t sv_h, int64_t sv_n, hipStream_t s);
+hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
+                            const int32_t* row_ptr, const int32_t* col_idx, int nb, int hq, int hkv,
+                            const Strides& st, hipStream_t s);
+
+// ---- proxy (proxy.hip)
+int proxy_chunks(int nb);
+hipError_t launch_proxy(int fp32, const void* Q, const void* K, int64_t n, int nb, int hq, int hkv,
+                        const Strides& st, int w_sink, int w_local,
+                        void* stats /*[hq*nchunk*128] float2*/, void* rowstat /*[hq*128] float2*/,
+                        void* tiles /*[hq*nb] float4*/, float* kbar /*[hkv*nb*128]*/, hipStream_t s);
+
+// ---- selection (select.hip)
+struct PeCut;                       // per-head radix-select state (select.hip)
+size_t pe_cut_state_bytes();
+constexpr int PE_BUCKETS = 2048;    // histogram size of one radix pass
+
+struct SelectBufs {
+  // inputs from the proxy
+  const void* tiles;
+  const float* kbar;
+  // scratch
+  float *pv, *ps, *qbar, *P;
+  int32_t *sv, *nv, *ss, *ns;
+  uint32_t* hcnt;  unsigned long long* hmass;  void* cut;
+  int32_t *eqrow, *counts;
+  // caller outputs
+  int32_t* route; float* c_struct; int32_t *row_ptr, *col_idx;
+  float *pv_out, *ps_out; int32_t *sv_out, *nv_out, *ss_out, *ns_out;
+};
+
+hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,
+                         const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
+                         int min_blocks, const SelectBufs& b, hipStream_t s);
+
+}  // namespace crisp

@@ -1,0 +1,586 @@
+// Routing and index selection (gfx950).
+//
+//  vs_select   per head: p^v, p^s from the proxy tile sums, C_struct, route
+//              (VS iff C_struct >= tau) [CRISP §3.2]; for VS heads the noise
+//              floor mu_d = max(1 - p_0 - p_last, 0)/(N_b - 2) and the sets
+//              S_d = {k : p_k > alpha mu_d} U {0, N_b - 1} per direction
+//              [CRISP §4], compacted in ascending order; optional min budget.
+//  pool_q      block means of Q for Pooled-Estimation heads.
+//  pe_logits   pooled logits  Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb.
+//  pe_softmax  causal row softmax of the pooled logits [CRISP §2, PE path].
+//  pe_hist/    global gamma-cut over the flattened causal matrix: a radix
+//  pe_scan     select on the float32 bit pattern (11+11+10 bits, three
+//              passes) with per-bucket mass in 2^-46 fixed point, so the sums
+//              are exact integers and order-independent.  Entries are taken in
+//              descending value, ties by ascending row-major flat index,
+//              until the mass reaches gamma * total.
+//  list_*      per (head, query block) ascending key-block lists in one CSR:
+//              VS rows = {S_v <= qb} U {qb - S_s} U {0, qb}, PE rows = the
+//              selected entries of the row plus (qb, 0) and (qb, qb), dense
+//              rows = 0..qb.
+//
+// The decision arithmetic (route, mu, threshold) is written with explicit
+// round-to-nearest float32 operations in a fixed order so that it can be
+// reproduced exactly on the host from the same float32 scores.
+#include "common.h"
+#include "launch.h"
+
+namespace crisp {
+
+struct PeCut {
+  unsigned long long total, target, need, above_mass, take, eq_cnt;
+  uint32_t prefix, vstar;
+  int32_t active;
+  int32_t pad;
+};
+size_t pe_cut_state_bytes() { return sizeof(PeCut); }
+
+constexpr double FX_SCALE = 70368744177664.0;  // 2^46
+__device__ __forceinline__ unsigned long long fx_mass(uint32_t bits) {
+  return (unsigned long long)((double)__uint_as_float(bits) * FX_SCALE);
+}
+
+// ------------------------------------------------------------------ block helpers (256 threads)
+
+__device__ int block_excl_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int x = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += x;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+// ------------------------------------------------------------------ VS selection
+
+__device__ void compact_flags(const uint8_t* flag, int nb, int32_t* out, int* count, int* sh) {
+  const int tid = threadIdx.x;
+  const int per = (nb + 255) / 256;
+  const int a = min(nb, tid * per), b = min(nb, a + per);
+  int c = 0;
+  for (int k = a; k < b; ++k) c += flag[k];
+  int tot;
+  int pos = block_excl_scan(c, sh, &tot);
+  for (int k = a; k < b; ++k)
+    if (flag[k]) out[pos++] = k;
+  if (tid == 0) *count = tot;
+  __syncthreads();
+}
+
+// top up the set to `want` members with the largest remaining scores, ties to the lower index
+__device__ void top_up(uint8_t* flag, const float* p, int nb, int want, float* shv, int* shi) {
+  const int tid = threadIdx.x;
+  int have = 0;
+  for (int k = tid; k < nb; k += 256) have += flag[k];
+  shi[tid] = have;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) shi[tid] += shi[tid + o];
+    __syncthreads();
+  }
+  have = shi[0];
+  __syncthreads();
+  for (; have < want; ++have) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int k = tid; k < nb; k += 256)
+      if (!flag[k] && (p[k] > bv || (p[k] == bv && k < bi))) { bv = p[k]; bi = k; }
+    shv[tid] = bv;
+    shi[tid] = bi;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) {
+        const float v2 = shv[tid + o];
+        const int i2 = shi[tid + o];
+        if (v2 > shv[tid] || (v2 == shv[tid] && i2 < shi[tid])) { shv[tid] = v2; shi[tid] = i2; }
+      }
+      __syncthreads();
+    }
+    if (tid == 0 && shi[0] < nb) flag[shi[0]] = 1;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void vs_select_kernel(
+    const float4* __restrict__ tiles, int64_t n, int nb, int w_sink, int w_local, float tau, float alpha,
+    int min_blocks, int dense, int32_t* __restrict__ route, float* __restrict__ c_struct, float* __restrict__ pv,
+    float* __restrict__ ps, int32_t* __restrict__ sv, int32_t* __restrict__ nv, int32_t* __restrict__ ss,
+    int32_t* __restrict__ ns, float* pv_out, float* ps_out) {
+  extern __shared__ uint8_t flag[];  // nb bytes
+  __shared__ int shi[256];
+  __shared__ float shv[256];
+  __shared__ int s_route;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (dense) {
+    if (tid == 0) { route[h] = -1; c_struct[h] = 0.f; nv[h] = 0; ns[h] = 0; }
+    return;
+  }
+  const float4* T = tiles + (int64_t)h * nb;
+  float* PV = pv + (int64_t)h * nb;
+  float* PS = ps + (int64_t)h * nb;
+  const float inv_b = 1.f / BLK;  // exact power of two
+  for (int k = tid; k < nb; k += 256) {
+    const float4 t = T[k];
+    const float v = __fmul_rn(__fadd_rn(t.x, t.y), inv_b);
+    const float lo = T[nb - 1 - k].x;
+    const float up = (k <= nb - 2) ? T[nb - 2 - k].y : 0.f;
+    const float sl = __fmul_rn(__fadd_rn(lo, up), inv_b);
+    PV[k] = v;
+    PS[k] = sl;
+    if (pv_out) pv_out[(int64_t)h * nb + k] = v;
+    if (ps_out) ps_out[(int64_t)h * nb + k] = sl;
+  }
+  if (tid == 0) {
+    float c = 0.f;
+    for (int kb = 0; kb < nb; ++kb) {
+      const int64_t j0 = (int64_t)kb * BLK;
+      if (j0 < w_sink || j0 + BLK > n - w_local) c = __fadd_rn(c, T[kb].z);
+    }
+    c = __fmul_rn(c, inv_b);
+    c_struct[h] = c;
+    const int r = (c >= tau) ? 1 : 0;
+    route[h] = r;
+    s_route = r;
+  }
+  __syncthreads();
+  if (s_route != 1) {
+    if (tid == 0) { nv[h] = 0; ns[h] = 0; }
+    return;
+  }
+  const float denom = (float)(nb - 2);
+  for (int dir = 0; dir < 2; ++dir) {
+    const float* p = dir == 0 ? PV : PS;
+    float t = __fsub_rn(1.f, p[0]);
+    t = __fsub_rn(t, p[nb - 1]);
+    t = fmaxf(t, 0.f);
+    const float mu = __fdiv_rn(t, denom);
+    const float thr = __fmul_rn(alpha, mu);
+    for (int k = tid; k < nb; k += 256) flag[k] = (p[k] > thr) || k == 0 || k == nb - 1;
+    __syncthreads();
+    if (min_blocks > 0) top_up(flag, p, nb, min(min_blocks, nb), shv, shi);
+    compact_flags(flag, nb, (dir == 0 ? sv : ss) + (int64_t)h * nb, (dir == 0 ? nv : ns) + h, shi);
+  }
+}
+
+// ------------------------------------------------------------------ PE: pooled Q
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, const int32_t* __restrict__ route,
+                                                     float* __restrict__ qbar, int nb, int64_t sq_h, int64_t sq_n) {
+  constexpr int E = 16 / sizeof(T);         // elements per 16-byte load
+  constexpr int CPR = HD / E;               // 16-byte chunks per row
+  constexpr int RG = 256 / CPR;             // row groups
+  __shared__ float red[RG][HD];
+  const int qb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (route[h] != 0) return;
+  const int ch = tid % CPR, rg = tid / CPR;
+  const T* base = Q + (int64_t)h * sq_h + (int64_t)qb * BLK * sq_n + ch * E;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int r = rg; r < BLK; r += RG) {
+    const T* p = base + (int64_t)r * sq_n;
+    const uint4 raw = *(const uint4*)p;
+    const T* v = (const T*)&raw;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += to_f32(v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[rg][ch * E + e] = acc[e];
+  __syncthreads();
+  if (tid < HD) {
+    float s = 0.f;
+    for (int q = 0; q < RG; ++q) s += red[q][tid];
+    qbar[((int64_t)h * nb + qb) * HD + tid] = s * (1.f / BLK);
+  }
+}
+
+// ------------------------------------------------------------------ PE: pooled logits (64 x 64 tiles)
+
+__device__ __forceinline__ int64_t tri(int64_t qb) { return qb * (qb + 1) / 2; }
+
+__global__ __launch_bounds__(256) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                        const int32_t* __restrict__ route, float* __restrict__ P,
+                                                        int nb, int hq, int hkv, float scale) {
+  constexpr int TP = 64, PP = HD + 1;
+  __shared__ float sq[TP * PP];
+  __shared__ float sk[TP * PP];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  if (route[h] != 0) return;
+  // linear tile id -> (ti, tj), tj <= ti
+  const int lin = blockIdx.x;
+  int ti = (int)((sqrtf(8.f * lin + 1.f) - 1.f) * 0.5f);
+  while ((int64_t)(ti + 1) * (ti + 2) / 2 <= lin) ++ti;
+  while ((int64_t)ti * (ti + 1) / 2 > lin) --ti;
+  const int tj = lin - ti * (ti + 1) / 2;
+  const int kvh = h / (hq / hkv);
+  const float* qs = qbar + ((int64_t)h * nb + ti * TP) * HD;
+  const float* ks = kbar + ((int64_t)kvh * nb + tj * TP) * HD;
+  for (int e = tid; e < TP * HD; e += 256) {
+    const int r = e / HD, d = e % HD;
+    sq[r * PP + d] = (ti * TP + r < nb) ? qs[(int64_t)r * HD + d] : 0.f;
+    sk[r * PP + d] = (tj * TP + r < nb) ? ks[(int64_t)r * HD + d] : 0.f;
+  }
+  __syncthreads();
+  const int r0 = 4 * (tid / 16), c0 = 4 * (tid % 16);
+  float acc[4][4] = {};
+  for (int d = 0; d < HD; ++d) {
+    float a[4], b[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { a[x] = sq[(r0 + x) * PP + d]; b[x] = sk[(c0 + x) * PP + d]; }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+  }
+  float* Ph = P + (int64_t)h * tri(nb);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int qb = ti * TP + r0 + x;
+    if (qb >= nb) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int kb = tj * TP + c0 + y;
+      if (kb <= qb) Ph[tri(qb) + kb] = acc[x][y] * scale;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ PE: row softmax
+
+__global__ __launch_bounds__(256) void pe_softmax_kernel(const int32_t* __restrict__ route, float* __restrict__ P,
+                                                         int nb) {
+  __shared__ float sh[256];
+  const int qb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (route[h] != 0) return;
+  float* row = P + (int64_t)h * tri(nb) + tri(qb);
+  const int len = qb + 1;
+  float mx = -INFINITY;
+  for (int k = tid; k < len; k += 256) mx = fmaxf(mx, row[k]);
+  sh[tid] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) sh[tid] = fmaxf(sh[tid], sh[tid + o]);
+    __syncthreads();
+  }
+  mx = sh[0];
+  __syncthreads();
+  float s = 0.f;
+  for (int k = tid; k < len; k += 256) s += expf(row[k] - mx);
+  sh[tid] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) sh[tid] += sh[tid + o];
+    __syncthreads();
+  }
+  const float inv = 1.f / sh[0];
+  for (int k = tid; k < len; k += 256) row[k] = expf(row[k] - mx) * inv;
+}
+
+// ------------------------------------------------------------------ PE: radix select of the gamma cut
+
+constexpr int PE_SLICE = 32768;  // entries per histogram work-group
+
+__global__ void pe_cut_init_kernel(const int32_t* __restrict__ route, PeCut* __restrict__ cut,
+                                   uint32_t* __restrict__ hcnt, unsigned long long* __restrict__ hmass,
+                                   float gamma) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  uint32_t* c = hcnt + (int64_t)h * 3 * PE_BUCKETS;
+  unsigned long long* m = hmass + (int64_t)h * 3 * PE_BUCKETS;
+  for (int i = tid; i < 3 * PE_BUCKETS; i += blockDim.x) { c[i] = 0; m[i] = 0; }
+  if (tid == 0) {
+    PeCut z = {};
+    z.active = (route[h] == 0 && gamma < 1.f) ? 1 : 0;
+    cut[h] = z;
+  }
+}
+
+__host__ __device__ constexpr int pe_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__host__ __device__ constexpr int pe_width(int pass) { return pass == 2 ? 10 : 11; }
+
+template <int PASS>
+__global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
+                                                      uint32_t* __restrict__ hcnt,
+                                                      unsigned long long* __restrict__ hmass, int64_t total) {
+  __shared__ uint32_t sc[PE_BUCKETS];
+  __shared__ unsigned long long sm[PE_BUCKETS];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  if (!cut[h].active) return;
+  constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
+  constexpr uint32_t mask = (1u << width) - 1;
+  constexpr int hi = shift + width;
+  const uint32_t prefix = cut[h].prefix;
+  for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
+  __syncthreads();
+  const uint32_t* bits = (const uint32_t*)(P + (int64_t)h * total);
+  const int64_t a = (int64_t)blockIdx.x * PE_SLICE, b = min(total, a + PE_SLICE);
+  for (int64_t e = a + tid; e < b; e += 256) {
+    const uint32_t x = bits[e];
+    if (PASS > 0 && (x >> hi) != (prefix >> hi)) continue;
+    const uint32_t bk = (x >> shift) & mask;
+    atomicAdd(&sc[bk], 1u);
+    atomicAdd(&sm[bk], fx_mass(x));
+  }
+  __syncthreads();
+  uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  for (int i = tid; i < PE_BUCKETS; i += 256)
+    if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
+}
+
+template <int PASS>
+__global__ void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
+                               const unsigned long long* __restrict__ hmass, float gamma) {
+  const int h = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  PeCut c = cut[h];
+  if (!c.active) return;
+  constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
+  const uint32_t* hc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  const unsigned long long* hm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  const int nbk = 1 << width;
+  if (PASS == 0) {
+    unsigned long long t = 0;
+    for (int i = 0; i < nbk; ++i) t += hm[i];
+    c.total = t;
+    c.target = (unsigned long long)ceil((double)gamma * (double)t);
+    if (c.target == 0) c.target = 1;
+    c.need = c.target;
+  }
+  unsigned long long acc = 0;
+  int sel = 0;
+  for (int i = nbk - 1; i >= 0; --i) {
+    if (acc + hm[i] >= c.need) { sel = i; break; }
+    acc += hm[i];
+    sel = i;
+  }
+  c.need -= acc;
+  c.above_mass += acc;
+  c.prefix |= (uint32_t)sel << shift;
+  if (PASS == 2) {
+    c.vstar = c.prefix;
+    c.eq_cnt = hc[sel];
+    const unsigned long long fv = fx_mass(c.vstar);
+    unsigned long long take = fv ? (c.need + fv - 1) / fv : c.eq_cnt;
+    c.take = take < c.eq_cnt ? take : c.eq_cnt;
+  }
+  cut[h] = c;
+}
+
+// count of entries equal to the cut value per row, then an exclusive scan per head (only when the cut
+// splits a run of equal values)
+__global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
+                                                          int32_t* __restrict__ eqrow, int nb) {
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qb = blockIdx.x * 4 + w;
+  const PeCut c = cut[h];
+  if (!c.active || c.take >= c.eq_cnt || qb >= nb) return;
+  const uint32_t* row = (const uint32_t*)(P + (int64_t)h * tri(nb) + tri(qb));
+  int cnt = 0;
+  for (int k = lane; k <= qb; k += 64) cnt += (row[k] == c.vstar);
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) eqrow[(int64_t)h * nb + qb] = cnt;
+}
+
+__global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict__ cut, int32_t* __restrict__ eqrow,
+                                                         int nb) {
+  __shared__ int sh[256];
+  const int h = blockIdx.x;
+  const PeCut c = cut[h];
+  if (!c.active || c.take >= c.eq_cnt) return;
+  int32_t* e = eqrow + (int64_t)h * nb;
+  const int per = (nb + 255) / 256;
+  const int a = min(nb, (int)threadIdx.x * per), b = min(nb, a + per);
+  int s = 0;
+  for (int k = a; k < b; ++k) s += e[k];
+  int tot;
+  int base = block_excl_scan(s, sh, &tot);
+  for (int k = a; k < b; ++k) { const int v = e[k]; e[k] = base; base += v; }
+}
+
+// ------------------------------------------------------------------ lists
+
+__device__ __forceinline__ int lane_prefix(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// One wave per (head, query block).  FILL = false writes the row's count,
+// FILL = true writes its ascending key blocks at row_ptr[row].
+template <bool FILL>
+__global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ route,
+                                                   const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
+                                                   const int32_t* __restrict__ ss, const int32_t* __restrict__ ns,
+                                                   const float* __restrict__ P, const PeCut* __restrict__ cut,
+                                                   const int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
+                                                   int nb, int pe_all) {
+  extern __shared__ uint32_t bitmap[];  // 4 waves x ceil(nb/32) words
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qb = blockIdx.x * 4 + w;
+  if (qb >= nb) return;
+  const int64_t row = (int64_t)h * nb + qb;
+  const int r = route[h];
+  int32_t* out = FILL ? col + row_ptr[row] : nullptr;
+  if (r == -1 || (r == 0 && pe_all)) {
+    if (!FILL) { if (lane == 0) counts[row] = qb + 1; }
+    else for (int k = lane; k <= qb; k += 64) out[k] = k;
+    return;
+  }
+  if (r == 0) {
+    const PeCut c = cut[h];
+    const uint32_t* bits = (const uint32_t*)(P + (int64_t)h * tri(nb) + tri(qb));
+    const bool split = c.take < c.eq_cnt;
+    int base = 0;
+    long long eqb = split ? eqrow[row] : 0;
+    for (int k0 = 0; k0 <= qb; k0 += 64) {
+      const int k = k0 + lane;
+      const bool valid = k <= qb;
+      const uint32_t x = valid ? bits[k] : 0u;
+      bool sel = valid && ((x > c.vstar) || k == 0 || k == qb || (!split && x == c.vstar));
+      if (split) {  // the cut splits a run of equal values: take them in flat order
+        const bool eq = valid && x == c.vstar;
+        const unsigned long long em = __ballot(eq);
+        if (eq && (unsigned long long)(eqb + lane_prefix(em)) < c.take) sel = true;
+        eqb += __popcll(em);
+      }
+      const unsigned long long m = __ballot(sel);
+      if (FILL && sel) out[base + lane_prefix(m)] = k;
+      base += __popcll(m);
+    }
+    if (!FILL && lane == 0) counts[row] = base;
+    return;
+  }
+  // Vertical-Slash: set bits in a per-wave bitmap, then read them out in order
+  const int nw = (nb + 31) / 32;
+  uint32_t* bm = bitmap + w * nw;
+  const int words = qb / 32 + 1;
+  for (int i = lane; i < words; i += 64) bm[i] = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int32_t* svh = sv + (int64_t)h * nb;
+  const int32_t* ssh = ss + (int64_t)h * nb;
+  const int cv = nv[h], cs = ns[h];
+  for (int i = lane; i < cv; i += 64) {
+    const int k = svh[i];
+    if (k <= qb) atomicOr(&bm[k >> 5], 1u << (k & 31));
+  }
+  for (int i = lane; i < cs; i += 64) {
+    const int k = ssh[i];
+    if (k <= qb) { const int kb = qb - k; atomicOr(&bm[kb >> 5], 1u << (kb & 31)); }
+  }
+  if (lane == 0) {
+    atomicOr(&bm[0], 1u);
+    atomicOr(&bm[qb >> 5], 1u << (qb & 31));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int wi = w0 + lane;
+    uint32_t word = wi < words ? bm[wi] : 0u;
+    if (wi == qb >> 5) word &= (qb & 31) == 31 ? 0xffffffffu : ((2u << (qb & 31)) - 1u);
+    const int pc = __popc(word);
+    int incl = pc;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (FILL) {
+      int pos = base + incl - pc;
+      while (word) {
+        const int b = __ffs(word) - 1;
+        out[pos++] = wi * 32 + b;
+        word &= word - 1;
+      }
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  if (!FILL && lane == 0) counts[row] = base;
+}
+
+// exclusive scan of the row counts into row_ptr (single work-group of 1024 threads)
+__global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ row_ptr, int64_t rows) {
+  __shared__ long long sh[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (rows + 1023) / 1024;
+  const int64_t a = min(rows, tid * per), b = min(rows, a + per);
+  long long s = 0;
+  for (int64_t i = a; i < b; ++i) s += counts[i];
+  sh[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const long long x = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += x;
+    __syncthreads();
+  }
+  long long base = sh[tid] - s;
+  for (int64_t i = a; i < b; ++i) { row_ptr[i] = (int32_t)base; base += counts[i]; }
+  if (tid == 1023) row_ptr[rows] = (int32_t)sh[1023];
+}
+
+__global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
+                                 const int32_t* __restrict__ ss, const int32_t* __restrict__ ns,
+                                 int32_t* sv_out, int32_t* nv_out, int32_t* ss_out, int32_t* ns_out, int nb) {
+  const int h = blockIdx.x;
+  const int a = nv[h], b = ns[h];
+  if (threadIdx.x == 0) { if (nv_out) nv_out[h] = a; if (ns_out) ns_out[h] = b; }
+  for (int i = threadIdx.x; i < a; i += blockDim.x) if (sv_out) sv_out[(int64_t)h * nb + i] = sv[(int64_t)h * nb + i];
+  for (int i = threadIdx.x; i < b; i += blockDim.x) if (ss_out) ss_out[(int64_t)h * nb + i] = ss[(int64_t)h * nb + i];
+}
+
+// ------------------------------------------------------------------ launcher
+
+hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,
+                         const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
+                         int min_blocks, const SelectBufs& b, hipStream_t s) {
+  vs_select_kernel<<<hq, 256, nb, s>>>((const float4*)b.tiles, n, nb, w_sink, w_local, tau, alpha, min_blocks,
+                                       dense ? 1 : 0, b.route, b.c_struct, b.pv, b.ps, b.sv, b.nv, b.ss, b.ns,
+                                       b.pv_out, b.ps_out);
+  PeCut* cut = (PeCut*)b.cut;
+  const int64_t total = (int64_t)nb * (nb + 1) / 2;
+  const int pe_all = gamma >= 1.f ? 1 : 0;
+  if (!dense) {
+    const dim3 gq(nb, hq);
+    if (fp32)
+      pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
+    else
+      pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
+    const int T = (nb + 63) / 64;
+    pe_logits_kernel<<<dim3(T * (T + 1) / 2, hq), 256, 0, s>>>(b.qbar, b.kbar, b.route, b.P, nb, hq, hkv,
+                                                               1.f / sqrtf((float)HD));
+    pe_softmax_kernel<<<dim3(nb, hq), 256, 0, s>>>(b.route, b.P, nb);
+    pe_cut_init_kernel<<<hq, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
+    const dim3 gh((unsigned)((total + PE_SLICE - 1) / PE_SLICE), hq);
+    pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
+    pe_scan_kernel<0><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
+    pe_scan_kernel<1><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    pe_hist_kernel<2><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
+    pe_scan_kernel<2><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    pe_eq_count_kernel<<<dim3((nb + 3) / 4, hq), 256, 0, s>>>(b.P, cut, b.eqrow, nb);
+    pe_eq_scan_kernel<<<hq, 256, 0, s>>>(cut, b.eqrow, nb);
+  } else {
+    pe_cut_init_kernel<<<hq, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
+  }
+  const dim3 gl((nb + 3) / 4, hq);
+  const size_t bm_bytes = 4 * ((nb + 31) / 32) * sizeof(uint32_t);
+  list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
+                                               b.row_ptr, b.col_idx, nb, pe_all);
+  scan_rows_kernel<<<1, 1024, 0, s>>>(b.counts, b.row_ptr, (int64_t)hq * nb);
+  list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
+                                              b.row_ptr, b.col_idx, nb, pe_all);
+  if (b.sv_out || b.nv_out || b.ss_out || b.ns_out)
+    copy_sets_kernel<<<hq, 256, 0, s>>>(b.sv, b.nv, b.ss, b.ns, b.sv_out, b.nv_out, b.ss_out, b.ns_out, nb);
+  return hipGetLastError();
+}
+
+}  // namespace crisp

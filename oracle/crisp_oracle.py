@@ -273,17 +273,15 @@ def pe_cut(P: np.ndarray, gamma: float):
     return mask, info
 
 
-def pe_tie(info: dict) -> bool:
-    """True when the cut sits within 1e-6 relative of gamma*T, or the value at
-    the cut equals its neighbour to 1e-6 relative (so the order of equal
-    values decides)."""
+def pe_tie(info: dict, rel: float = TIE_REL) -> bool:
+    """True when gamma*T lies within `rel` (relative) of the prefix sum just
+    before or at the cut, i.e. when the summation order of an implementation
+    can move the cut by one entry.  Equal values straddling the cut are not a
+    tie: the lower flat index wins on every implementation."""
     t = info["target"]
     if t <= 0:
         return False
-    near = abs(info["prefix"] - t) <= TIE_REL * t or abs(info["prefix_before"] - t) <= TIE_REL * t
-    cv, nv = info["cut_value"], info["next_value"]
-    same = nv >= 0 and abs(cv - nv) <= TIE_REL * max(cv, 1e-300)
-    return bool(near or same)
+    return bool(abs(info["prefix"] - t) <= rel * t or abs(info["prefix_before"] - t) <= rel * t)
 
 
 def mask_to_lists(mask: np.ndarray) -> list:

@@ -1,0 +1,100 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/crisp.h declares, and its host-side validation rejects bad arguments
+before anything is launched (no GPU work is requested here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_prefill_amd as dsp
+from dynamic_sparse_prefill_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "crisp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(crisp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_exports_agree():
+    names = declared_functions()
+    assert set(names) == set(api.EXPORTS)
+    L = dsp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _shape(n=4096, hq=4, hkv=2, d=128, dtype=0):
+    return api.CrispShape(n, hq, hkv, d, dtype, n * d, d, n * d, d, n * d, d, n * d, d)
+
+
+def test_workspace_and_capacity_queries():
+    s = _shape()
+    p = dsp.CrispParams()
+    nb = 4096 // 128
+    assert dsp.col_capacity(s) == 4 * nb * (nb + 1) // 2
+    ws = dsp.select_workspace_bytes(s, p)
+    assert ws > 4 * nb * (nb + 1) // 2 * 4          # holds the pooled matrix of every head
+    assert dsp.attn_workspace_bytes(s) == 2 * 4096 * 128 * 2
+    assert dsp.workspace_bytes(s, p) == ws + dsp.attn_workspace_bytes(s)
+    # invalid shapes and parameters report zero
+    assert dsp.select_workspace_bytes(_shape(d=64), p) == 0
+    assert dsp.col_capacity(_shape(n=1000)) == 0
+    bad = dsp.CrispParams(gamma=0.0)
+    assert dsp.workspace_bytes(s, bad) == 0
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(d=64), -2), (dict(n=1000), -1), (dict(hq=3, hkv=2), -1), (dict(dtype=7), -2), (dict(n=0), -1),
+])
+def test_select_rejects_bad_shapes(mut, status):
+    kw = dict(n=4096, hq=4, hkv=2, d=128, dtype=0)
+    kw.update(mut)
+    s = _shape(**kw)
+    sel = api.CrispSelectionC()
+    st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(dsp.CrispParams().c()), C.byref(sel), 256, 1 << 30, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("mut", [dict(gamma=1.5), dict(gamma=0.0), dict(tau=-1.0), dict(alpha=float("nan")),
+                                 dict(sink=-1), dict(min_blocks=-2), dict(flags=1), dict(local=10 ** 9)])
+def test_select_rejects_bad_params(mut):
+    p = dsp.CrispParams(**mut)
+    s = _shape()
+    sel = api.CrispSelectionC(16, 16, 16, 16, 1 << 40)
+    st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(p.c()), C.byref(sel), 256, 1 << 40, None)
+    assert st == -1
+
+
+def test_select_rejects_block_other_than_128_and_small_buffers():
+    s = _shape()
+    sel = api.CrispSelectionC(16, 16, 16, 16, 1 << 40)
+    st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(dsp.CrispParams(block=64).c()), C.byref(sel), 256,
+                                1 << 40, None)
+    assert st == -2
+    small = api.CrispSelectionC(16, 16, 16, 16, 10)
+    st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(dsp.CrispParams().c()), C.byref(small), 256, 1 << 40, None)
+    assert st == -3
+    st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(dsp.CrispParams().c()), C.byref(sel), 256, 1024, None)
+    assert st == -3
+    st = dsp.lib().crisp_select(C.byref(s), 0, 16, C.byref(dsp.CrispParams().c()), C.byref(sel), 256, 1 << 40, None)
+    assert st == -1
+    st = dsp.lib().crisp_select(C.byref(s), 8, 16, C.byref(dsp.CrispParams().c()), C.byref(sel), 256, 1 << 40, None)
+    assert st == -1                                          # misaligned pointer
+
+
+def test_attention_entry_points_validate():
+    s = _shape()
+    L = dsp.lib()
+    assert L.crisp_dense_attn(C.byref(s), 16, 16, 16, 0, 256, 1 << 30, None) == -1
+    assert L.crisp_dense_attn(C.byref(s), 16, 16, 16, 16, 256, 10, None) == -3
+    bad = _shape()
+    bad.sk_n = 100                                          # not a multiple of 8
+    assert L.crisp_dense_attn(C.byref(bad), 16, 16, 16, 16, 256, 1 << 30, None) == -1
+    assert L.crisp_sparse_attn(C.byref(s), 16, 16, 16, None, 16, 256, 1 << 30, None) == -1
+    assert L.crisp_prefill(C.byref(s), 16, 16, 16, C.byref(dsp.CrispParams().c()), None, 16, 256, 1 << 40,
+                           None) == -1
+    assert dsp.api.status_string(-3).startswith("workspace")

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes: the tiny fp32 layer and small bf16 layers are compared in full; the
+Llama / Qwen layers (32k, 128k, 512k) are compared on every routing and
+selection decision and on a seeded sample of query blocks, in the same launch
+configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import crisp_oracle as O
+from workloads import synth
+
+import dynamic_sparse_prefill_amd as dsp
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_layer(spec, Q, K, V, params):
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    o, sel = dsp.crisp_prefill(q, k, v, params, pe_prob=True)
+    torch.cuda.synchronize()
+    return q, k, v, o, sel
+
+
+def _lists_fn(sel, nb):
+    rp, col = P.gpu_lists(sel, None, nb)
+    return lambda h, qb: col[rp[h * nb + qb]: rp[h * nb + qb + 1]]
+
+
+# ------------------------------------------------------------------ tiny fp32 layer, everything in full
+
+def test_tiny_fp32_layer_full():
+    spec = synth.make_spec(synth.CONFIGS[0])
+    cfg = spec.cfg
+    Q, K, V = synth.generate(spec)
+    p = P.params_of(cfg)
+    q, k, v, o, sel = _run_layer(spec, Q, K, V, p)
+    route = sel.route.cpu().numpy()
+    assert route.tolist() == [1, 0], route            # concentrated head -> VS, diffuse -> PE
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+    P.log("[tiny] decisions", rep)
+    assert rep["heads_checked"] == 2
+    P.log("[tiny] score err", P.check_score_fidelity(spec, Q, K, sel, [0, 1], tol=1e-5))
+    P.log("[tiny] PE prob err", P.check_pe_fidelity(spec, Q, K, sel, [1], tol=1e-6))
+    # full outputs, fp32 path: tighter than the bf16 tolerance
+    lists = _lists_fn(sel, cfg.nb)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, lists, [0, 1], range(cfg.nb), max_abs=1e-4, mean_abs=1e-5)
+    P.log(f"[tiny] attention max {mx:.2e} mean {mean:.2e}")
+    # independent decisions (oracle's own float64 scores) agree as well
+    for h in range(2):
+        r = O.select_head(Q[h].astype(np.float64), K[h].astype(np.float64), 128, 128, 128, cfg.tau, cfg.alpha,
+                          cfg.gamma)
+        assert r["route"] == route[h]
+        gl = [lists(h, qb) for qb in range(cfg.nb)]
+        assert all(np.array_equal(a, b) for a, b in zip(gl, r["lists"]))
+    # dense attention of the same engine against the oracle's dense attention
+    od = dsp.crisp_dense_attn(q, k, v)
+    torch.cuda.synchronize()
+    for h in range(2):
+        ref = O.dense_causal_attention(Q[h].astype(np.float64), K[h].astype(np.float64), V[h].astype(np.float64))
+        assert np.abs(od[h].cpu().numpy() - ref).max() < 1e-4
+
+
+# ------------------------------------------------------------------ attention alone, on lists the oracle makes
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_sparse_attention_on_oracle_lists(dtype):
+    cfg = synth.custom_config("lists", 1280, 4, 2, dtype=dtype, seed=11)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    nb = cfg.nb
+    rng = np.random.default_rng(5)
+    per_head = []
+    for h in range(cfg.hq):
+        lists = []
+        for qb in range(nb):
+            s = sorted({kb for kb in range(qb + 1) if rng.random() < 0.5} | ({qb} if (qb + h) % 4 else set()))
+            lists.append(np.array(s, np.int64))
+        per_head.append(lists)
+    per_head[1][3] = np.zeros(0, np.int64)             # an empty row: zero output
+    per_head[2][7] = np.array([7])                     # diagonal only
+    rp, col = O.lists_to_csr(per_head)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    sel = dsp.Selection(torch.zeros(cfg.hq, dtype=torch.int32, device="cuda"),
+                        torch.zeros(cfg.hq, device="cuda"),
+                        torch.from_numpy(rp.astype(np.int32)).cuda(), torch.from_numpy(col.astype(np.int32)).cuda())
+    o = dsp.crisp_sparse_attn(q, k, v, sel)
+    torch.cuda.synchronize()
+    tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-5)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: per_head[h][qb], range(cfg.hq), range(nb),
+                                        *tol)
+    assert torch.all(o[1, 3 * 128:4 * 128] == 0)
+    P.log(f"[lists {dtype}] max {mx:.2e} mean {mean:.2e}")
+
+
+@pytest.mark.parametrize("hq,hkv,n", [(7, 1, 2048), (4, 4, 1152)])
+def test_dense_attention_bf16_full(hq, hkv, n):
+    cfg = synth.custom_config("dense", n, hq, hkv, seed=3)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    o = dsp.crisp_dense_attn(q, k, v)
+    torch.cuda.synchronize()
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: range(qb + 1), range(hq), range(cfg.nb))
+    P.log(f"[dense {hq}/{hkv} n={n}] max {mx:.2e} mean {mean:.2e}")
+
+
+def test_strided_layout_matches_contiguous():
+    """[n, heads, d] storage (token-major) through the stride arguments gives the same result."""
+    cfg = synth.custom_config("strided", 2048, 4, 2, seed=9)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    p = P.params_of(cfg)
+    o1, s1 = dsp.crisp_prefill(q, k, v, p)
+    qt = q.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    kt = k.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    vt = v.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    ot = torch.empty(q.shape[1], q.shape[0], 128, dtype=q.dtype, device="cuda").permute(1, 0, 2)
+    o2, s2 = dsp.crisp_prefill(qt, kt, vt, p, o=ot)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.route, s2.route) and torch.equal(s1.row_ptr, s2.row_ptr)
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ small mixed layers: selection in full
+
+@pytest.mark.parametrize("n,hq,hkv,seed", [(8192, 8, 2, 21), (1664, 7, 1, 22), (384, 2, 1, 23)])
+def test_small_layer_selection_and_output(n, hq, hkv, seed):
+    cfg = synth.custom_config("small", n, hq, hkv, seed=seed, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    p = P.params_of(cfg)
+    q, k, v, o, sel = _run_layer(spec, Q, K, V, p)
+    rep = P.check_decisions(sel, hq, cfg.nb, p)
+    P.log(f"[small n={n}] decisions", rep, "routes", sel.route.cpu().tolist())
+    assert rep["heads_checked"] + rep["pe_exempt"] == hq
+    P.log("[small] score err", P.check_score_fidelity(spec, Q, K, sel, range(hq)))
+    pe = [h for h in range(hq) if sel.route[h].item() == 0]
+    if pe:
+        P.log("[small] PE prob err", P.check_pe_fidelity(spec, Q, K, sel, pe))
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(hq), range(cfg.nb))
+    P.log(f"[small] attention max {mx:.2e} mean {mean:.2e}")
+
+
+def test_dense_fallback_paths():
+    cfg = synth.custom_config("fallback", 256, 2, 1, seed=4)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v, o, sel = _run_layer(spec, Q, K, V, P.params_of(cfg))
+    assert sel.route.cpu().tolist() == [-1, -1]
+    assert sel.row_ptr.cpu().tolist() == [0, 1, 3, 4, 6]
+    P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: range(qb + 1), range(2), range(2))
+    cfg2 = synth.custom_config("gate", 2048, 2, 1, seed=4)
+    spec2 = synth.make_spec(cfg2)
+    Q2, K2, V2 = synth.generate(spec2)
+    _, _, _, o2, sel2 = _run_layer(spec2, Q2, K2, V2, P.params_of(cfg2, dense_below_n=4096))
+    assert sel2.route.cpu().tolist() == [-1, -1]
+    rp = sel2.row_ptr.cpu().numpy()
+    assert np.array_equal(np.diff(rp), np.tile(np.arange(1, 17), 2))
+
+
+def test_parameter_sweep_and_min_blocks():
+    cfg = synth.custom_config("sweep", 8192, 8, 2, seed=31, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k = P.to_device(spec, Q), P.to_device(spec, K)
+    for tau in (0.2, 0.3, 0.5):
+        for alpha in (0.5, 1.0, 2.0):
+            for mb in (0, 8):
+                p = P.params_of(cfg, tau=tau, alpha=alpha, min_blocks=mb)
+                sel = dsp.crisp_select(q, k, p, pe_prob=True)
+                torch.cuda.synchronize()
+                rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+                if mb:
+                    nv = sel.nv.cpu().numpy()[sel.route.cpu().numpy() == 1]
+                    assert np.all(nv >= mb)
+
+
+def test_selection_is_deterministic():
+    cfg = synth.custom_config("det", 16384, 8, 2, seed=41, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k = P.to_device(spec, Q), P.to_device(spec, K)
+    p = P.params_of(cfg)
+    a = dsp.crisp_select(q, k, p, pe_prob=True)
+    b = dsp.crisp_select(q, k, p, pe_prob=True)
+    torch.cuda.synchronize()
+    for f in ("route", "c_struct", "row_ptr", "pv", "ps", "nv", "ns"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # pooled probabilities are written for Pooled-Estimation heads only
+    t = cfg.nb * (cfg.nb + 1) // 2
+    for h in range(cfg.hq):
+        if a.route[h].item() == 0:
+            assert torch.equal(a.pe_prob[h * t:(h + 1) * t], b.pe_prob[h * t:(h + 1) * t])
+    n = int(a.row_ptr[-1])
+    assert torch.equal(a.col_idx[:n], b.col_idx[:n])
+
+
+def test_output_is_causal():
+    cfg = synth.custom_config("causal", 4096, 4, 2, seed=51, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    o = dsp.crisp_dense_attn(q, k, v)
+    i = 2500
+    k2, v2 = k.clone(), v.clone()
+    k2[:, i + 1:] += 3
+    v2[:, i + 1:] -= 2
+    o2 = dsp.crisp_dense_attn(q, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :i + 1], o2[:, :i + 1])
+    assert not torch.equal(o[:, i + 1:], o2[:, i + 1:])
+
+
+# ------------------------------------------------------------------ the Llama / Qwen layers
+
+def _big_layer(cid, heads_fid, nblk, seed_blocks):
+    spec = synth.make_spec(synth.CONFIGS[cid])
+    cfg = spec.cfg
+    Q, K, V = P.load_layer(spec)
+    p = P.params_of(cfg)
+    q, k, v, o, sel = _run_layer(spec, Q, K, V, p)
+    del q, k, v
+    route = sel.route.cpu().numpy()
+    P.log(f"[{cfg.name}] routes VS={int((route == 1).sum())} PE={int((route == 0).sum())}")
+    # diffuse heads route to PE; each KV group's lead concentrated head (its keys carry the
+    # recency alignment) routes to VS.  Other concentrated heads go either way depending on
+    # their sink / recency strength: that is the router's call, checked bit-exactly below.
+    assert np.all(route[~spec.concentrated] == 0), route
+    assert np.all(route[spec.lead[spec.lead >= 0]] == 1), route
+    P.log(f"[{cfg.name}] C_struct", np.round(sel.c_struct.cpu().numpy(), 3).tolist())
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+    P.log(f"[{cfg.name}] decisions", rep)
+    assert rep["heads_checked"] + rep["pe_exempt"] == cfg.hq
+    vs = [h for h in range(cfg.hq) if route[h] == 1][:heads_fid]
+    pe = [h for h in range(cfg.hq) if route[h] == 0][:heads_fid]
+    P.log(f"[{cfg.name}] score err", P.check_score_fidelity(spec, Q, K, sel, vs + pe))
+    P.log(f"[{cfg.name}] PE prob err", P.check_pe_fidelity(spec, Q, K, sel, pe[:1]))
+    blocks = synth.sample_blocks(cfg.nb, nblk, seed_blocks)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), vs[:2] + pe[:2], blocks)
+    P.log(f"[{cfg.name}] attention (sampled {len(blocks)} blocks x 4 heads) max {mx:.2e} mean {mean:.2e}")
+
+
+def test_llama_32k_layer():
+    _big_layer(1, 3, 8, 1)
+
+
+@pytest.mark.timeout(900)
+def test_llama_128k_layer():
+    _big_layer(2, 2, 6, 2)
+
+
+@pytest.mark.timeout(900)
+def test_qwen_128k_layer():
+    _big_layer(3, 2, 6, 3)
+
+
+@pytest.mark.timeout(1200)
+def test_llama_512k_layer():
+    _big_layer(4, 1, 4, 4)

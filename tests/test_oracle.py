@@ -245,7 +245,9 @@ def test_pe_cut_ties_go_to_lower_flat_index():
     m, info = O.pe_cut(P, 0.95)
     assert info["kstar"] == 9
     assert m[3, 1] and not m[3, 2]
-    assert O.pe_tie(info)            # the cut value equals its neighbour: reported as a tie
+    assert not O.pe_tie(info)        # 3.85 vs 3.8: far from the target, equal values are no tie
+    _, info_t = O.pe_cut(P, 3.85 / 4)
+    assert O.pe_tie(info_t)          # the target sits exactly on a prefix sum
     m2, info2 = O.pe_cut(P, 0.9)     # 3.6 reached by the eighth entry (0.2 at (2,1))
     assert info2["kstar"] == 8 and m2[2, 1] and not m2[3, 1] and not m2[3, 2]
 
