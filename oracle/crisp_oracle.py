@@ -239,9 +239,10 @@ def pe_cut(P: np.ndarray, gamma: float):
     """Global gamma-cumsum over the flattened causal pooled matrix [CRISP §2, PE path].
 
     Entries (qb, kb <= qb) are ordered by descending P, ties by ascending
-    row-major flat index; the shortest prefix whose float64 sum reaches
-    gamma * sum(P) is kept; gamma >= 1 keeps everything.  The anchors (qb, 0)
-    and (qb, qb) of every row are then added.
+    row-major flat index; the shortest prefix whose sum reaches gamma * sum(P)
+    is kept; gamma >= 1 keeps everything.  The anchors (qb, 0) and (qb, qb) of
+    every row are then added.  Sums are accumulated in extended precision
+    (np.longdouble) so that their rounding stays far below any tie band.
     Returns (mask [N_b, N_b] bool, info dict with the cut position and mass).
     """
     P = np.asarray(P, np.float64)
@@ -249,23 +250,22 @@ def pe_cut(P: np.ndarray, gamma: float):
     qi, ki = np.tril_indices(nb)
     vals = P[qi, ki]
     flat = qi * nb + ki
-    total = float(vals.sum())
     order = np.lexsort((flat, -vals))
+    csum = np.cumsum(vals[order].astype(np.longdouble))
+    total = csum[-1] if vals.size else np.longdouble(0)
     mask = np.zeros((nb, nb), bool)
     if gamma >= 1.0:
         kstar = vals.size
         target = total
-        csum = np.cumsum(vals[order])
     else:
-        target = gamma * total
-        csum = np.cumsum(vals[order])
+        target = np.longdouble(gamma) * total
         kstar = int(np.searchsorted(csum, target, side="left")) + 1
         kstar = min(kstar, vals.size)
     take = order[:kstar]
     mask[qi[take], ki[take]] = True
     mask[np.arange(nb), 0] = True
     mask[np.arange(nb), np.arange(nb)] = True
-    info = dict(kstar=kstar, target=target, total=total,
+    info = dict(kstar=kstar, target=float(target), total=float(total), entries=int(vals.size),
                 prefix=float(csum[kstar - 1]) if kstar > 0 else 0.0,
                 prefix_before=float(csum[kstar - 2]) if kstar > 1 else 0.0,
                 cut_value=float(vals[order[kstar - 1]]) if kstar > 0 else 0.0,
@@ -273,15 +273,16 @@ def pe_cut(P: np.ndarray, gamma: float):
     return mask, info
 
 
-def pe_tie(info: dict, rel: float = TIE_REL) -> bool:
-    """True when gamma*T lies within `rel` (relative) of the prefix sum just
-    before or at the cut, i.e. when the summation order of an implementation
-    can move the cut by one entry.  Equal values straddling the cut are not a
-    tie: the lower flat index wins on every implementation."""
+def pe_tie(info: dict, rel: float = TIE_REL, band: float = 0.0) -> bool:
+    """True when gamma*T lies within max(rel * gamma*T, band) of the prefix sum
+    just before or at the cut, i.e. where the summation arithmetic of an
+    implementation can move the cut by one entry.  Equal values straddling the
+    cut are not a tie: the lower flat index wins on every implementation."""
     t = info["target"]
     if t <= 0:
         return False
-    return bool(abs(info["prefix"] - t) <= rel * t or abs(info["prefix_before"] - t) <= rel * t)
+    eps = max(rel * t, band)
+    return bool(abs(info["prefix"] - t) <= eps or abs(info["prefix_before"] - t) <= eps)
 
 
 def mask_to_lists(mask: np.ndarray) -> list:

@@ -94,9 +94,11 @@ def check_decisions(sel, hq, nb, p: dsp.CrispParams, heads=None):
                                                        p.gamma, p.min_blocks)
         # route and VS thresholds are the same float32 operations on the same float32
         # scores on both sides: they must agree even inside the tie band (ties are
-        # only counted).  The PE cut compares sums taken in different orders (exact
-        # fixed point on the GPU, float64 in sorted order here); it is exempt only
-        # where those can legitimately differ, 1e-8 relative of gamma*T.
+        # only counted).  The PE cut compares sums of the same float32 values taken
+        # with different arithmetic: the GPU truncates each entry to a multiple of
+        # 2^-46 (error < entries * 2^-46 in both the total and the prefix), the
+        # oracle accumulates in extended precision.  A head is exempt only when
+        # gamma*T lies within entries * 2^-45 of the prefix at the cut.
         rep["route_ties"] += int(route[h] != -1 and O.route_tie(cs[h], p.tau))
         assert r == route[h], f"head {h}: route gpu {route[h]} oracle {r} (C={cs[h]!r})"
         gl = head_lists(rp, col, h, nb)
@@ -108,7 +110,7 @@ def check_decisions(sel, hq, nb, p: dsp.CrispParams, heads=None):
         elif r == 0:
             rep["pe_heads"] += 1
             rep["pe_ties"] += int(O.pe_tie(info))
-            if O.pe_tie(info, 1e-8):
+            if O.pe_tie(info, 0.0, info["entries"] * 2.0 ** -45):
                 rep["pe_exempt"] += 1
                 continue
         else:
