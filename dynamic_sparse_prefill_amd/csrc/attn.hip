@@ -30,7 +30,16 @@ namespace crisp {
 
 // ------------------------------------------------------------------ V re-layout
 
-// V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128]
+// Position of key e (0..127) inside a re-laid-out V^T row (bf16 only).  Within
+// each group of 16 keys, positions 8g..8g+7 hold keys {4g..4g+3, 8+4g..8+4g+3}:
+// exactly the eight keys that lane half g contributes to one 32x32x16 MFMA of
+// O^T += V^T P^T, so each A operand is a single 16-byte LDS read.
+__host__ __device__ __forceinline__ int vt_pos(int e) {
+  const int grp = e >> 4, k = e & 15, h = k >> 3, g = (k >> 2) & 1, j = k & 3;
+  return 16 * grp + 8 * g + 4 * h + j;
+}
+
+// V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128]; bf16 rows use vt_pos order.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, T* __restrict__ Vt,
                                                           int nb, int64_t sv_h, int64_t sv_n) {
@@ -45,23 +54,82 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
   T* dst = Vt + ((int64_t)g * nb + kb) * (BLK * HD);
   for (int e = tid; e < BLK * HD; e += 256) {
     const int d = e / BLK, r = e % BLK;
-    dst[e] = tile[r][d];
+    const int pos = sizeof(T) == 2 ? vt_pos(r) : r;
+    dst[d * BLK + pos] = tile[r][d];
   }
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// gfx9 s_waitcnt immediates: wait for vector-memory count <= N only.
+constexpr int WAIT_VM0 = 0x0F70;
+constexpr int WAIT_VM8 = 0x0F78;
+
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A 128-row x 256-byte tile goes to LDS as 16-byte chunks, chunk c of row r at
+// physical chunk c ^ (r & 15): 16 lanes reading the same logical chunk of 16
+// consecutive rows hit 16 different bank groups.  Wave w copies rows
+// 32w..32w+31 with 8 direct global->LDS loads of 1 KB (4 rows) each; lane L
+// of load i fills row 32w + 4i + L/16, physical chunk L%16.  The per-lane byte
+// offset of that source chunk repeats every 4 loads up to +16 rows, so 4
+// offsets per tile suffice.
+struct TileCopy {
+  uint32_t off[4];
+  __device__ void init(int wu, int lane, uint32_t row_bytes) {
+    const int pc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wu + 4 * i + (lane >> 4);
+      off[i] = (uint32_t)r * row_bytes + ((uint32_t)(pc ^ (r & 15)) << 4);
+    }
+  }
+  __device__ void issue(const char* src, uint32_t row_bytes, uint32_t lds, int wu) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off[i & 3] + (i >> 2) * 16 * row_bytes),
+                                       (lds_void*)(uintptr_t)(lds + (32 * wu + 4 * i) * 256), 16, 0, 0);
+  }
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Four 16-byte LDS reads at addr + OFF + {0, 8, 16, 24} KB (rows 0, 32, 64, 96
+// of a tile for this lane), completed inside the same asm block.  Written by
+// hand so that the compiler does not add a wait on the in-flight global->LDS
+// copy of the other tile before them.
+template <int OFF>
+__device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(a[0]), "=v"(a[1]), "=v"(a[2]), "=v"(a[3])
+      : "v"(addr), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
+      : "memory");
+}
+
+constexpr int SV_OFF = 32768;  // V^T tile follows the K tile in LDS
 
 template <bool DENSE>
 __global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
     int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, float sl2) {
-  constexpr int KP = Tile<bf16>::KP;  // K tile pitch (elements)
-  constexpr int VP = 132;             // V^T tile pitch: 264 B, conflict-free 8-B reads
-  __shared__ __attribute__((aligned(16))) bf16 sK[BLK * KP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[HD * VP];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BLK * 256];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = hq / hkv;
   const int bid = blockIdx.x;
   const int qb = nb - 1 - bid / hq;
@@ -75,63 +143,68 @@ __global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
   }
   const int qrow = 32 * w + l32;
   bf16* orow = O + (int64_t)h * so_h + (int64_t)(qb * BLK + qrow) * so_n;
-  if (cnt <= 0) {
+  // listed blocks outside [0, qb] hold no key j <= i: skipped
+  auto block_at = [&](int i) {
+    return DENSE ? i : __builtin_amdgcn_readfirstlane(col_idx[beg + __builtin_amdgcn_readfirstlane(i)]);
+  };
+  auto next_valid = [&](int i) {
+    while (i < cnt && (unsigned)block_at(i) > (unsigned)qb) ++i;
+    return i;
+  };
+  int cur = next_valid(0);
+  if (cur >= cnt) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(bf16x4*)(orow + 32 * u + 8 * j + 4 * g) = bf16x4{};
     return;
   }
+  int kb = block_at(cur);
+
+  const uint32_t lbase = lds_addr(smem);
+  const uint32_t krow = (uint32_t)(sk_n * 2);
+  const char* Kh = (const char*)(K + (int64_t)kvh * sk_h);
+  const char* Vh = (const char*)(Vt + (int64_t)kvh * nb * (BLK * HD));
+  TileCopy kc, vc;
+  kc.init(w, lane, krow);
+  vc.init(w, lane, 256);
+  kc.issue(Kh + (int64_t)kb * BLK * krow, krow, lbase, w);
 
   Tile<bf16>::QFrag qf;
   Tile<bf16>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)(qb * BLK + qrow) * sq_n, g);
-
-  const bf16* Kh = K + (int64_t)kvh * sk_h;
-  const bf16* Vh = Vt + (int64_t)kvh * nb * (BLK * HD);
-  uint4 kr[8], vr[8];
-  auto gload = [&](int kb) {
-    const bf16* kbase = Kh + (int64_t)kb * BLK * sk_n;
-    const bf16* vbase = Vh + (int64_t)kb * (BLK * HD);
+  // LDS address of logical chunk 2c + g of this lane's row in the K tile
+  uint32_t kx[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
-      kr[i] = *(const uint4*)(kbase + (int64_t)r * sk_n + gr * 8);
-      vr[i] = *(const uint4*)(vbase + r * BLK + gr * 8);
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
-      *(uint4*)(sK + r * KP + gr * 8) = kr[i];
-      uint2* vd = (uint2*)(sV + r * VP + gr * 8);
-      vd[0] = make_uint2(vr[i].x, vr[i].y);
-      vd[1] = make_uint2(vr[i].z, vr[i].w);
-    }
-  };
+  for (int c = 0; c < 8; ++c) kx[c] = lbase + l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
 
-  // Listed blocks outside [0, qb] hold no key j <= i: they are skipped (never loaded).
-  auto valid = [&](int kb) { return (unsigned)kb <= (unsigned)qb; };
-  int kb_next = DENSE ? 0 : col_idx[beg];
-  if (valid(kb_next)) gload(kb_next);
   f32x16 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
   float m = -1e30f, l = 0.f;
 
-  for (int it = 0; it < cnt; ++it) {
-    const int kb = kb_next;
-    const bool ok = valid(kb);
-    __syncthreads();
-    if (ok) lstore();
-    __syncthreads();
-    if (it + 1 < cnt) {
-      kb_next = DENSE ? it + 1 : col_idx[beg + it + 1];
-      if (valid(kb_next)) gload(kb_next);
-    }
-    if (!ok) continue;
+  while (true) {
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);       // this wave's part of K_kb has landed
+    block_barrier();                            // K_kb complete; every wave is done with V of the last block
+    vc.issue(Vh + (int64_t)kb * (BLK * HD * 2), 256, lbase + SV_OFF, w);
+
     f32x16 s[4];
-    Tile<bf16>::st(s, sK, qf, l32, g);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[t] = f32x16{};
+    {
+      bf16x8 fa[4], fb[4];
+      lds_read4<0>(fa, kx[0]);
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_read4<0>(fb, kx[c + 1]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < 8) lds_read4<0>(fa, kx[c + 2]);
+      }
+    }
     if (kb == qb) {  // diagonal tile: keys after the query are masked
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -161,19 +234,41 @@ __global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
     m = mn;
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+
+    const int nxt = next_valid(cur + 1);
+    const int kbn = nxt < cnt ? block_at(nxt) : -1;
+    block_barrier();                            // every wave is done reading K_kb
+    if (kbn >= 0) {
+      kc.issue(Kh + (int64_t)kbn * BLK * krow, krow, lbase, w);
+      __builtin_amdgcn_s_waitcnt(WAIT_VM8);     // V_kb landed, K_kbn may still be in flight
+    } else {
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    }
+    block_barrier();                            // V_kb complete
+
+    {
+      bf16x8 fa[4], fb[4];
+      lds_read4<SV_OFF>(fa, kx[0]);
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      bf16x8 b;
+      for (int mm = 0; mm < 8; mm += 2) {
+        bf16x8 b0, b1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = (bf16)s[mm >> 1][8 * (mm & 1) + j];
+        for (int j = 0; j < 8; ++j) b0[j] = (bf16)s[mm >> 1][j];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16* vp = sV + (32 * u + l32) * VP + 16 * mm + 4 * g;
-        const bf16x4 lo = *(const bf16x4*)vp, hi = *(const bf16x4*)(vp + 8);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[u] = mfma_bf16(a, b, acc[u]);
+        for (int j = 0; j < 8; ++j) b1[j] = (bf16)s[mm >> 1][8 + j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], b0, acc[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_read4<SV_OFF>(fb, kx[mm + 1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], b1, acc[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (mm + 2 < 8) lds_read4<SV_OFF>(fa, kx[mm + 2]);
       }
     }
+    if (kbn < 0) break;
+    cur = nxt;
+    kb = kbn;
   }
   l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -394,7 +394,7 @@ def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, den
         out.update(sv=sv, ss=ss, lists=vs_block_lists(sv, ss, nb))
     else:
         P = pe_probabilities(q, k, blk)
-        mask, info = pe_cut(P, gamma)
+        mask, info = pe_cut(P, float(np.float32(gamma)))
         out.update(P=P, pe_info=info, lists=mask_to_lists(mask))
     return out
 
@@ -407,6 +407,7 @@ def decide_from_scores(route_in, c, pv, ps, P, nb, tau, alpha, gamma, min_blocks
     """
     if route_in == -1:
         return -1, None, None, dense_lists(nb), None
+    gamma = float(np.float32(gamma))        # the parameter as the float32 it is passed as
     vs = route_decision(np.float32(c), tau)
     if vs:
         sv = vs_select_direction(np.asarray(pv, np.float32), alpha, min_blocks)
