@@ -66,6 +66,18 @@ def event_ms(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
+def calibrate_copy(mib, torch):
+    """One plain device copy of `mib` MiB (read mib, write mib): the reference that
+    scales the HBM byte counters of the attention kernel."""
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {mib} MiB read + {mib} MiB written")
+
+
 def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True):
     spec = synth.make_spec(synth.CONFIGS[cfg_id])
     cfg = spec.cfg
@@ -166,6 +178,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--workload", type=int, default=4, help="layer id: 1 llama-32k, 2 llama-128k, 3 qwen-128k, 4 llama-512k")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline (counter-collection runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding (by KV group) is not built",
@@ -179,7 +194,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
-    main_res, spec, route = run_layer(args.workload, args.steps, args.warmup, torch, dsp, synth)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, torch)
+    main_res, spec, route = run_layer(args.workload, args.steps, args.warmup, torch, dsp, synth,
+                                      with_dense=not args.no_dense)
     log("[bench]", json.dumps(main_res))
     extra = {}
     if not args.no_extra:
@@ -213,8 +231,8 @@ def main():
         "config": {"workload": main_res["workload"], "n": main_res["n"], "hq": main_res["hq"], "hkv": main_res["hkv"],
                    "d": 128, "block": 128, "tau": 0.3, "alpha": 1.0, "gamma": 0.95,
                    "generator": "seeded sink/recency/needle heads, length-compensated"},
-        "speedup_vs_dense": round(main_res["speedup"], 3),
-        "dense_ms": round(main_res["dense_ms"], 3),
+        "speedup_vs_dense": round(main_res["speedup"], 3) if "speedup" in main_res else None,
+        "dense_ms": round(main_res["dense_ms"], 3) if "dense_ms" in main_res else None,
         "stages": {"select_ms": round(main_res["select_ms"], 3), "sparse_attn_ms": round(main_res["sparse_attn_ms"], 3)},
         "density": round(main_res["density"], 4),
         "heads": {"vs": main_res["vs_heads"], "pe": main_res["pe_heads"]},
@@ -222,7 +240,9 @@ def main():
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "fa_bf16_kernel<false> (sparse attention; event time includes the V re-layout)",
                      "flops_per_launch": main_res["tiles"] * TILE_FLOPS},
-        "dense_roofline": {"achieved": round(main_res["dense_tflops"], 2), "frac": round(main_res["dense_tflops"] / PEAK_BF16_TFLOPS, 4)},
+        "dense_roofline": ({"achieved": round(main_res["dense_tflops"], 2),
+                            "frac": round(main_res["dense_tflops"] / PEAK_BF16_TFLOPS, 4)}
+                           if "dense_tflops" in main_res else None),
         "cpu_baseline": cpu,
         "extra": extra,
     }

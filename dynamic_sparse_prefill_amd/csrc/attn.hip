@@ -75,26 +75,24 @@ __device__ __forceinline__ void block_barrier() {
 
 // A 128-row x 256-byte tile goes to LDS as 16-byte chunks, chunk c of row r at
 // physical chunk c ^ (r & 15): 16 lanes reading the same logical chunk of 16
-// consecutive rows hit 16 different bank groups.  Wave w copies rows
-// 32w..32w+31 with 8 direct global->LDS loads of 1 KB (4 rows) each; lane L
-// of load i fills row 32w + 4i + L/16, physical chunk L%16.  The per-lane byte
-// offset of that source chunk repeats every 4 loads up to +16 rows, so 4
-// offsets per tile suffice.
+// consecutive rows hit 16 different bank groups.  With 8 waves, wave w copies
+// rows 16w..16w+15 with 4 direct global->LDS loads of 1 KB (4 rows) each; lane
+// L of load i fills row 16w + 4i + L/16, physical chunk L%16.
 struct TileCopy {
   uint32_t off[4];
   __device__ void init(int wu, int lane, uint32_t row_bytes) {
     const int pc = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 32 * wu + 4 * i + (lane >> 4);
+      const int r = 16 * wu + 4 * i + (lane >> 4);
       off[i] = (uint32_t)r * row_bytes + ((uint32_t)(pc ^ (r & 15)) << 4);
     }
   }
-  __device__ void issue(const char* src, uint32_t row_bytes, uint32_t lds, int wu) const {
+  __device__ void issue(const char* src, uint32_t lds, int wu) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + off[i & 3] + (i >> 2) * 16 * row_bytes),
-                                       (lds_void*)(uintptr_t)(lds + (32 * wu + 4 * i) * 256), 16, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (lds_void*)(uintptr_t)(lds + (16 * wu + 4 * i) * 256),
+                                       16, 0, 0);
   }
 };
 
@@ -105,7 +103,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Four 16-byte LDS reads at addr + OFF + {0, 8, 16, 24} KB (rows 0, 32, 64, 96
 // of a tile for this lane), completed inside the same asm block.  Written by
 // hand so that the compiler does not add a wait on the in-flight global->LDS
-// copy of the other tile before them.
+// copy of the next tile before them.
 template <int OFF>
 __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
   asm volatile(
@@ -119,47 +117,95 @@ __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
       : "memory");
 }
 
-constexpr int SV_OFF = 32768;  // V^T tile follows the K tile in LDS
+constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 
+// Walks the union of the ascending key-block lists of the two query blocks of
+// a work-group.  Entries outside [0, qb] of their own block are skipped.
+struct PairCursor {
+  const int32_t* a;  const int32_t* b;
+  int na, nb_, ia, ib, qa, qb;
+  __device__ int head(const int32_t* l, int n, int& i, int q) const {
+    while (i < n) {
+      const int k = __builtin_amdgcn_readfirstlane(l[__builtin_amdgcn_readfirstlane(i)]);
+      if ((unsigned)k <= (unsigned)q) return k;
+      ++i;
+    }
+    return 0x7fffffff;
+  }
+  // next block of the union (-1 when done) and which halves list it
+  __device__ int next(bool& in_a, bool& in_b) {
+    const int x = head(a, na, ia, qa), y = head(b, nb_, ib, qb);
+    const int k = min(x, y);
+    in_a = (x == k) && k != 0x7fffffff;
+    in_b = (y == k) && k != 0x7fffffff;
+    if (in_a) ++ia;
+    if (in_b) ++ib;
+    return k == 0x7fffffff ? -1 : k;
+  }
+};
+
+// One work-group = one query head x two adjacent query blocks (2p, 2p+1):
+// waves 0-3 own block 2p, waves 4-7 block 2p+1, 32 rows per wave.  The K and
+// V^T tiles of a key block are loaded once into LDS and used by both halves;
+// tiles are double-buffered so the next block's copy runs during a whole
+// iteration, with one barrier per key block.
 template <bool DENSE>
-__global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
+__global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
     int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, float sl2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = w >> 2, wq = w & 3;
   const int G = hq / hkv;
+  const int npair = (nb + 1) >> 1;
+  // blockIdx -> (KV head, query-block pair descending, head in group).  Dispatch
+  // hands consecutive work-groups to the 8 XCDs in turn, so every XCD gets an
+  // equal share of each KV group's rows whatever the routes of its heads, and
+  // all XCDs stream the same group's K/V at the same time.
   const int bid = blockIdx.x;
-  const int qb = nb - 1 - bid / hq;
-  const int rem = bid % hq;
-  const int kvh = rem % hkv, h = kvh * G + rem / hkv;
-  int beg = 0, cnt = qb + 1;
+  const int kvh = bid / (npair * G);
+  const int rem = bid % (npair * G);
+  const int pair = npair - 1 - rem / G;
+  const int h = kvh * G + rem % G;
+  const int qlo = 2 * pair, qhi = 2 * pair + 1;
+  const bool hi_ok = qhi < nb;
+  const int qmine = half ? qhi : qlo;
+  const bool rows_ok = half == 0 || hi_ok;
+
+  PairCursor cur;
+  cur.qa = qlo;
+  cur.qb = hi_ok ? qhi : -1;
+  cur.ia = cur.ib = 0;
   if (!DENSE) {
-    const int64_t r = (int64_t)h * nb + qb;
-    beg = row_ptr[r];
-    cnt = row_ptr[r + 1] - beg;
+    const int64_t ra = (int64_t)h * nb + qlo;
+    cur.a = col_idx + row_ptr[ra];
+    cur.na = row_ptr[ra + 1] - row_ptr[ra];
+    if (hi_ok) {
+      cur.b = col_idx + row_ptr[ra + 1];
+      cur.nb_ = row_ptr[ra + 2] - row_ptr[ra + 1];
+    } else {
+      cur.b = cur.a;
+      cur.nb_ = 0;
+    }
   }
-  const int qrow = 32 * w + l32;
-  bf16* orow = O + (int64_t)h * so_h + (int64_t)(qb * BLK + qrow) * so_n;
-  // listed blocks outside [0, qb] hold no key j <= i: skipped
-  auto block_at = [&](int i) {
-    return DENSE ? i : __builtin_amdgcn_readfirstlane(col_idx[beg + __builtin_amdgcn_readfirstlane(i)]);
+  int dense_next = 0;
+  auto next_block = [&](bool& ia, bool& ib) -> int {
+    if (DENSE) {
+      const int k = dense_next++;
+      const int top = hi_ok ? qhi : qlo;
+      ia = k <= qlo;
+      ib = hi_ok && k <= qhi;
+      return k <= top ? k : -1;
+    }
+    return cur.next(ia, ib);
   };
-  auto next_valid = [&](int i) {
-    while (i < cnt && (unsigned)block_at(i) > (unsigned)qb) ++i;
-    return i;
-  };
-  int cur = next_valid(0);
-  if (cur >= cnt) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(bf16x4*)(orow + 32 * u + 8 * j + 4 * g) = bf16x4{};
-    return;
-  }
-  int kb = block_at(cur);
+
+  const int qrow = 32 * wq + l32;
+  bf16* orow = O + (int64_t)h * so_h + (int64_t)(qmine * BLK + qrow) * so_n;
 
   const uint32_t lbase = lds_addr(smem);
   const uint32_t krow = (uint32_t)(sk_n * 2);
@@ -168,11 +214,21 @@ __global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
   TileCopy kc, vc;
   kc.init(w, lane, krow);
   vc.init(w, lane, 256);
-  kc.issue(Kh + (int64_t)kb * BLK * krow, krow, lbase, w);
+  auto issue = [&](int kb, int stage) {
+    const uint32_t sb = lbase + stage * STAGE_BYTES;
+    kc.issue(Kh + (int64_t)kb * BLK * krow, sb, w);
+    vc.issue(Vh + (int64_t)kb * (BLK * HD * 2), sb + TILE_BYTES, w);
+  };
+
+  bool a0, b0;
+  int kb = next_block(a0, b0);
+  if (kb >= 0) issue(kb, 0);
+  bool a1 = false, b1 = false;
+  int kb1 = kb >= 0 ? next_block(a1, b1) : -1;
 
   Tile<bf16>::QFrag qf;
-  Tile<bf16>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)(qb * BLK + qrow) * sq_n, g);
-  // LDS address of logical chunk 2c + g of this lane's row in the K tile
+  if (rows_ok) Tile<bf16>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)(qmine * BLK + qrow) * sq_n, g);
+  // LDS address of logical chunk 2c + g of this lane's row in the K tile of stage 0
   uint32_t kx[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) kx[c] = lbase + l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
@@ -181,95 +237,96 @@ __global__ __launch_bounds__(256, 2) void fa_bf16_kernel(
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
   float m = -1e30f, l = 0.f;
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  int stage = 0;
 
-  while (true) {
-    __builtin_amdgcn_s_waitcnt(WAIT_VM0);       // this wave's part of K_kb has landed
-    block_barrier();                            // K_kb complete; every wave is done with V of the last block
-    vc.issue(Vh + (int64_t)kb * (BLK * HD * 2), 256, lbase + SV_OFF, w);
-
-    f32x16 s[4];
+  while (kb >= 0) {
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);       // this wave's share of the tiles of kb has landed
+    block_barrier();                            // all of them have; every wave left the other stage
+    if (kb1 >= 0) issue(kb1, stage ^ 1);
+    bool a2 = false, b2 = false;
+    const int kb2 = kb1 >= 0 ? next_block(a2, b2) : -1;   // list lookup overlaps the MFMAs
+    const bool active = half ? b0 : a0;
+    if (active) {
+      const uint32_t so = stage * STAGE_BYTES;
+      f32x16 s[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s[t] = f32x16{};
-    {
-      bf16x8 fa[4], fb[4];
-      lds_read4<0>(fa, kx[0]);
+      for (int t = 0; t < 4; ++t) s[t] = f32x16{};
+      {
+        bf16x8 fa[4], fb[4];
+        lds_read4<0>(fa, kx[0] + so);
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) {
+        for (int c = 0; c < 8; c += 2) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_read4<0>(fb, kx[c + 1]);
+          for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
+          __builtin_amdgcn_sched_barrier(0);
+          lds_read4<0>(fb, kx[c + 1] + so);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 < 8) lds_read4<0>(fa, kx[c + 2]);
+          for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (c + 2 < 8) lds_read4<0>(fa, kx[c + 2] + so);
+        }
       }
-    }
-    if (kb == qb) {  // diagonal tile: keys after the query are masked
+      if (kb == qmine) {  // diagonal tile: keys after the query are masked
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * t + mfma32_row(i, g) > qrow) s[t][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * t + mfma32_row(i, g) > qrow) s[t][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // Lazy running max: m is raised only when a row's tile max exceeds it by
+      // more than 2^8 in probability, so most tiles skip rescaling O and l.
+      // Exact softmax either way: p = exp2((s - m) sl2) <= 2^8 in fp32 / bf16.
+      if (__ballot((mx - m) * sl2 > 8.f)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - mn) * sl2);
+        l *= alpha;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2((m - mn) * sl2);
-    const float mb = mn * sl2;
-    float rs = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
-        s[t][i] = p;
-        rs += p;
+        for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+        m = mn;
       }
-    l = fmaf(l, alpha, rs);
-    m = mn;
+      const float mb = m * sl2;
+      // P in bf16, already in the B-operand order of the O^T MFMAs; the row sum
+      // is taken over the same rounded values (v_dot2 with (1, 1)).
+      bf16x8 pb[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] *= alpha;
-
-    const int nxt = next_valid(cur + 1);
-    const int kbn = nxt < cnt ? block_at(nxt) : -1;
-    block_barrier();                            // every wave is done reading K_kb
-    if (kbn >= 0) {
-      kc.issue(Kh + (int64_t)kbn * BLK * krow, krow, lbase, w);
-      __builtin_amdgcn_s_waitcnt(WAIT_VM8);     // V_kb landed, K_kbn may still be in flight
-    } else {
-      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-    }
-    block_barrier();                            // V_kb complete
-
-    {
-      bf16x8 fa[4], fb[4];
-      lds_read4<SV_OFF>(fa, kx[0]);
+      for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
-      for (int mm = 0; mm < 8; mm += 2) {
-        bf16x8 b0, b1;
+        for (int j = 0; j < 8; j += 2) {
+          bf16x2 pr;
+          pr[0] = (bf16)fast_exp2(fmaf(s[mm >> 1][8 * (mm & 1) + j], sl2, -mb));
+          pr[1] = (bf16)fast_exp2(fmaf(s[mm >> 1][8 * (mm & 1) + j + 1], sl2, -mb));
+          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+          pb[mm][j] = pr[0];
+          pb[mm][j + 1] = pr[1];
+        }
+      {
+        bf16x8 fa[4], fb[4];
+        lds_read4<TILE_BYTES>(fa, kx[0] + so);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b0[j] = (bf16)s[mm >> 1][j];
+        for (int mm = 0; mm < 8; mm += 2) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b1[j] = (bf16)s[mm >> 1][8 + j];
+          for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], pb[mm], acc[u]);
+          __builtin_amdgcn_sched_barrier(0);
+          lds_read4<TILE_BYTES>(fb, kx[mm + 1] + so);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], b0, acc[u]);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_read4<SV_OFF>(fb, kx[mm + 1]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], b1, acc[u]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (mm + 2 < 8) lds_read4<SV_OFF>(fa, kx[mm + 2]);
+          for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], pb[mm + 1], acc[u]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (mm + 2 < 8) lds_read4<TILE_BYTES>(fa, kx[mm + 2] + so);
+        }
       }
     }
-    if (kbn < 0) break;
-    cur = nxt;
-    kb = kbn;
+    kb = kb1; a0 = a1; b0 = b1;
+    kb1 = kb2; a1 = a2; b1 = b2;
+    stage ^= 1;
   }
+  if (!rows_ok) return;
   l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -396,8 +453,9 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
                            hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   } else {
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
-    k<<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, nb, hq,
-                           hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
+    const dim3 pgrid((unsigned)((int64_t)((nb + 1) / 2) * hq));
+    k<<<pgrid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, nb, hq,
+                            hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   }
   return hipGetLastError();
 }
