@@ -8,7 +8,7 @@
 // blocks it selects).  Dense attention is the same loop over every block
 // 0..qb.
 //
-// Design (one work-group = one (head, query block) = 128 query rows, 4 waves):
+// Design:
 //  * Scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so
 //    each lane owns one query row and 64 of its 128 scores per key tile; the
 //    online-softmax max / sum are in-lane plus one lane^32 exchange.
@@ -16,12 +16,16 @@
 //    is already in the B-operand layout, and V^T comes from LDS.  V is
 //    re-laid out once per call as per-block transposed tiles [d][key] so that
 //    the tile copy to LDS is a plain coalesced 32 KB copy.
-//  * K and V^T tiles are staged in padded LDS (67 KB per work-group, two
-//    work-groups per CU); the next tile's global loads are issued into
-//    registers before the current tile is computed.
-//  * Work order: blockIdx -> (qb descending, head-in-group, KV head).  With 8
-//    KV heads the 8 XCDs each see one KV head (blockIdx mod 8), so a KV head's
-//    K/V stream stays in one XCD's L2; long (late) rows start first.
+//  * One work-group = one head x two adjacent query blocks (256 rows, 8
+//    waves).  K and V^T tiles go straight from global memory to LDS
+//    (global_load_lds, no staging registers), XOR-swizzled for conflict-free
+//    16-byte reads, double-buffered so the next block streams in during a
+//    whole iteration; one barrier per key block.
+//  * Scheduling: a persistent grid (one work-group per CU) pulls (pair, head)
+//    items from an atomic queue, longest rows first, heads of one KV group
+//    together: every CU stays busy whatever the list lengths.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
@@ -40,11 +44,13 @@ __host__ __device__ __forceinline__ int vt_pos(int e) {
 }
 
 // V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128]; bf16 rows use vt_pos order.
+// Also clears the attention kernel's work-queue counter (it runs right before).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, T* __restrict__ Vt,
-                                                          int nb, int64_t sv_h, int64_t sv_n) {
+                                                          int nb, int64_t sv_h, int64_t sv_n, int* queue) {
   __shared__ T tile[BLK][HD + 2];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  if (kb == 0 && g == 0 && tid == 0 && queue) *queue = 0;
   const T* src = V + (int64_t)g * sv_h + (int64_t)kb * BLK * sv_n;
   for (int e = tid; e < BLK * HD; e += 256) {
     const int r = e / HD, d = e % HD;
@@ -120,6 +126,20 @@ __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
 constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 
+// Work queue.  The kernel is persistent (one work-group per CU) and pulls
+// items from an atomic counter, so every CU stays busy until the queue is
+// empty whatever the lengths of the lists.  Item i is query-block pair
+// npair-1 - i / hq (longest rows first) and, within the pair, KV head
+// (i % hq) / G and head-in-group (i % hq) % G, so the heads of one KV group
+// are taken together and stream the same K/V.
+__device__ inline void queue_item(int item, int npair, int hq, int hkv, int& pair, int& kvh, int& h) {
+  const int G = hq / hkv;
+  pair = npair - 1 - item / hq;
+  const int j = item % hq;
+  kvh = j / G;
+  h = kvh * G + j % G;
+}
+
 // Walks the union of the ascending key-block lists of the two query blocks of
 // a work-group.  Entries outside [0, qb] of their own block are skipped.
 struct PairCursor {
@@ -151,26 +171,15 @@ struct PairCursor {
 // tiles are double-buffered so the next block's copy runs during a whole
 // iteration, with one barrier per key block.
 template <bool DENSE>
-__global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
+__device__ __forceinline__ void fa_bf16_item(
+    char* smem, int pair, int kvh, int h,
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
     int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, float sl2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
-
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = w >> 2, wq = w & 3;
   const int G = hq / hkv;
-  const int npair = (nb + 1) >> 1;
-  // blockIdx -> (KV head, query-block pair descending, head in group).  Dispatch
-  // hands consecutive work-groups to the 8 XCDs in turn, so every XCD gets an
-  // equal share of each KV group's rows whatever the routes of its heads, and
-  // all XCDs stream the same group's K/V at the same time.
-  const int bid = blockIdx.x;
-  const int kvh = bid / (npair * G);
-  const int rem = bid % (npair * G);
-  const int pair = npair - 1 - rem / G;
-  const int h = kvh * G + rem % G;
   const int qlo = 2 * pair, qhi = 2 * pair + 1;
   const bool hi_ok = qhi < nb;
   const int qmine = half ? qhi : qlo;
@@ -340,6 +349,32 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     }
 }
 
+// Persistent driver: one work-group per CU takes (pair, head) items from the
+// queue until it is empty.  `queue` must be zero at launch.
+template <bool DENSE>
+__global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue, int nb,
+    int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n,
+    float sl2) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  __shared__ int s_item;
+  const int npair = (nb + 1) >> 1;
+  const int total = npair * hq;
+  while (true) {
+    __builtin_amdgcn_s_waitcnt(0);                // nothing of the last item is still in flight
+    __syncthreads();                              // every wave is done with the last item's LDS
+    if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) break;
+    int pair, kvh, h;
+    queue_item(item, npair, hq, hkv, pair, kvh, h);
+    fa_bf16_item<DENSE>(smem, pair, kvh, h, Q, K, Vt, O, row_ptr, col_idx, nb, hq, hkv, sq_h, sq_n, sk_h, sk_n,
+                        so_h, so_n, sl2);
+  }
+}
+
 // ------------------------------------------------------------------ fp32 MFMA kernel
 
 template <bool DENSE>
@@ -433,29 +468,42 @@ __global__ __launch_bounds__(256, 1) void fa_f32_kernel(
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv, int64_t sv_h, int64_t sv_n,
-                              hipStream_t s) {
+                              int* queue, hipStream_t s) {
   dim3 grid(nb, hkv);
   if (fp32)
-    transpose_v_kernel<float><<<grid, 256, 0, s>>>((const float*)V, (float*)Vt, nb, sv_h, sv_n);
+    transpose_v_kernel<float><<<grid, 256, 0, s>>>((const float*)V, (float*)Vt, nb, sv_h, sv_n, queue);
   else
-    transpose_v_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)V, (bf16*)Vt, nb, sv_h, sv_n);
+    transpose_v_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)V, (bf16*)Vt, nb, sv_h, sv_n, queue);
   return hipGetLastError();
 }
 
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
-                            const int32_t* row_ptr, const int32_t* col_idx, int nb, int hq, int hkv,
+                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, int nb, int hq, int hkv,
                             const Strides& st, hipStream_t s) {
   const float sl2 = LOG2E / sqrtf((float)HD);
-  const dim3 grid((unsigned)((int64_t)nb * hq));
   if (fp32) {
+    const dim3 grid((unsigned)((int64_t)nb * hq));
     auto k = dense ? fa_f32_kernel<true> : fa_f32_kernel<false>;
     k<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (const float*)Vt, (float*)O, row_ptr, col_idx, nb,
                            hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   } else {
+    const int64_t items = (int64_t)((nb + 1) / 2) * hq;
+    const dim3 grid((unsigned)std::min<int64_t>(items, cu_count()));
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
-    const dim3 pgrid((unsigned)((int64_t)((nb + 1) / 2) * hq));
-    k<<<pgrid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, nb, hq,
-                            hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
+    k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, nb,
+                           hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   }
   return hipGetLastError();
 }

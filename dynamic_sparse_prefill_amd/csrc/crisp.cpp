@@ -87,10 +87,12 @@ SelectLayout select_layout(const crisp_shape* s) {
   return L;
 }
 
-size_t attn_ws(const crisp_shape* s) {
+// Attention workspace: re-laid-out V^T, then the work-queue counter.
+size_t vt_bytes(const crisp_shape* s) {
   const size_t esz = s->dtype == CRISP_FP32 ? 4 : 2;
   return align256((size_t)s->hkv * (size_t)s->n * HD * esz);
 }
+size_t attn_ws(const crisp_shape* s) { return vt_bytes(s) + 256; }
 
 bool dense_path(const crisp_shape* s, const crisp_params* p) {
   const int64_t nb = s->n / BLK;
@@ -178,10 +180,11 @@ int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, 
              const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream) {
   const int nb = (int)(s->n / BLK);
   const int fp32 = s->dtype == CRISP_FP32;
-  hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, stream);
+  int* queue = (int*)((char*)ws + vt_bytes(s));
+  hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, queue, stream);
   if (e != hipSuccess) return CRISP_E_HIP;
-  return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, nb, s->hq, s->hkv, strides(s),
-                                    stream));
+  return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, queue, nb, s->hq, s->hkv,
+                                    strides(s), stream));
 }
 
 }  // namespace

@@ -9,10 +9,12 @@ namespace crisp {
 struct Strides { int64_t q_h, q_n, k_h, k_n, v_h, v_n, o_h, o_n; };
 
 // ---- attention (attn.hip)
+// V [hkv][n][d] -> per-block transposed V^T; also zeroes *queue (may be NULL)
 hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv,
-                              int64_t sv_h, int64_t sv_n, hipStream_t s);
+                              int64_t sv_h, int64_t sv_n, int* queue, hipStream_t s);
+// queue: the persistent kernel's work counter, zero at launch (set by launch_transpose_v)
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
-                            const int32_t* row_ptr, const int32_t* col_idx, int nb, int hq, int hkv,
+                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, int nb, int hq, int hkv,
                             const Strides& st, hipStream_t s);
 
 // ---- proxy (proxy.hip)

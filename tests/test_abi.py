@@ -38,7 +38,7 @@ def test_workspace_and_capacity_queries():
     assert dsp.col_capacity(s) == 4 * nb * (nb + 1) // 2
     ws = dsp.select_workspace_bytes(s, p)
     assert ws > 4 * nb * (nb + 1) // 2 * 4          # holds the pooled matrix of every head
-    assert dsp.attn_workspace_bytes(s) == 2 * 4096 * 128 * 2
+    assert dsp.attn_workspace_bytes(s) == 2 * 4096 * 128 * 2 + 256
     assert dsp.workspace_bytes(s, p) == ws + dsp.attn_workspace_bytes(s)
     # invalid shapes and parameters report zero
     assert dsp.select_workspace_bytes(_shape(d=64), p) == 0
