@@ -22,8 +22,9 @@
 //    16-byte reads, double-buffered so the next block streams in during a
 //    whole iteration; one barrier per key block.
 //  * Scheduling: a persistent grid (one work-group per CU) pulls (pair, head)
-//    items from an atomic queue, longest rows first, heads of one KV group
-//    together: every CU stays busy whatever the list lengths.
+//    items from 8 per-XCD queues, longest rows first, the heads of one KV
+//    group on one XCD, stealing from other queues at the end: every CU stays
+//    busy whatever the list lengths and K/V is shared through L2.
 #include <algorithm>
 
 #include "common.h"
@@ -31,6 +32,8 @@
 #include "tile.h"
 
 namespace crisp {
+
+constexpr int NQUEUE = 8;  // work queues of the persistent attention kernel (one per XCD)
 
 // ------------------------------------------------------------------ V re-layout
 
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ 
                                                           int nb, int64_t sv_h, int64_t sv_n, int* queue) {
   __shared__ T tile[BLK][HD + 2];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  if (kb == 0 && g == 0 && tid == 0 && queue) *queue = 0;
+  if (kb == 0 && g == 0 && tid < NQUEUE && queue) queue[tid] = 0;
   const T* src = V + (int64_t)g * sv_h + (int64_t)kb * BLK * sv_n;
   for (int e = tid; e < BLK * HD; e += 256) {
     const int r = e / HD, d = e % HD;
@@ -126,18 +129,25 @@ __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
 constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 
-// Work queue.  The kernel is persistent (one work-group per CU) and pulls
-// items from an atomic counter, so every CU stays busy until the queue is
-// empty whatever the lengths of the lists.  Item i is query-block pair
-// npair-1 - i / hq (longest rows first) and, within the pair, KV head
-// (i % hq) / G and head-in-group (i % hq) % G, so the heads of one KV group
-// are taken together and stream the same K/V.
-__device__ inline void queue_item(int item, int npair, int hq, int hkv, int& pair, int& kvh, int& h) {
+// Work queues.  The kernel is persistent (one work-group per CU).  A unit of
+// work is one (query-block pair, KV head) with its G query heads.  Units are
+// numbered u = pair' * hkv + kvh with pair' counted from the longest rows, and
+// unit u belongs to queue u % 8: with 8 KV heads each queue holds one KV
+// group, so the items running together on an XCD stream the same K/V through
+// its L2.  Work-group b starts on queue b % 8 (dispatch places it on XCD
+// b % 8), takes items from it longest first, then steals from the other
+// queues until all are empty, which evens out groups of unequal work.  Only
+// locality depends on the placement; every item is taken exactly once.
+
+// t-th item of queue x -> (pair, kvh, h); false once the queue is exhausted
+__device__ inline bool queue_item(int x, int t, int npair, int hq, int hkv, int& pair, int& kvh, int& h) {
   const int G = hq / hkv;
-  pair = npair - 1 - item / hq;
-  const int j = item % hq;
-  kvh = j / G;
-  h = kvh * G + j % G;
+  const int u = NQUEUE * (t / G) + x;                       // the queue's (t/G)-th unit
+  if (u >= npair * hkv) return false;
+  pair = npair - 1 - u / hkv;
+  kvh = u % hkv;
+  h = kvh * G + t % G;
+  return true;
 }
 
 // Walks the union of the ascending key-block lists of the two query blocks of
@@ -349,8 +359,8 @@ __device__ __forceinline__ void fa_bf16_item(
     }
 }
 
-// Persistent driver: one work-group per CU takes (pair, head) items from the
-// queue until it is empty.  `queue` must be zero at launch.
+// Persistent driver: one work-group per CU takes items from the queues until
+// all are empty.  `queue` holds NQUEUE counters, zero at launch.
 template <bool DENSE>
 __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
@@ -360,18 +370,19 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
   __shared__ int s_item;
   const int npair = (nb + 1) >> 1;
-  const int total = npair * hq;
-  while (true) {
-    __builtin_amdgcn_s_waitcnt(0);                // nothing of the last item is still in flight
-    __syncthreads();                              // every wave is done with the last item's LDS
-    if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
-    __syncthreads();
-    const int item = s_item;
-    if (item >= total) break;
-    int pair, kvh, h;
-    queue_item(item, npair, hq, hkv, pair, kvh, h);
-    fa_bf16_item<DENSE>(smem, pair, kvh, h, Q, K, Vt, O, row_ptr, col_idx, nb, hq, hkv, sq_h, sq_n, sk_h, sk_n,
-                        so_h, so_n, sl2);
+  const int home = blockIdx.x % NQUEUE;
+  for (int k = 0; k < NQUEUE; ++k) {
+    const int x = (home + k) % NQUEUE;
+    while (true) {
+      __builtin_amdgcn_s_waitcnt(0);              // nothing of the last item is still in flight
+      __syncthreads();                            // every wave is done with the last item's LDS
+      if (threadIdx.x == 0) s_item = atomicAdd(queue + x, 1);
+      __syncthreads();
+      int pair, kvh, h;
+      if (!queue_item(x, s_item, npair, hq, hkv, pair, kvh, h)) break;
+      fa_bf16_item<DENSE>(smem, pair, kvh, h, Q, K, Vt, O, row_ptr, col_idx, nb, hq, hkv, sq_h, sq_n, sk_h,
+                          sk_n, so_h, so_n, sl2);
+    }
   }
 }
 
