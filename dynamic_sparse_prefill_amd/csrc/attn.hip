@@ -126,6 +126,26 @@ __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
       : "memory");
 }
 
+// Eight 16-byte LDS reads: rows 0/32/64/96 at a0 + OFF and at a1 + OFF, completed
+// inside the block.  Issued right behind eight queued MFMAs, whose execution
+// (~256 cycles) covers the LDS latency.
+template <int OFF>
+__device__ __forceinline__ void lds_read8(bf16x8 (&a)[4], bf16x8 (&b)[4], uint32_t a0, uint32_t a1) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%10\n\t"
+      "ds_read_b128 %1, %8 offset:%11\n\t"
+      "ds_read_b128 %2, %8 offset:%12\n\t"
+      "ds_read_b128 %3, %8 offset:%13\n\t"
+      "ds_read_b128 %4, %9 offset:%10\n\t"
+      "ds_read_b128 %5, %9 offset:%11\n\t"
+      "ds_read_b128 %6, %9 offset:%12\n\t"
+      "ds_read_b128 %7, %9 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(a[0]), "=v"(a[1]), "=v"(a[2]), "=v"(a[3]), "=v"(b[0]), "=v"(b[1]), "=v"(b[2]), "=v"(b[3])
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
+      : "memory");
+}
+
 constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 
@@ -271,20 +291,20 @@ __device__ __forceinline__ void fa_bf16_item(
       f32x16 s[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = f32x16{};
-      {
-        bf16x8 fa[4], fb[4];
-        lds_read4<0>(fa, kx[0] + so);
+      bf16x8 fa[4], fb[4];
+      lds_read8<0>(fa, fb, kx[0] + so, kx[1] + so);
 #pragma unroll
-        for (int c = 0; c < 8; c += 2) {
+      for (int c = 0; c < 8; c += 2) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
-          __builtin_amdgcn_sched_barrier(0);
-          lds_read4<0>(fb, kx[c + 1] + so);
+        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (c + 2 < 8) lds_read4<0>(fa, kx[c + 2] + so);
-        }
+        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < 8)
+          lds_read8<0>(fa, fb, kx[c + 2] + so, kx[c + 3] + so);
+        else  // first V^T fragments, behind the tail of the score MFMAs
+          lds_read8<TILE_BYTES>(fa, fb, kx[0] + so, kx[1] + so);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (kb == qmine) {  // diagonal tile: keys after the query are masked
 #pragma unroll
@@ -325,20 +345,15 @@ __device__ __forceinline__ void fa_bf16_item(
           pb[mm][j] = pr[0];
           pb[mm][j + 1] = pr[1];
         }
-      {
-        bf16x8 fa[4], fb[4];
-        lds_read4<TILE_BYTES>(fa, kx[0] + so);
 #pragma unroll
-        for (int mm = 0; mm < 8; mm += 2) {
+      for (int mm = 0; mm < 8; mm += 2) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], pb[mm], acc[u]);
-          __builtin_amdgcn_sched_barrier(0);
-          lds_read4<TILE_BYTES>(fb, kx[mm + 1] + so);
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], pb[mm], acc[u]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], pb[mm + 1], acc[u]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (mm + 2 < 8) lds_read4<TILE_BYTES>(fa, kx[mm + 2] + so);
-        }
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], pb[mm + 1], acc[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (mm + 2 < 8) lds_read8<TILE_BYTES>(fa, fb, kx[mm + 2] + so, kx[mm + 3] + so);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     kb = kb1; a0 = a1; b0 = b1;
