@@ -41,6 +41,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def profiled_traffic():
+    """HBM bytes per launch of the sparse attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel source (matching sha256 prefix of attn.hip); otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_llama512k_hbm_counters.txt")
+    src = os.path.join(ROOT, "dynamic_sparse_prefill_amd", "csrc", "attn.hip")
+    try:
+        text = open(path).read()
+        want = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if f"attn.hip sha256:{want}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("sparse attention traffic_bytes_per_launch:"):
+            return int(line.split(":")[1].split()[0])
+    return None
+
+
 def timed(fn, steps, warmup, torch):
     """Mean ms per call over `steps` calls after `warmup`, bracketed by device syncs."""
     for _ in range(warmup):
@@ -237,7 +257,8 @@ def main():
         "density": round(main_res["density"], 4),
         "heads": {"vs": main_res["vs_heads"], "pe": main_res["pe_heads"]},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic() if args.workload == 4 else None,
                      "kernel": "fa_bf16_kernel<false> (sparse attention; event time includes the V re-layout)",
                      "flops_per_launch": main_res["tiles"] * TILE_FLOPS},
         "dense_roofline": ({"achieved": round(main_res["dense_tflops"], 2),
