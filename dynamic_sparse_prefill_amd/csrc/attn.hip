@@ -99,9 +99,14 @@ struct TileCopy {
   }
   __device__ void issue(const char* src, uint32_t lds, int wu) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (lds_void*)(uintptr_t)(lds + (16 * wu + 4 * i) * 256),
+    for (int i = 0; i < 4; ++i) {
+      // keep only the 32-bit offset live across the loop: the 64-bit address is
+      // formed right before the copy instead of being hoisted (register pressure)
+      uint32_t o = off[i];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds((const void*)(src + o), (lds_void*)(uintptr_t)(lds + (16 * wu + 4 * i) * 256),
                                        16, 0, 0);
+    }
   }
 };
 
@@ -307,11 +312,14 @@ __device__ __forceinline__ void fa_bf16_item(
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kb == qmine) {  // diagonal tile: keys after the query are masked
+        // key 32t + 8(i/4) + 4g + i%4 > qrow  <=>  32t + 8(i/4) + i%4 > lim; lim is
+        // formed from kb so the 64 compares are not hoisted out of the loop
+        const int lim = qrow - 4 * g + (kb - qmine) * BLK;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (32 * t + mfma32_row(i, g) > qrow) s[t][i] = -INFINITY;
+            if (32 * t + 8 * (i >> 2) + (i & 3) > lim) s[t][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -332,10 +340,10 @@ __device__ __forceinline__ void fa_bf16_item(
       }
       const float mb = m * sl2;
       // P in bf16, already in the B-operand order of the O^T MFMAs; the row sum
-      // is taken over the same rounded values (v_dot2 with (1, 1)).
+      // is taken over the same rounded values (v_dot2 with (1, 1)).  P for key
+      // chunks mm+2, mm+3 is formed while the MFMAs of chunks mm, mm+1 run.
       bf16x8 pb[8];
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm)
+      auto form_p = [&](int mm) {
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
           bf16x2 pr;
@@ -345,6 +353,9 @@ __device__ __forceinline__ void fa_bf16_item(
           pb[mm][j] = pr[0];
           pb[mm][j + 1] = pr[1];
         }
+      };
+      form_p(0);
+      form_p(1);
 #pragma unroll
       for (int mm = 0; mm < 8; mm += 2) {
 #pragma unroll
@@ -352,7 +363,12 @@ __device__ __forceinline__ void fa_bf16_item(
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], pb[mm + 1], acc[u]);
         __builtin_amdgcn_sched_barrier(0);
-        if (mm + 2 < 8) lds_read8<TILE_BYTES>(fa, fb, kx[mm + 2] + so, kx[mm + 3] + so);
+        if (mm + 2 < 8) {
+          form_p(mm + 2);
+          form_p(mm + 3);
+          __builtin_amdgcn_sched_barrier(0);
+          lds_read8<TILE_BYTES>(fa, fb, kx[mm + 2] + so, kx[mm + 3] + so);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
