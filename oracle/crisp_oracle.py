@@ -39,6 +39,21 @@ against gamma * sum(P), ties broken by lower flat (row-major) index, plus the
 two anchors per row; the min-budget top-up takes the largest remaining score,
 ties to the lower index.
 
+Variants the pages compare CRISP against (same proxy, same lists, same
+attention; only a decision rule changes):
+
+* [CRISP §2, FlexPrefill background] JSD router: the pooled estimate
+               a_bar = softmax over key blocks of the pooled last-block query
+               against the block means of K (softmax after pooling), the
+               per-query mean a_hat = the block-pooled column mean of A_hat
+               (softmax before averaging, i.e. p^v); Vertical-Slash iff
+               JSD(a_bar, a_hat) >= tau.
+* [CRISP §2, FlexPrefill background] coverage budget for Vertical-Slash:
+               each direction sorted by descending score and accumulated until
+               the mass reaches gamma, union plus the first and last blocks.
+* [CRISP appendix on the noise floor, median alternative] the floor is the
+               median of the non-anchor block scores instead of their mean.
+
 Decision arithmetic (route, mu, threshold) is spelled out in float32 in a
 fixed order so that, given the GPU's float32 scores, the oracle's decisions are
 the exact ones the GPU must reproduce.
@@ -146,6 +161,40 @@ def route_tie(c: float, tau: float) -> bool:
     return abs(float(c) - float(tau)) <= TIE_REL * abs(float(tau))
 
 
+def pooled_estimate(q_last: np.ndarray, k: np.ndarray, blk: int) -> np.ndarray:
+    """a_bar: softmax over the key blocks of (mean of the last block's query
+    rows) . (block mean of K) / sqrt(d) -- softmax applied after pooling
+    queries and keys [CRISP §2, FlexPrefill's pooled estimate].  Every key
+    block takes part (all of them precede or contain the last query block)."""
+    d = q_last.shape[1]
+    qm = q_last.astype(np.float64).mean(axis=0)
+    L = block_means(k, blk) @ qm / math.sqrt(d)
+    e = np.exp(L - L.max())
+    return e / e.sum()
+
+
+def jsd(a: np.ndarray, b: np.ndarray) -> float:
+    """Jensen-Shannon divergence with natural logarithms:
+    JSD = KL(a || m)/2 + KL(b || m)/2, m = (a + b)/2, terms with a zero weight
+    contribute 0.  Bounded by ln 2."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    m = 0.5 * (a + b)
+
+    def kl(x):
+        nz = x > 0
+        return float(np.sum(x[nz] * np.log(x[nz] / m[nz])))
+
+    return 0.5 * kl(a) + 0.5 * kl(b)
+
+
+def route_jsd(j: float, tau: float) -> bool:
+    """FlexPrefill's router as the pages state it: Vertical-Slash iff
+    JSD(a_bar, a_hat) >= tau [CRISP §2]; the divergence is a float64 value,
+    tau the float32 parameter."""
+    return bool(float(j) >= float(np.float32(tau)))
+
+
 # =============================================================== stage 3a: Vertical-Slash selection
 
 def noise_floor_f32(p: np.ndarray) -> np.float32:
@@ -175,12 +224,85 @@ def vs_select_direction(p: np.ndarray, alpha: float, min_blocks: int = 0) -> np.
     sel = p > thr
     sel[0] = True
     sel[nb - 1] = True
-    need = min(min_blocks, nb) - int(sel.sum())
+    return _top_up(sel, p, min_blocks)
+
+
+def median_floor_f32(p: np.ndarray) -> np.float32:
+    """Median of the non-anchor scores p_1 .. p_{N_b-2} in float32 [CRISP
+    appendix on the noise floor: the median as the robust alternative to the
+    mean over non-retained blocks].  For an even count it is the float32 mean
+    of the two middle values, (a + b) * 0.5, rounded once per operation."""
+    p = np.asarray(p, np.float32)
+    r = np.sort(p[1:-1])[::-1]
+    m = r.size
+    if m % 2:
+        return np.float32(r[(m - 1) // 2])
+    return np.float32(np.float32(r[m // 2 - 1] + r[m // 2]) * np.float32(0.5))
+
+
+def vs_select_median(p: np.ndarray, alpha: float, min_blocks: int = 0) -> np.ndarray:
+    """S_d = {k : p_k > alpha * median} plus the anchors 0 and N_b - 1, topped up
+    like vs_select_direction."""
+    p = np.asarray(p, np.float32)
+    nb = p.shape[0]
+    thr = np.float32(np.float32(alpha) * median_floor_f32(p))
+    sel = p > thr
+    sel[0] = True
+    sel[nb - 1] = True
+    return _top_up(sel, p, min_blocks)
+
+
+def _top_up(sel: np.ndarray, p: np.ndarray, min_blocks: int) -> np.ndarray:
+    need = min(min_blocks, sel.size) - int(sel.sum())
     if need > 0:
         rest = np.flatnonzero(~sel)
         order = sorted(rest, key=lambda i: (-float(p[i]), int(i)))
         sel[np.array(order[:need], dtype=int)] = True
     return np.flatnonzero(sel)
+
+
+def median_ties(p: np.ndarray, alpha: float) -> np.ndarray:
+    """Indices whose score lies within 1e-6 relative of alpha * median."""
+    p = np.asarray(p, np.float32)
+    thr = float(np.float32(np.float32(alpha) * median_floor_f32(p)))
+    band = TIE_REL * max(thr, float(FLT_MIN))
+    return np.flatnonzero(np.abs(p.astype(np.float64) - thr) <= band)
+
+
+def coverage_cut(vals: np.ndarray, gamma: float):
+    """Shortest prefix of the entries in descending order (ties to the lower
+    index) whose sum reaches gamma * sum(vals); gamma >= 1 keeps everything.
+    Sums in extended precision.  Returns (kept indices, info) with the same
+    info fields as pe_cut."""
+    vals = np.asarray(vals, np.float64)
+    idx = np.arange(vals.size)
+    order = np.lexsort((idx, -vals))
+    csum = np.cumsum(vals[order].astype(np.longdouble))
+    total = csum[-1] if vals.size else np.longdouble(0)
+    if gamma >= 1.0:
+        kstar, target = vals.size, total
+    else:
+        target = np.longdouble(gamma) * total
+        kstar = min(int(np.searchsorted(csum, target, side="left")) + 1, vals.size)
+    info = dict(kstar=kstar, target=float(target), total=float(total), entries=int(vals.size),
+                prefix=float(csum[kstar - 1]) if kstar > 0 else 0.0,
+                prefix_before=float(csum[kstar - 2]) if kstar > 1 else 0.0)
+    return order[:kstar], info
+
+
+def vs_select_coverage(p: np.ndarray, gamma: float, min_blocks: int = 0):
+    """FlexPrefill's Vertical-Slash budget for one direction [CRISP §2]: the
+    blocks sorted by descending score and accumulated until the mass reaches
+    gamma of the direction's total, plus the anchors 0 and N_b - 1, topped up
+    like vs_select_direction.  Returns (sorted indices, cut info)."""
+    p = np.asarray(p, np.float32)
+    nb = p.shape[0]
+    keep, info = coverage_cut(p.astype(np.float64), gamma)
+    sel = np.zeros(nb, bool)
+    sel[keep] = True
+    sel[0] = True
+    sel[nb - 1] = True
+    return _top_up(sel, p, min_blocks), info
 
 
 def vs_ties(p: np.ndarray, alpha: float) -> np.ndarray:
@@ -369,12 +491,32 @@ def mask_matrix(lists, n, blk):
 
 # =============================================================== per-head pipeline
 
-def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, dense_below_n=0):
+def _vs_sets(pv, ps, alpha, gamma, min_blocks, budget):
+    """Both Vertical-Slash directions under one budget rule: "mean" (the CRISP
+    noise floor), "median" (median floor) or "coverage" (FlexPrefill's
+    gamma-cumsum).  Returns (sv, ss, infos)."""
+    pv = np.asarray(pv, np.float32)
+    ps = np.asarray(ps, np.float32)
+    if budget == "mean":
+        return vs_select_direction(pv, alpha, min_blocks), vs_select_direction(ps, alpha, min_blocks), None
+    if budget == "median":
+        return vs_select_median(pv, alpha, min_blocks), vs_select_median(ps, alpha, min_blocks), None
+    if budget == "coverage":
+        sv, iv = vs_select_coverage(pv, gamma, min_blocks)
+        ss, is_ = vs_select_coverage(ps, gamma, min_blocks)
+        return sv, ss, (iv, is_)
+    raise ValueError(budget)
+
+
+def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, dense_below_n=0,
+                router="cstruct", budget="mean"):
     """Stages 1-3 for one query head from its own Q [n, d] and its KV head's K.
 
     Returns a dict with the float64 scores, the decisions and the per-block
     lists.  route is 1 (VS), 0 (PE) or -1 (dense fallback: N_b <= 2, or n below
     the length gate, where mu is undefined or sparsity does not pay).
+    router "cstruct" (CRISP) or "jsd" (FlexPrefill); budget "mean" (CRISP),
+    "median" or "coverage" (FlexPrefill) for Vertical-Slash heads.
     """
     n = k.shape[0]
     nb = n // blk
@@ -386,12 +528,16 @@ def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, den
     pv, ps = vertical_scores(A, blk), slash_scores(A, blk)
     cs = c_struct(A, w_sink, w_local)
     out.update(pv=pv, ps=ps, c_struct=cs)
-    vs = route_decision(np.float32(cs), tau)
+    if router == "jsd":
+        abar = pooled_estimate(q[n - blk:], k, blk)
+        out.update(abar=abar, jsd=jsd(abar, pv))
+        vs = route_jsd(out["jsd"], tau)
+    else:
+        vs = route_decision(np.float32(cs), tau)
     out["route"] = 1 if vs else 0
     if vs:
-        sv = vs_select_direction(pv.astype(np.float32), alpha, min_blocks)
-        ss = vs_select_direction(ps.astype(np.float32), alpha, min_blocks)
-        out.update(sv=sv, ss=ss, lists=vs_block_lists(sv, ss, nb))
+        sv, ss, infos = _vs_sets(pv, ps, alpha, float(np.float32(gamma)), min_blocks, budget)
+        out.update(sv=sv, ss=ss, vs_info=infos, lists=vs_block_lists(sv, ss, nb))
     else:
         P = pe_probabilities(q, k, blk)
         mask, info = pe_cut(P, float(np.float32(gamma)))
@@ -399,27 +545,32 @@ def select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks=0, den
     return out
 
 
-def decide_from_scores(route_in, c, pv, ps, P, nb, tau, alpha, gamma, min_blocks=0):
+def decide_from_scores(route_in, c, pv, ps, P, nb, tau, alpha, gamma, min_blocks=0, router="cstruct",
+                       budget="mean", abar=None):
     """Stages 2-3 given float32 scores computed elsewhere (the GPU's).
 
     route_in == -1 marks the dense fallback.  Returns (route, sv, ss, lists,
-    info); P is only read for Pooled-Estimation heads.
+    info); P is only read for Pooled-Estimation heads.  With router "jsd" the
+    route is JSD(abar, pv) >= tau on the given float32 abar and pv; with budget
+    "coverage" info holds the two directions' cut infos for VS heads.
     """
     if route_in == -1:
         return -1, None, None, dense_lists(nb), None
     gamma = float(np.float32(gamma))        # the parameter as the float32 it is passed as
-    vs = route_decision(np.float32(c), tau)
+    if router == "jsd":
+        vs = route_jsd(jsd(np.asarray(abar, np.float32), np.asarray(pv, np.float32)), tau)
+    else:
+        vs = route_decision(np.float32(c), tau)
     if vs:
-        sv = vs_select_direction(np.asarray(pv, np.float32), alpha, min_blocks)
-        ss = vs_select_direction(np.asarray(ps, np.float32), alpha, min_blocks)
-        return 1, sv, ss, vs_block_lists(sv, ss, nb), None
+        sv, ss, infos = _vs_sets(pv, ps, alpha, gamma, min_blocks, budget)
+        return 1, sv, ss, vs_block_lists(sv, ss, nb), infos
     mask, info = pe_cut(np.asarray(P, np.float32).astype(np.float64), gamma)
     return 0, None, None, mask_to_lists(mask), info
 
 
 def prefill_head(q, k, v, blk=128, w_sink=128, w_local=128, tau=0.3, alpha=1.0, gamma=0.95,
-                 min_blocks=0, dense_below_n=0):
+                 min_blocks=0, dense_below_n=0, router="cstruct", budget="mean"):
     """All four stages for one head: selection then block-sparse attention."""
-    sel = select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks, dense_below_n)
+    sel = select_head(q, k, blk, w_sink, w_local, tau, alpha, gamma, min_blocks, dense_below_n, router, budget)
     sel["O"] = block_sparse_attention(q, k, v, sel["lists"], blk)
     return sel

@@ -331,3 +331,138 @@ def test_dense_fallback_cases():
     q, k = _rand((512, 16), 63), _rand((512, 16), 64)
     r = O.select_head(q, k, 128, 128, 128, 0.3, 1.0, 0.95, dense_below_n=1024)
     assert r["route"] == -1
+
+
+# ------------------------------------------------------------------ variants: median floor, coverage budget, JSD router
+
+def test_median_floor_golden_cases():
+    """Hand-worked: non-anchor scores .1 .2 .05 .3 have median (.1 + .2)/2 = .15,
+    so alpha = 1 keeps blocks 2 (.2) and 4 (.3) plus the anchors; with an odd
+    count .3 .1 .05 the median is .1 and only block 1 exceeds it."""
+    p = np.array([0.5, 0.1, 0.2, 0.05, 0.3, 0.2], np.float32)
+    assert O.median_floor_f32(p) == np.float32(0.15)
+    assert O.vs_select_median(p, 1.0).tolist() == [0, 2, 4, 5]
+    p = np.array([0.4, 0.3, 0.1, 0.05, 0.15], np.float32)
+    assert O.median_floor_f32(p) == np.float32(0.1)
+    assert O.vs_select_median(p, 1.0).tolist() == [0, 1, 4]
+    assert O.vs_select_median(p, 0.4).tolist() == [0, 1, 2, 3, 4]     # .1 > .04, .05 > .04
+    assert O.vs_select_median(p, 0.6).tolist() == [0, 1, 2, 4]        # .05 is not > .06
+
+
+def test_median_floor_is_robust_to_one_dominant_block():
+    """The pages' motivation for the median: one dominant block lifts the mean
+    floor above a weak genuine block.  Here mu = (1 - .3 - .18)/9 = .0578 drops
+    block 7 (.03) under the mean rule, while the median of the nine non-anchor
+    scores is .01 and keeps it."""
+    p = np.array([0.3, 0.4, 0.02, 0.02, 0.01, 0.01, 0.01, 0.03, 0.01, 0.01, 0.18], np.float32)
+    assert abs(float(p.astype(np.float64).sum()) - 1.0) < 1e-6
+    assert 7 not in O.vs_select_direction(p, 1.0).tolist()
+    assert O.median_floor_f32(p) == np.float32(0.01)
+    assert O.vs_select_median(p, 1.0).tolist() == [0, 1, 2, 3, 7, 10]
+
+
+def test_median_floor_matches_library_median():
+    rng = np.random.default_rng(71)
+    for nb in [3, 4, 5, 64, 65, 1000]:
+        p = rng.random(nb).astype(np.float32)
+        ref = float(np.median(p[1:-1].astype(np.float64)))
+        assert abs(float(O.median_floor_f32(p)) - ref) <= 2 * np.finfo(np.float32).eps * ref
+
+
+def test_coverage_golden_and_ties():
+    """Scores .5 .1 .2 .05 .3 .2 (sum 1.35), gamma .95: target 1.2825; sorted
+    .5 .3 .2 .2 .1 reach 1.3 at the fifth entry, so every block but 3 is kept.
+    Four equal scores with gamma .5: the two lowest indices are taken."""
+    p = np.array([0.5, 0.1, 0.2, 0.05, 0.3, 0.2], np.float32)
+    sel, info = O.vs_select_coverage(p, 0.95)
+    assert sel.tolist() == [0, 1, 2, 4, 5] and info["kstar"] == 5
+    q = np.array([0.25, 0.25, 0.25, 0.25, 0.0, 0.0], np.float32)
+    keep, info = O.coverage_cut(q, 0.5)
+    assert sorted(keep.tolist()) == [0, 1] and info["kstar"] == 2
+    sel, _ = O.vs_select_coverage(q, 0.5)
+    assert sel.tolist() == [0, 1, 5]                                   # anchors 0 and N_b - 1 added
+
+
+def test_coverage_brute_force_minimum_cardinality():
+    """The coverage prefix is a smallest subset reaching gamma of the mass, and
+    no subset of that size carries more."""
+    rng = np.random.default_rng(73)
+    for trial in range(60):
+        nb = int(rng.integers(3, 11))
+        p = rng.dirichlet(np.full(nb, float(rng.uniform(0.2, 3.0))))
+        gamma = float(rng.uniform(0.3, 0.99))
+        T = p.sum()
+        best = None
+        for r in range(1, nb + 1):
+            ok = [sum(p[list(c)]) for c in itertools.combinations(range(nb), r) if sum(p[list(c)]) >= gamma * T]
+            if ok:
+                best = (r, max(ok))
+                break
+        keep, info = O.coverage_cut(p, gamma)
+        assert info["kstar"] == best[0] == len(keep)
+        assert abs(info["prefix"] - best[1]) < 1e-12
+
+
+def test_coverage_limits_and_monotone():
+    rng = np.random.default_rng(79)
+    p = rng.dirichlet(np.full(40, 0.5)).astype(np.float32)
+    assert O.vs_select_coverage(p, 1.0)[0].tolist() == list(range(40))
+    prev = set()
+    for gamma in [0.1, 0.3, 0.6, 0.9, 0.95, 0.99]:
+        s = set(O.vs_select_coverage(p, gamma)[0].tolist())
+        assert {0, 39} <= s and prev <= s
+        prev = s
+
+
+def test_jsd_matches_library_and_limits():
+    from scipy.spatial.distance import jensenshannon
+    rng = np.random.default_rng(83)
+    for trial in range(20):
+        a = rng.dirichlet(np.ones(17))
+        b = rng.dirichlet(np.ones(17) * 0.3)
+        assert abs(O.jsd(a, b) - jensenshannon(a, b) ** 2) < 1e-12
+        assert abs(O.jsd(a, b) - O.jsd(b, a)) < 1e-15
+        assert O.jsd(a, a) == 0.0
+    a = np.array([0.5, 0.5, 0.0, 0.0])
+    b = np.array([0.0, 0.0, 0.25, 0.75])
+    assert abs(O.jsd(a, b) - math.log(2.0)) < 1e-15                    # disjoint supports
+
+
+def test_pooled_estimate_closed_forms():
+    """Q = 0 gives the uniform distribution over blocks; adding one vector to
+    every key shifts every pooled logit equally and changes nothing; a block
+    whose mean key is a large multiple of the pooled query takes all the mass."""
+    rng = np.random.default_rng(89)
+    blk, nb, d = 4, 6, 8
+    k = rng.standard_normal((nb * blk, d))
+    q0 = np.zeros((blk, d))
+    assert np.allclose(O.pooled_estimate(q0, k, blk), np.full(nb, 1.0 / nb), atol=1e-15)
+    q = rng.standard_normal((blk, d))
+    a = O.pooled_estimate(q, k, blk)
+    assert abs(a.sum() - 1.0) < 1e-12
+    assert np.allclose(O.pooled_estimate(q, k + rng.standard_normal(d), blk), a, atol=1e-12)
+    k2 = k.copy()
+    k2[2 * blk:3 * blk] += 200.0 * q.mean(axis=0) / np.linalg.norm(q.mean(axis=0))
+    assert O.pooled_estimate(q, k2, blk)[2] > 1 - 1e-12
+
+
+def test_jsd_router_threshold_and_variants_on_tiny_layer():
+    """JSD routing is VS iff JSD >= tau, so the VS set shrinks as tau grows;
+    the variants produce valid lists (ascending, anchors present, causal)."""
+    from workloads import synth
+    spec = synth.make_spec(synth.CONFIGS[0])
+    cfg = spec.cfg
+    Q, K, V = synth.generate(spec)
+    js = []
+    for h in range(2):
+        q, k = Q[h].astype(np.float64), K[h].astype(np.float64)
+        r = O.select_head(q, k, 128, 128, 128, 0.0, cfg.alpha, cfg.gamma, router="jsd", budget="coverage")
+        assert r["route"] == 1 and 0.0 <= r["jsd"] <= math.log(2.0)
+        js.append(r["jsd"])
+        for budget in ["mean", "median", "coverage"]:
+            r = O.select_head(q, k, 128, 128, 128, 0.0, cfg.alpha, cfg.gamma, router="jsd", budget=budget)
+            for qb, l in enumerate(r["lists"]):
+                assert l[0] == 0 and l[-1] == qb and np.all(np.diff(l) > 0)
+    for tau in [0.0, min(js), max(js), max(js) + 1e-9]:
+        vs = [O.route_jsd(j, tau) for j in js]
+        assert vs == [j >= float(np.float32(tau)) for j in js]
