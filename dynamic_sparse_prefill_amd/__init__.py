@@ -3,10 +3,10 @@
 The computation lives in libcrisp.so (hand-written HIP kernels behind the C
 ABI in include/crisp.h); this package only marshals PyTorch tensors into it.
 """
-from .api import (BLOCK, CrispError, CrispParams, Selection, attn_workspace_bytes, col_capacity,
-                  crisp_dense_attn, crisp_prefill, crisp_select, crisp_sparse_attn, lib, make_shape,
-                  new_selection, select_workspace_bytes, workspace_bytes)
+from .api import (BLOCK, FLAG_ROUTE_JSD, FLAG_VS_COVERAGE, FLAG_VS_MEDIAN, CrispError, CrispParams, Selection,
+                  attn_workspace_bytes, col_capacity, crisp_dense_attn, crisp_prefill, crisp_select,
+                  crisp_sparse_attn, lib, make_shape, new_selection, select_workspace_bytes, workspace_bytes)
 
-__all__ = ["BLOCK", "CrispError", "CrispParams", "Selection", "attn_workspace_bytes", "col_capacity",
-           "crisp_dense_attn", "crisp_prefill", "crisp_select", "crisp_sparse_attn", "lib", "make_shape",
-           "new_selection", "select_workspace_bytes", "workspace_bytes"]
+__all__ = ["BLOCK", "FLAG_ROUTE_JSD", "FLAG_VS_COVERAGE", "FLAG_VS_MEDIAN", "CrispError", "CrispParams",
+           "Selection", "attn_workspace_bytes", "col_capacity", "crisp_dense_attn", "crisp_prefill", "crisp_select",
+           "crisp_sparse_attn", "lib", "make_shape", "new_selection", "select_workspace_bytes", "workspace_bytes"]

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(HERE, "libcrisp.so")
 
 BLOCK = 128
 BF16, FP32 = 0, 1
+# crisp_params.flags (include/crisp.h): variants the pages compare CRISP against
+FLAG_ROUTE_JSD, FLAG_VS_MEDIAN, FLAG_VS_COVERAGE = 1, 2, 4
 
 EXPORTS = ("crisp_select_workspace_bytes", "crisp_attn_workspace_bytes", "crisp_workspace_bytes",
            "crisp_col_capacity", "crisp_select", "crisp_sparse_attn", "crisp_dense_attn",
@@ -43,7 +45,8 @@ class CrispParamsC(C.Structure):
 class CrispSelectionC(C.Structure):
     _fields_ = [("route", C.c_void_p), ("c_struct", C.c_void_p), ("row_ptr", C.c_void_p), ("col_idx", C.c_void_p),
                 ("col_capacity", C.c_int64), ("pv", C.c_void_p), ("ps", C.c_void_p), ("sv", C.c_void_p),
-                ("nv", C.c_void_p), ("ss", C.c_void_p), ("ns", C.c_void_p), ("pe_prob", C.c_void_p)]
+                ("nv", C.c_void_p), ("ss", C.c_void_p), ("ns", C.c_void_p), ("pe_prob", C.c_void_p),
+                ("jsd", C.c_void_p), ("abar", C.c_void_p)]
 
 
 class CrispError(RuntimeError):
@@ -121,13 +124,15 @@ class Selection:
     ss: torch.Tensor | None = None
     ns: torch.Tensor | None = None
     pe_prob: torch.Tensor | None = None
+    jsd: torch.Tensor | None = None   # [hq] float64, written with FLAG_ROUTE_JSD
+    abar: torch.Tensor | None = None  # [hq*nb] float32 pooled estimate, written with FLAG_ROUTE_JSD
     extra: dict = field(default_factory=dict)
 
     def c(self) -> CrispSelectionC:
         p = lambda t: t.data_ptr() if t is not None else None
         return CrispSelectionC(p(self.route), p(self.c_struct), p(self.row_ptr), p(self.col_idx),
                                self.col_idx.numel(), p(self.pv), p(self.ps), p(self.sv), p(self.nv), p(self.ss),
-                               p(self.ns), p(self.pe_prob))
+                               p(self.ns), p(self.pe_prob), p(self.jsd), p(self.abar))
 
 
 # ------------------------------------------------------------------ marshalling
@@ -205,6 +210,8 @@ def new_selection(q: torch.Tensor, k: torch.Tensor, diagnostics: bool = True, pe
         sel.pv, sel.ps = torch.empty(hq * nb, **f32), torch.empty(hq * nb, **f32)
         sel.sv, sel.ss = torch.empty(hq * nb, **i32), torch.empty(hq * nb, **i32)
         sel.nv, sel.ns = torch.empty(hq, **i32), torch.empty(hq, **i32)
+        sel.jsd = torch.zeros(hq, dtype=torch.float64, device=dev)
+        sel.abar = torch.zeros(hq * nb, **f32)
     if pe_prob:
         sel.pe_prob = torch.empty(hq * nb * (nb + 1) // 2, **f32)
     return sel

@@ -46,7 +46,10 @@ int check_params(const crisp_shape* s, const crisp_params* p) {
   if (p->sink < 0 || p->local < 0 || p->sink > s->n || p->local > s->n) return CRISP_E_ARG;
   if (!(p->tau >= 0.f) || !(p->alpha >= 0.f) || !isfinite(p->tau) || !isfinite(p->alpha)) return CRISP_E_ARG;
   if (!(p->gamma > 0.f) || !(p->gamma <= 1.f)) return CRISP_E_ARG;
-  if (p->min_blocks < 0 || p->dense_below_n < 0 || p->flags != 0) return CRISP_E_ARG;
+  if (p->min_blocks < 0 || p->dense_below_n < 0) return CRISP_E_ARG;
+  const int known = CRISP_FLAG_ROUTE_JSD | CRISP_FLAG_VS_MEDIAN | CRISP_FLAG_VS_COVERAGE;
+  if (p->flags & ~known) return CRISP_E_ARG;
+  if ((p->flags & CRISP_FLAG_VS_MEDIAN) && (p->flags & CRISP_FLAG_VS_COVERAGE)) return CRISP_E_ARG;
   return CRISP_OK;
 }
 
@@ -58,7 +61,8 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
-  size_t stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, total;
+  size_t stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
+      total;
 };
 
 SelectLayout select_layout(const crisp_shape* s) {
@@ -83,6 +87,8 @@ SelectLayout select_layout(const crisp_shape* s) {
   L.cut = take(hq * pe_cut_state_bytes());
   L.eqrow = take(hq * nb * 4);
   L.counts = take(hq * nb * 4);
+  L.jsd = take(hq * 8);
+  L.abar = take(hq * nb * 4);
   L.total = o;
   return L;
 }
@@ -172,6 +178,10 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.nv_out = out->nv;
   b.ss_out = out->ss;
   b.ns_out = out->ns;
+  b.jsd = out->jsd ? out->jsd : (double*)(w + L.jsd);
+  b.abar = out->abar ? out->abar : (float*)(w + L.abar);
+  b.router = (p->flags & CRISP_FLAG_ROUTE_JSD) ? 1 : 0;
+  b.vs_budget = (p->flags & CRISP_FLAG_VS_MEDIAN) ? 1 : ((p->flags & CRISP_FLAG_VS_COVERAGE) ? 2 : 0);
   return status_of(launch_select(fp32, dense, q, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, p->tau,
                                  p->alpha, p->gamma, p->min_blocks, b, stream));
 }

@@ -41,6 +41,9 @@ struct SelectBufs {
   // caller outputs
   int32_t* route; float* c_struct; int32_t *row_ptr, *col_idx;
   float *pv_out, *ps_out; int32_t *sv_out, *nv_out, *ss_out, *ns_out;
+  // variants: router 0 = C_struct, 1 = JSD; vs_budget 0 = mean floor, 1 = median floor, 2 = coverage
+  double* jsd; float* abar;
+  int router, vs_budget;
 };
 
 hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,

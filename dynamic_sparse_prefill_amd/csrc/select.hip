@@ -19,6 +19,15 @@
 //              selected entries of the row plus (qb, 0) and (qb, qb), dense
 //              rows = 0..qb.
 //
+// Variants the pages compare against (selected by flags):
+//  jsd_route   FlexPrefill's router [CRISP §2]: pooled estimate a_bar =
+//              softmax over key blocks of mean(Q_last) . Kbar / sqrt(d), and
+//              JSD(a_bar, p^v) in float64; Vertical-Slash iff JSD >= tau.
+//  vs_rank     per (head, direction) of a Vertical-Slash head: the median
+//              noise floor [CRISP appendix on the floor] or FlexPrefill's
+//              coverage budget (descending scores until gamma of the mass)
+//              [CRISP §2], both by radix selection on the float32 bits.
+//
 // The decision arithmetic (route, mu, threshold) is written with explicit
 // round-to-nearest float32 operations in a fixed order so that it can be
 // reproduced exactly on the host from the same float32 scores.
@@ -110,9 +119,9 @@ __device__ void top_up(uint8_t* flag, const float* p, int nb, int want, float* s
 
 __global__ __launch_bounds__(256) void vs_select_kernel(
     const float4* __restrict__ tiles, int64_t n, int nb, int w_sink, int w_local, float tau, float alpha,
-    int min_blocks, int dense, int32_t* __restrict__ route, float* __restrict__ c_struct, float* __restrict__ pv,
-    float* __restrict__ ps, int32_t* __restrict__ sv, int32_t* __restrict__ nv, int32_t* __restrict__ ss,
-    int32_t* __restrict__ ns, float* pv_out, float* ps_out) {
+    int min_blocks, int dense, const double* __restrict__ jsd, int vs_budget, int32_t* __restrict__ route,
+    float* __restrict__ c_struct, float* __restrict__ pv, float* __restrict__ ps, int32_t* __restrict__ sv,
+    int32_t* __restrict__ nv, int32_t* __restrict__ ss, int32_t* __restrict__ ns, float* pv_out, float* ps_out) {
   extern __shared__ uint8_t flag[];  // nb bytes
   __shared__ int shi[256];
   __shared__ float shv[256];
@@ -145,12 +154,13 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     }
     c = __fmul_rn(c, inv_b);
     c_struct[h] = c;
-    const int r = (c >= tau) ? 1 : 0;
+    // jsd != NULL: FlexPrefill's router on the float64 divergence
+    const int r = (jsd ? (jsd[h] >= (double)tau) : (c >= tau)) ? 1 : 0;
     route[h] = r;
     s_route = r;
   }
   __syncthreads();
-  if (s_route != 1) {
+  if (s_route != 1 || vs_budget != 0) {   // other budgets: vs_rank_kernel writes the sets
     if (tid == 0) { nv[h] = 0; ns[h] = 0; }
     return;
   }
@@ -167,6 +177,296 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     if (min_blocks > 0) top_up(flag, p, nb, min(min_blocks, nb), shv, shi);
     compact_flags(flag, nb, (dir == 0 ? sv : ss) + (int64_t)h * nb, (dir == 0 ? nv : ns) + h, shi);
   }
+}
+
+// ------------------------------------------------------------------ variant: JSD router
+
+__device__ float block256_max(float v, float* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) sh[tid] = fmaxf(sh[tid], sh[tid + o]);
+    __syncthreads();
+  }
+  const float r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+template <typename V>
+__device__ V block256_sum(V v, V* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) sh[tid] += sh[tid + o];
+    __syncthreads();
+  }
+  const V r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// One work-group per query head.  a_bar[kb] = softmax_kb(scale * qm . Kbar[kb]),
+// qm = mean of the head's last 128 query rows; p^v[kb] = (lower + upper)/b from
+// the proxy tile sums, exactly as vs_select forms it; then
+// JSD = (KL(a_bar || m) + KL(p^v || m)) / 2, m = (a_bar + p^v)/2, in float64
+// with natural logarithms, terms of zero weight dropped.
+template <typename T>
+__global__ __launch_bounds__(256) void jsd_route_kernel(const T* __restrict__ Q, const float4* __restrict__ tiles,
+                                                        const float* __restrict__ kbar, float* __restrict__ abar,
+                                                        double* __restrict__ jsd, int nb, int hq, int hkv,
+                                                        int64_t sq_h, int64_t sq_n, float scale) {
+  __shared__ float qm[HD];
+  __shared__ float red[2][HD];
+  __shared__ float shf[256];
+  __shared__ double shd[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int kvh = h / (hq / hkv);
+  {
+    const int d = tid & (HD - 1), half = tid >> 7;
+    const T* base = Q + (int64_t)h * sq_h + ((int64_t)(nb - 1) * BLK + 64 * half) * sq_n + d;
+    float sum = 0.f;
+    for (int r = 0; r < 64; ++r) sum += to_f32(base[(int64_t)r * sq_n]);
+    red[half][d] = sum;
+    __syncthreads();
+    if (half == 0) qm[d] = (red[0][d] + red[1][d]) * (1.f / BLK);
+    __syncthreads();
+  }
+  float* A = abar + (int64_t)h * nb;
+  const float* Kb = kbar + (int64_t)kvh * nb * HD;
+  float mx = -INFINITY;
+  for (int kb = tid; kb < nb; kb += 256) {
+    const float* kr = Kb + (int64_t)kb * HD;
+    float acc = 0.f;
+    for (int d = 0; d < HD; ++d) acc = fmaf(qm[d], kr[d], acc);
+    const float L = acc * scale;
+    A[kb] = L;
+    mx = fmaxf(mx, L);
+  }
+  mx = block256_max(mx, shf);
+  float se = 0.f;
+  for (int kb = tid; kb < nb; kb += 256) {
+    const float e = expf(A[kb] - mx);
+    A[kb] = e;
+    se += e;
+  }
+  se = block256_sum(se, shf);
+  const float4* Th = tiles + (int64_t)h * nb;
+  double acc = 0.0;
+  for (int kb = tid; kb < nb; kb += 256) {
+    const float a = __fdiv_rn(A[kb], se);
+    A[kb] = a;
+    const float4 t = Th[kb];
+    const float b = __fmul_rn(__fadd_rn(t.x, t.y), 1.f / BLK);
+    const double m = 0.5 * ((double)a + (double)b);
+    if (a > 0.f) acc += (double)a * log((double)a / m);
+    if (b > 0.f) acc += (double)b * log((double)b / m);
+  }
+  acc = block256_sum(acc, shd);
+  if (tid == 0) jsd[h] = 0.5 * acc;
+}
+
+// ------------------------------------------------------------------ variant: median floor / coverage budget
+
+// 1024-thread helpers
+__device__ int block1k_excl_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0;
+    for (int i = 0; i < 16; ++i) { const int x = sh[i]; sh[i] = a; a += x; }
+    sh[16] = a;
+  }
+  __syncthreads();
+  const int r = sh[w] + incl - v;
+  *total = sh[16];
+  __syncthreads();
+  return r;
+}
+
+__device__ unsigned long long block1k_sum_u64(unsigned long long v, unsigned long long* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) sh[tid] += sh[tid + o];
+    __syncthreads();
+  }
+  const unsigned long long r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// Radix selection over the float32 bit patterns of p[lo, hi) (values >= 0, so
+// bit order is value order), three passes of 11 / 11 / 10 bits from the top.
+// BY_MASS = false: bits of the r-th largest value (r counted from 0).
+// BY_MASS = true:  bits of the value at which the descending 2^-46 fixed-point
+// prefix mass first reaches `need`; on return *above = mass of the larger
+// values, *eq_cnt = number of entries equal to the result.
+template <bool BY_MASS>
+__device__ uint32_t radix_pick(const float* __restrict__ p, int lo, int hi, unsigned long long need,
+                               uint32_t* cnt, unsigned long long* mass, unsigned long long* above,
+                               uint32_t* eq_cnt) {
+  __shared__ uint32_t s_prefix;
+  __shared__ unsigned long long s_need, s_above;
+  __shared__ uint32_t s_eq;
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_prefix = 0; s_need = need; s_above = 0; }
+  __syncthreads();
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int width = pass == 2 ? 10 : 11;
+    const uint32_t mask = (1u << width) - 1;
+    const int top = shift + width;
+    for (int i = tid; i < PE_BUCKETS; i += 1024) { cnt[i] = 0; if (BY_MASS) mass[i] = 0; }
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    for (int k = lo + tid; k < hi; k += 1024) {
+      const uint32_t x = __float_as_uint(p[k]);
+      if (pass > 0 && (x >> top) != (prefix >> top)) continue;
+      const uint32_t b = (x >> shift) & mask;
+      atomicAdd(&cnt[b], 1u);
+      if (BY_MASS) atomicAdd(&mass[b], fx_mass(x));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long acc = 0, nd = s_need;
+      int sel = 0;
+      for (int b = (int)mask; b >= 0; --b) {
+        const unsigned long long v = BY_MASS ? mass[b] : (unsigned long long)cnt[b];
+        if (BY_MASS ? (acc + v >= nd) : (acc + v > nd)) { sel = b; break; }
+        acc += v;
+        sel = b;
+      }
+      s_need = nd - acc;
+      s_above += acc;
+      s_prefix = prefix | ((uint32_t)sel << shift);
+      s_eq = cnt[sel];
+    }
+    __syncthreads();
+  }
+  const uint32_t r = s_prefix;
+  if (above) *above = s_above;
+  if (eq_cnt) *eq_cnt = s_eq;
+  __syncthreads();
+  return r;
+}
+
+// One work-group (1024 threads) per (Vertical-Slash head, direction).
+//   MEDIAN:   thr = alpha * median(p_1 .. p_{N_b-2}) (the mean of the two middle
+//             values for an even count, (a + b) * 0.5 in float32); keep p_k > thr.
+//   COVERAGE: keep the entries in descending order (ties to the lower index)
+//             until their 2^-46 fixed-point mass reaches ceil(gamma * total),
+//             the same arithmetic as the Pooled-Estimation cut; gamma >= 1 keeps all.
+// Then the anchors 0 and N_b - 1, the optional min budget, ascending compaction.
+template <bool MEDIAN>
+__global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict__ route, const float* __restrict__ pv,
+                                                       const float* __restrict__ ps, int nb, float alpha, float gamma,
+                                                       int min_blocks, int32_t* __restrict__ sv,
+                                                       int32_t* __restrict__ nv, int32_t* __restrict__ ss,
+                                                       int32_t* __restrict__ ns) {
+  extern __shared__ uint8_t flag[];  // nb bytes
+  // radix histograms; outside the radix passes the same memory serves the
+  // block reductions (shi: 1024 ints over cnt, shv: 1024 floats over mass)
+  __shared__ uint32_t cnt[PE_BUCKETS];
+  __shared__ unsigned long long mass[PE_BUCKETS];
+  int* shi = (int*)cnt;
+  float* shv = (float*)mass;
+  const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
+  if (route[h] != 1) return;
+  const float* p = (dir == 0 ? pv : ps) + (int64_t)h * nb;
+  if (MEDIAN) {
+    const int m = nb - 2;
+    float med;
+    if (m & 1) {
+      med = __uint_as_float(radix_pick<false>(p, 1, nb - 1, (unsigned long long)((m - 1) / 2), cnt, mass,
+                                              nullptr, nullptr));
+    } else {
+      const float a = __uint_as_float(radix_pick<false>(p, 1, nb - 1, (unsigned long long)(m / 2 - 1), cnt, mass,
+                                                        nullptr, nullptr));
+      const float b = __uint_as_float(radix_pick<false>(p, 1, nb - 1, (unsigned long long)(m / 2), cnt, mass,
+                                                        nullptr, nullptr));
+      med = __fmul_rn(__fadd_rn(a, b), 0.5f);
+    }
+    const float thr = __fmul_rn(alpha, med);
+    for (int k = tid; k < nb; k += 1024) flag[k] = (p[k] > thr) || k == 0 || k == nb - 1;
+    __syncthreads();
+  } else if (gamma >= 1.f) {
+    for (int k = tid; k < nb; k += 1024) flag[k] = 1;
+    __syncthreads();
+  } else {
+    unsigned long long t = 0;
+    for (int k = tid; k < nb; k += 1024) t += fx_mass(__float_as_uint(p[k]));
+    t = block1k_sum_u64(t, mass);
+    unsigned long long target = (unsigned long long)ceil((double)gamma * (double)t);
+    if (target == 0) target = 1;
+    unsigned long long above = 0;
+    uint32_t eq_cnt = 0;
+    const uint32_t vstar = radix_pick<true>(p, 0, nb, target, cnt, mass, &above, &eq_cnt);
+    const unsigned long long need = target - above;
+    const unsigned long long fv = fx_mass(vstar);
+    unsigned long long take = fv ? (need + fv - 1) / fv : eq_cnt;
+    if (take > eq_cnt) take = eq_cnt;
+    // entries equal to the cut value are taken in index order: rank them with a scan
+    const int per = (nb + 1023) / 1024;
+    const int a = min(nb, tid * per), b = min(nb, a + per);
+    int e = 0;
+    for (int k = a; k < b; ++k) e += (__float_as_uint(p[k]) == vstar);
+    int tot;
+    int rank = block1k_excl_scan(e, shi, &tot);
+    for (int k = a; k < b; ++k) {
+      const uint32_t x = __float_as_uint(p[k]);
+      bool sel = x > vstar || k == 0 || k == nb - 1;
+      if (x == vstar) { if ((unsigned long long)rank < take) sel = true; ++rank; }
+      flag[k] = sel;
+    }
+    __syncthreads();
+  }
+  if (min_blocks > 0) {  // top up with the largest remaining scores, ties to the lower index
+    const int want = min(min_blocks, nb);
+    int have = 0;
+    for (int k = tid; k < nb; k += 1024) have += flag[k];
+    int tot;
+    block1k_excl_scan(have, shi, &tot);
+    for (have = tot; have < want; ++have) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int k = tid; k < nb; k += 1024)
+        if (!flag[k] && (p[k] > bv || (p[k] == bv && k < bi))) { bv = p[k]; bi = k; }
+      shv[tid] = bv;
+      shi[tid] = bi;
+      __syncthreads();
+      for (int o = 512; o > 0; o >>= 1) {
+        if (tid < o) {
+          const float v2 = shv[tid + o];
+          const int i2 = shi[tid + o];
+          if (v2 > shv[tid] || (v2 == shv[tid] && i2 < shi[tid])) { shv[tid] = v2; shi[tid] = i2; }
+        }
+        __syncthreads();
+      }
+      if (tid == 0 && shi[0] < nb) flag[shi[0]] = 1;
+      __syncthreads();
+    }
+  }
+  // ascending compaction
+  const int per = (nb + 1023) / 1024;
+  const int a = min(nb, tid * per), b = min(nb, a + per);
+  int c = 0;
+  for (int k = a; k < b; ++k) c += flag[k];
+  int tot;
+  int pos = block1k_excl_scan(c, shi, &tot);
+  int32_t* out = (dir == 0 ? sv : ss) + (int64_t)h * nb;
+  for (int k = a; k < b; ++k)
+    if (flag[k]) out[pos++] = k;
+  if (tid == 0) (dir == 0 ? nv : ns)[h] = tot;
 }
 
 // ------------------------------------------------------------------ PE: pooled Q
@@ -542,9 +842,27 @@ __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* 
 hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,
                          const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
                          int min_blocks, const SelectBufs& b, hipStream_t s) {
+  const bool jsd_on = b.router == 1 && !dense;
+  if (jsd_on) {
+    const float scale = 1.f / sqrtf((float)HD);
+    if (fp32)
+      jsd_route_kernel<float><<<hq, 256, 0, s>>>((const float*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd,
+                                                 nb, hq, hkv, st.q_h, st.q_n, scale);
+    else
+      jsd_route_kernel<bf16><<<hq, 256, 0, s>>>((const bf16*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd, nb,
+                                                hq, hkv, st.q_h, st.q_n, scale);
+  }
   vs_select_kernel<<<hq, 256, nb, s>>>((const float4*)b.tiles, n, nb, w_sink, w_local, tau, alpha, min_blocks,
-                                       dense ? 1 : 0, b.route, b.c_struct, b.pv, b.ps, b.sv, b.nv, b.ss, b.ns,
-                                       b.pv_out, b.ps_out);
+                                       dense ? 1 : 0, jsd_on ? b.jsd : nullptr, b.vs_budget, b.route, b.c_struct,
+                                       b.pv, b.ps, b.sv, b.nv, b.ss, b.ns, b.pv_out, b.ps_out);
+  if (!dense && b.vs_budget != 0) {
+    if (b.vs_budget == 1)
+      vs_rank_kernel<true><<<dim3(hq, 2), 1024, nb, s>>>(b.route, b.pv, b.ps, nb, alpha, gamma, min_blocks, b.sv,
+                                                         b.nv, b.ss, b.ns);
+    else
+      vs_rank_kernel<false><<<dim3(hq, 2), 1024, nb, s>>>(b.route, b.pv, b.ps, nb, alpha, gamma, min_blocks, b.sv,
+                                                          b.nv, b.ss, b.ns);
+  }
   PeCut* cut = (PeCut*)b.cut;
   const int64_t total = (int64_t)nb * (nb + 1) / 2;
   const int pe_all = gamma >= 1.f ? 1 : 0;

@@ -80,8 +80,25 @@ typedef struct {
                                 a direction's set is topped up with its largest remaining scores,
                                 ties to the lower index, until it holds min_blocks indices */
   int32_t dense_below_n;     /* length gate: n < dense_below_n takes the dense path (0 = off) */
-  int32_t flags;             /* reserved, must be 0 */
+  int32_t flags;             /* 0 = CRISP as published; otherwise an OR of the CRISP_FLAG_* variants
+                                below (unknown bits, or MEDIAN together with COVERAGE: CRISP_E_ARG) */
 } crisp_params;
+
+/* Variants the pages compare CRISP against; each changes one decision rule and
+ * keeps the proxy, the lists and the attention kernel. */
+/* Route by the Jensen-Shannon divergence (natural log) between the pooled
+ * estimate a_bar = softmax over key blocks of mean(Q_last) . mean_block(K) /
+ * sqrt(d) and the per-query mean p^v: Vertical-Slash iff JSD >= tau, instead
+ * of C_struct >= tau [CRISP §2, FlexPrefill's router]. */
+#define CRISP_FLAG_ROUTE_JSD   1
+/* Vertical-Slash noise floor = median of the non-anchor block scores of the
+ * direction instead of their mean [CRISP appendix on the noise floor]. */
+#define CRISP_FLAG_VS_MEDIAN   2
+/* Vertical-Slash budget = per-direction coverage: blocks by descending score
+ * (ties to the lower index) until gamma of the direction's mass, plus the first
+ * and last blocks, instead of the noise floor [CRISP §2, FlexPrefill's
+ * gamma-cumsum]. */
+#define CRISP_FLAG_VS_COVERAGE 4
 
 /* Selection results.  route, c_struct, row_ptr and col_idx are required; the
  * rest are optional diagnostics (NULL = not written).  Lists are one CSR over
@@ -99,6 +116,8 @@ typedef struct {
   float *pe_prob;            /* optional [hq * N_b*(N_b+1)/2]: pooled-estimate probabilities of
                                 Pooled-Estimation heads, causal triangle row-major
                                 (row qb starts at qb*(qb+1)/2); rows of other heads untouched */
+  double *jsd;               /* optional [hq]: JSD(a_bar, p^v) (written with CRISP_FLAG_ROUTE_JSD only) */
+  float *abar;               /* optional [hq * N_b]: pooled estimate a_bar (CRISP_FLAG_ROUTE_JSD only) */
 } crisp_selection;
 
 /* Bytes of workspace needed by crisp_select / crisp_sparse_attn /

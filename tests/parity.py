@@ -74,8 +74,18 @@ def tri_to_dense(vals, nb):
     return P
 
 
+def variant_of(p: dsp.CrispParams):
+    """(router, budget) names of the oracle for the flags of p."""
+    router = "jsd" if p.flags & dsp.FLAG_ROUTE_JSD else "cstruct"
+    budget = "median" if p.flags & dsp.FLAG_VS_MEDIAN else ("coverage" if p.flags & dsp.FLAG_VS_COVERAGE else "mean")
+    return router, budget
+
+
 def check_decisions(sel, hq, nb, p: dsp.CrispParams, heads=None):
     """Bit-exact decision parity from the GPU's own float32 scores.  Returns a report dict."""
+    router, budget = variant_of(p)
+    abar = sel.abar.cpu().numpy().reshape(hq, nb) if router == "jsd" else None
+    jsd_gpu = sel.jsd.cpu().numpy() if router == "jsd" else None
     route = sel.route.cpu().numpy()
     cs = sel.c_struct.cpu().numpy()
     pv = sel.pv.cpu().numpy().reshape(hq, nb) if sel.pv is not None else None
@@ -84,14 +94,25 @@ def check_decisions(sel, hq, nb, p: dsp.CrispParams, heads=None):
     sv = sel.sv.cpu().numpy().reshape(hq, nb); ss = sel.ss.cpu().numpy().reshape(hq, nb)
     rp, col = gpu_lists(sel, hq, nb)
     rep = dict(route_ties=0, vs_ties=0, pe_ties=0, pe_exempt=0, heads_checked=0, vs_heads=0, pe_heads=0,
-               dense_heads=0)
+               dense_heads=0, vs_exempt=0, jsd_err=0.0)
     for h in (range(hq) if heads is None else heads):
         Pd = None
         if route[h] == 0:
             Pd = tri_to_dense(sel.pe_prob[tri_slice(nb, h)].cpu().numpy(), nb)
+        if router == "jsd" and route[h] != -1:
+            # the divergence is a float64 sum of logarithms: the oracle's value from the
+            # GPU's own float32 a_bar and p^v agrees to rounding, and a route that sits
+            # within 1e-6 relative of tau is a tie (counted, and the head skipped)
+            j = O.jsd(abar[h], pv[h])
+            rep["jsd_err"] = max(rep["jsd_err"], abs(j - float(jsd_gpu[h])))
+            assert abs(j - float(jsd_gpu[h])) <= 1e-9, f"head {h}: jsd gpu {jsd_gpu[h]} oracle {j}"
+            if abs(j - float(np.float32(p.tau))) <= O.TIE_REL * max(float(np.float32(p.tau)), 1e-30):
+                rep["route_ties"] += 1
+                continue
         r, osv, oss, lists, info = O.decide_from_scores(int(route[h]), cs[h], pv[h] if pv is not None else None,
                                                        ps[h] if ps is not None else None, Pd, nb, p.tau, p.alpha,
-                                                       p.gamma, p.min_blocks)
+                                                       p.gamma, p.min_blocks, router=router, budget=budget,
+                                                       abar=abar[h] if abar is not None else None)
         # route and VS thresholds are the same float32 operations on the same float32
         # scores on both sides: they must agree even inside the tie band (ties are
         # only counted).  The PE cut compares sums of the same float32 values taken
@@ -99,12 +120,22 @@ def check_decisions(sel, hq, nb, p: dsp.CrispParams, heads=None):
         # 2^-46 (error < entries * 2^-46 in both the total and the prefix), the
         # oracle accumulates in extended precision.  A head is exempt only when
         # gamma*T lies within entries * 2^-45 of the prefix at the cut.
-        rep["route_ties"] += int(route[h] != -1 and O.route_tie(cs[h], p.tau))
+        if router == "cstruct":
+            rep["route_ties"] += int(route[h] != -1 and O.route_tie(cs[h], p.tau))
         assert r == route[h], f"head {h}: route gpu {route[h]} oracle {r} (C={cs[h]!r})"
         gl = head_lists(rp, col, h, nb)
         if r == 1:
             rep["vs_heads"] += 1
-            rep["vs_ties"] += len(O.vs_ties(pv[h], p.alpha)) + len(O.vs_ties(ps[h], p.alpha))
+            if budget == "mean":
+                rep["vs_ties"] += len(O.vs_ties(pv[h], p.alpha)) + len(O.vs_ties(ps[h], p.alpha))
+            elif budget == "median":
+                rep["vs_ties"] += len(O.median_ties(pv[h], p.alpha)) + len(O.median_ties(ps[h], p.alpha))
+            else:
+                # same exemption as the PE cut: the GPU sums 2^-46 fixed-point masses
+                rep["vs_ties"] += sum(int(O.pe_tie(i)) for i in info)
+                if any(O.pe_tie(i, 0.0, i["entries"] * 2.0 ** -45) for i in info):
+                    rep["vs_exempt"] += 1
+                    continue
             assert np.array_equal(sv[h, :nv[h]], osv), f"head {h}: S_v differs"
             assert np.array_equal(ss[h, :ns[h]], oss), f"head {h}: S_s differs"
         elif r == 0:
@@ -144,6 +175,25 @@ def check_score_fidelity(spec, Q, K, sel, heads, tol=1e-4):
         e = max(np.abs(pv[h] - opv).max(), np.abs(ps[h] - ops).max(), abs(cs[h] - ocs))
         worst = max(worst, float(e))
         assert e <= tol, f"head {h}: score error {e}"
+    return worst
+
+
+def check_jsd_fidelity(spec, Q, K, sel, heads, tol=1e-5):
+    """Oracle float64 pooled estimate and JSD from Q, K against the GPU's."""
+    cfg = spec.cfg
+    nb, n = cfg.nb, cfg.n
+    abar = sel.abar.cpu().numpy().reshape(cfg.hq, nb)
+    jg = sel.jsd.cpu().numpy()
+    worst = 0.0
+    for h in heads:
+        g = h // (cfg.hq // cfg.hkv)
+        q = synth.as_f64(spec, Q[h, n - 128:])
+        k = synth.as_f64(spec, K[g])
+        a = O.pooled_estimate(q, k, 128)
+        pv = O.vertical_scores(O.proxy_attention(q, k), 128)
+        e = max(float(np.abs(a - abar[h]).max()), abs(O.jsd(a, pv) - float(jg[h])))
+        worst = max(worst, e)
+        assert e <= tol, f"head {h}: a_bar / JSD error {e}"
     return worst
 
 

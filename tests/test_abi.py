@@ -60,13 +60,20 @@ def test_select_rejects_bad_shapes(mut, status):
 
 
 @pytest.mark.parametrize("mut", [dict(gamma=1.5), dict(gamma=0.0), dict(tau=-1.0), dict(alpha=float("nan")),
-                                 dict(sink=-1), dict(min_blocks=-2), dict(flags=1), dict(local=10 ** 9)])
+                                 dict(sink=-1), dict(min_blocks=-2), dict(flags=8), dict(flags=6),
+                                 dict(local=10 ** 9)])
 def test_select_rejects_bad_params(mut):
     p = dsp.CrispParams(**mut)
     s = _shape()
     sel = api.CrispSelectionC(16, 16, 16, 16, 1 << 40)
     st = dsp.lib().crisp_select(C.byref(s), 16, 16, C.byref(p.c()), C.byref(sel), 256, 1 << 40, None)
     assert st == -1
+
+
+@pytest.mark.parametrize("flags", [1, 2, 4, 3, 5])
+def test_variant_flags_are_accepted(flags):
+    s = _shape()
+    assert dsp.select_workspace_bytes(s, dsp.CrispParams(flags=flags)) > 0
 
 
 def test_select_rejects_block_other_than_128_and_small_buffers():

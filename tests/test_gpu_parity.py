@@ -271,3 +271,89 @@ def test_qwen_128k_layer():
 @pytest.mark.timeout(1200)
 def test_llama_512k_layer():
     _big_layer(4, 1, 4, 4)
+
+
+# ------------------------------------------------------------------ variants: JSD router, median floor, coverage budget
+
+VARIANTS = [dsp.FLAG_ROUTE_JSD, dsp.FLAG_VS_MEDIAN, dsp.FLAG_VS_COVERAGE,
+            dsp.FLAG_ROUTE_JSD | dsp.FLAG_VS_COVERAGE, dsp.FLAG_ROUTE_JSD | dsp.FLAG_VS_MEDIAN]
+
+
+@pytest.mark.parametrize("n,hq,hkv,seed", [(8192, 8, 2, 21), (1664, 7, 1, 22), (384, 2, 1, 23)])
+def test_variant_selection_and_output(n, hq, hkv, seed):
+    """Every variant on small mixed layers: decisions bit-exact from the GPU's
+    own scores, the pooled estimate and JSD against the oracle's float64 ones,
+    and the full output on the variant's lists.  The JSD threshold is taken at
+    0 (every head Vertical-Slash), at the median of the heads' divergences
+    (both routes) and above ln 2 (every head Pooled-Estimation)."""
+    cfg = synth.custom_config("variant", n, hq, hkv, seed=seed, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    for flags in VARIANTS:
+        taus = [cfg.tau]
+        if flags & dsp.FLAG_ROUTE_JSD:
+            sel0 = dsp.crisp_select(q, k, P.params_of(cfg, tau=0.0, flags=flags), pe_prob=True)
+            torch.cuda.synchronize()
+            P.log(f"[variant {flags} n={n}] jsd err", P.check_jsd_fidelity(spec, Q, K, sel0, range(hq)))
+            taus = [0.0, float(np.median(sel0.jsd.cpu().numpy())), 1.0]
+        for tau in taus:
+            p = P.params_of(cfg, tau=tau, flags=flags)
+            o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+            torch.cuda.synchronize()
+            rep = P.check_decisions(sel, hq, cfg.nb, p)
+            route = sel.route.cpu().numpy()
+            P.log(f"[variant {flags} n={n} tau={tau:.4g}] routes {route.tolist()} decisions", rep)
+            assert rep["heads_checked"] + rep["pe_exempt"] + rep["vs_exempt"] + rep["route_ties"] == hq
+            if flags & dsp.FLAG_ROUTE_JSD and tau == 0.0:
+                assert np.all(route == 1)
+            if tau == 1.0:
+                assert np.all(route == 0)
+            P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(hq), range(cfg.nb))
+
+
+def test_variant_min_blocks_and_gamma_sweep():
+    cfg = synth.custom_config("vsweep", 8192, 8, 2, seed=31, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k = P.to_device(spec, Q), P.to_device(spec, K)
+    for flags in (dsp.FLAG_VS_MEDIAN, dsp.FLAG_VS_COVERAGE):
+        for alpha, gamma in ((0.5, 0.9), (1.0, 0.95), (2.0, 0.99), (1.0, 1.0)):
+            for mb in (0, 8):
+                p = P.params_of(cfg, tau=0.2, alpha=alpha, gamma=gamma, min_blocks=mb, flags=flags)
+                sel = dsp.crisp_select(q, k, p, pe_prob=True)
+                torch.cuda.synchronize()
+                rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+                vs = sel.route.cpu().numpy() == 1
+                if mb:
+                    assert np.all(sel.nv.cpu().numpy()[vs] >= mb) and np.all(sel.ns.cpu().numpy()[vs] >= mb)
+                if flags == dsp.FLAG_VS_COVERAGE and gamma == 1.0:
+                    assert np.all(sel.nv.cpu().numpy()[vs] == cfg.nb)
+
+
+@pytest.mark.timeout(900)
+def test_flexprefill_configuration_llama_128k():
+    """FlexPrefill's pair of rules (JSD router, coverage budget at gamma 0.95)
+    on the Llama 128k layer: decisions in full, sampled outputs."""
+    spec = synth.make_spec(synth.CONFIGS[2])
+    cfg = spec.cfg
+    Q, K, V = P.load_layer(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    flags = dsp.FLAG_ROUTE_JSD | dsp.FLAG_VS_COVERAGE
+    sel0 = dsp.crisp_select(q, k, P.params_of(cfg, tau=0.0, flags=flags))
+    torch.cuda.synchronize()
+    js = sel0.jsd.cpu().numpy()
+    P.log("[flex 128k] jsd", np.round(js, 4).tolist())
+    P.log("[flex 128k] jsd err", P.check_jsd_fidelity(spec, Q, K, sel0, [0, 1, 31]))
+    p = P.params_of(cfg, tau=float(np.median(js)), flags=flags)
+    o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+    P.log("[flex 128k] decisions", rep, "routes", sel.route.cpu().tolist())
+    assert rep["heads_checked"] + rep["pe_exempt"] + rep["vs_exempt"] + rep["route_ties"] == cfg.hq
+    route = sel.route.cpu().numpy()
+    heads = [h for h in range(cfg.hq) if route[h] == 1][:2] + [h for h in range(cfg.hq) if route[h] == 0][:1]
+    blocks = synth.sample_blocks(cfg.nb, 4, 5)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), heads, blocks)
+    P.log(f"[flex 128k] attention max {mx:.2e} mean {mean:.2e}")
