@@ -13,11 +13,17 @@ gamma 0.95, length-compensated generator).  Printed as one JSON line:
   roofline       the sparse attention kernel: executed-tile MFMA flops per
                  launch / its launch time (HIP events on the launch stream),
                  against the 2.5 PFLOP/s dense bf16 peak
+  step_ms        per-step HIP-event times: warm, and after a 512 MiB write
+                 that flushes L2 / MALL (median and min)
+  selection_roofline  the selection stage against max(HBM, MFMA)
+  rules          the decision rules the pages compare, on the same layer:
+                 median floor, universal configuration, FlexPrefill's pair
   cpu_baseline   the CPU oracle on a bounded sample of the same layer,
                  extrapolated to ms per layer
-  extra          the 128k layers (Llama and Qwen shaped), fewer steps
+  extra          the 128k layers (Llama and Qwen shaped) and an 8k-64k
+                 length sweep (CRISP vs dense, the length gate)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra] [--no-compare] [--no-sweep]
 """
 from __future__ import annotations
 
@@ -86,6 +92,110 @@ def event_ms(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
+def step_events(fn, reps, torch, flush=None):
+    """Per-call ms from HIP events on the launch stream, optionally writing a
+    512 MiB buffer (L2 / MALL flush) before each call, outside the events."""
+    out = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e))
+    return out
+
+
+def selection_roofline(cfg, route, tiles, sel_ms):
+    """Selection as a whole against max(HBM, MFMA): algorithmic bytes = K once,
+    Q of the Pooled-Estimation heads once, the pooled matrix of those heads
+    written once and read twice (softmax + cut), the lists written once; flops =
+    the two proxy passes over K (2 * 128 * n * d * hq each)."""
+    nb = cfg.n // 128
+    h_pe = int((route == 0).sum())
+    tri = nb * (nb + 1) // 2
+    nbytes = cfg.hkv * cfg.n * 128 * 2 + h_pe * cfg.n * 128 * 2 + 3 * 4 * tri * h_pe + 4 * tiles
+    flops = 2 * (2 * 128 * cfg.n * 128 * cfg.hq)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    return {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "bytes": int(nbytes), "flops": int(flops),
+            "achieved_gbs": round(nbytes / (sel_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "roofline_ms": round(max(t_hbm, t_mfma) * 1e3, 4), "frac": round(max(t_hbm, t_mfma) * 1e3 / sel_ms, 4)}
+
+
+def compare_rules(cfg, q, k, v, dsp, torch, steps, dense_ms):
+    """The decision rules the pages compare on one resident layer: CRISP as
+    published, its median-floor variant, the universal configuration (min budget
+    8, tau 0.2, alpha 1 / 1.25 / 1.5) and FlexPrefill's pair (JSD router,
+    coverage budget at gamma 0.95 / 0.97; JSD threshold 0.1).  For each: ms per
+    layer, executed-tile density, Vertical-Slash head count, mean per-direction
+    budget of the VS heads, and agreement of the route with C_struct routing."""
+    J, M, C = dsp.FLAG_ROUTE_JSD, dsp.FLAG_VS_MEDIAN, dsp.FLAG_VS_COVERAGE
+    rules = [("crisp", {}), ("crisp-median-floor", dict(flags=M)),
+             ("crisp-universal-a1.0", dict(tau=0.2, alpha=1.0, min_blocks=8)),
+             ("crisp-universal-a1.25", dict(tau=0.2, alpha=1.25, min_blocks=8)),
+             ("crisp-universal-a1.5", dict(tau=0.2, alpha=1.5, min_blocks=8)),
+             ("flexprefill-g0.95", dict(tau=0.1, gamma=0.95, flags=J | C)),
+             ("flexprefill-g0.97", dict(tau=0.1, gamma=0.97, flags=J | C)),
+             ("jsd-router+noise-floor", dict(tau=0.1, flags=J)),
+             ("cstruct-router+coverage-g0.95", dict(flags=C))]
+    nb = cfg.n // 128
+    dense_tiles = cfg.hq * nb * (nb + 1) // 2
+    base_route = None
+    out = {}
+    for name, over in rules:
+        p = dsp.CrispParams(tau=cfg.tau, alpha=cfg.alpha, gamma=cfg.gamma)
+        for a, b in over.items():
+            setattr(p, a, b)
+        o = torch.empty_like(q)
+        sel = dsp.new_selection(q, k, diagnostics=True)
+        ws = torch.empty(dsp.workspace_bytes(dsp.make_shape(q, k, v, o), p), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws), steps, 1, torch)
+        route = sel.route.cpu().numpy()
+        nv, ns = sel.nv.cpu().numpy(), sel.ns.cpu().numpy()
+        vs = route == 1
+        tiles = int(sel.row_ptr[-1].item())
+        if base_route is None:
+            base_route = route
+        out[name] = {"ms": round(ms, 3), "speedup_vs_dense": round(dense_ms / ms, 3) if dense_ms else None,
+                     "density": round(tiles / dense_tiles, 4), "vs_heads": int(vs.sum()),
+                     "vs_budget_blocks": round(float((nv[vs] + ns[vs]).mean()) / 2, 2) if vs.any() else None,
+                     "route_agrees_with_cstruct": round(float((route == base_route).mean()), 4)}
+        log(f"[bench] rule {name}: {out[name]}")
+        del o, sel, ws
+    return out
+
+
+def length_sweep(dsp, torch, synth, ns=(8192, 16384, 32768, 65536), steps=3):
+    """CRISP vs dense ms per layer on Llama-shaped layers of growing length:
+    where sparse prefill starts to pay (the length gate)."""
+    res = {}
+    for n in ns:
+        cfg = synth.custom_config(f"llama-shape-{n // 1024}k", n, 32, 8, seed=7, conc_frac=0.6)
+        spec = synth.make_spec(cfg)
+        Q, K, V = synth.generate(spec, threads=16)
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+        p = dsp.CrispParams(tau=cfg.tau, alpha=cfg.alpha, gamma=cfg.gamma)
+        o = torch.empty_like(q)
+        sel = dsp.new_selection(q, k, diagnostics=False)
+        ws = torch.empty(dsp.workspace_bytes(dsp.make_shape(q, k, v, o), p), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws), steps, 2, torch)
+        aws = ws[dsp.select_workspace_bytes(dsp.make_shape(q, k, v, o), p):]
+        dms = timed(lambda: dsp.crisp_dense_attn(q, k, v, o=o, ws=aws), steps, 2, torch)
+        nb = n // 128
+        res[n] = {"crisp_ms": round(ms, 3), "dense_ms": round(dms, 3), "speedup": round(dms / ms, 3),
+                  "density": round(int(sel.row_ptr[-1].item()) / (32 * nb * (nb + 1) // 2), 4)}
+        log(f"[bench] length {n}: {res[n]}")
+        del q, k, v, o, sel, ws, aws
+        torch.cuda.empty_cache()
+    return res
+
+
 def calibrate_copy(mib, torch):
     """One plain device copy of `mib` MiB (read mib, write mib): the reference that
     scales the HBM byte counters of the attention kernel."""
@@ -98,7 +208,7 @@ def calibrate_copy(mib, torch):
     log(f"[bench] calibration copy: {mib} MiB read + {mib} MiB written")
 
 
-def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True):
+def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True, compare=False):
     spec = synth.make_spec(synth.CONFIGS[cfg_id])
     cfg = spec.cfg
     t = time.time()
@@ -117,6 +227,10 @@ def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True):
 
     step = lambda: dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws)
     ms = timed(step, steps, warmup, torch)
+    warm = step_events(step, max(1, steps), torch)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = step_events(step, max(1, steps), torch, flush=flush)
+    del flush
     route = sel.route.cpu().numpy()
     tiles = int(sel.row_ptr[-1].item())
     nb = cfg.nb
@@ -126,7 +240,10 @@ def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True):
     attn_ms = event_ms(lambda: dsp.crisp_sparse_attn(q, k, v, sel, o=o, ws=attn_ws), max(1, steps), torch)
     out = dict(workload=cfg.name, n=cfg.n, hq=cfg.hq, hkv=cfg.hkv, ms=ms, select_ms=sel_ms, sparse_attn_ms=attn_ms,
                vs_heads=int((route == 1).sum()), pe_heads=int((route == 0).sum()), tiles=tiles,
-               dense_tiles=dense_tiles, density=tiles / dense_tiles)
+               dense_tiles=dense_tiles, density=tiles / dense_tiles,
+               step_ms={"warm_median": float(np.median(warm)), "warm_min": float(np.min(warm)),
+                        "l2_flushed_median": float(np.median(cold)), "l2_flushed_min": float(np.min(cold))})
+    out["selection_roofline"] = selection_roofline(cfg, route, tiles, sel_ms)
     if with_dense:
         od = torch.empty_like(q)
         dws = attn_ws
@@ -136,6 +253,13 @@ def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True):
         out["speedup"] = out["dense_ms"] / ms
         out["dense_tflops"] = dense_tiles * TILE_FLOPS / (out["dense_kernel_ms"] * 1e-3) / 1e12
     out["sparse_tflops"] = tiles * TILE_FLOPS / (attn_ms * 1e-3) / 1e12
+    if compare:
+        del sel, o, ws
+        torch.cuda.empty_cache()
+        out["rules"] = compare_rules(cfg, q, k, v, dsp, torch, 2, out.get("dense_ms"))
+        del q, k, v
+        torch.cuda.empty_cache()
+        return out, spec, route
     del q, k, v, o, ws
     torch.cuda.empty_cache()
     return out, spec, route
@@ -199,6 +323,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--workload", type=int, default=4, help="layer id: 1 llama-32k, 2 llama-128k, 3 qwen-128k, 4 llama-512k")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline (counter-collection runs)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the decision-rule comparison (median floor, universal config, FlexPrefill)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 8k-64k length sweep (length gate)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -217,9 +344,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, torch)
     main_res, spec, route = run_layer(args.workload, args.steps, args.warmup, torch, dsp, synth,
-                                      with_dense=not args.no_dense)
+                                      with_dense=not args.no_dense, compare=not args.no_compare)
     log("[bench]", json.dumps(main_res))
     extra = {}
+    if not args.no_sweep:
+        extra["length_sweep"] = length_sweep(dsp, torch, synth)
     if not args.no_extra:
         for cid in (2, 3):
             if cid == args.workload:
@@ -227,7 +356,7 @@ def main():
             r, _, _ = run_layer(cid, max(2, args.steps), 1, torch, dsp, synth)
             extra[r["workload"]] = {k: r[k] for k in ("ms", "dense_ms", "speedup", "select_ms", "sparse_attn_ms",
                                                       "density", "vs_heads", "pe_heads", "sparse_tflops",
-                                                      "dense_tflops")}
+                                                      "dense_tflops", "selection_roofline")}
             log("[bench]", json.dumps(r))
     cpu = None
     if not args.no_cpu:
@@ -254,6 +383,9 @@ def main():
         "speedup_vs_dense": round(main_res["speedup"], 3) if "speedup" in main_res else None,
         "dense_ms": round(main_res["dense_ms"], 3) if "dense_ms" in main_res else None,
         "stages": {"select_ms": round(main_res["select_ms"], 3), "sparse_attn_ms": round(main_res["sparse_attn_ms"], 3)},
+        "step_ms": {k: round(v, 3) for k, v in main_res["step_ms"].items()},
+        "selection_roofline": main_res["selection_roofline"],
+        "rules": main_res.get("rules"),
         "density": round(main_res["density"], 4),
         "heads": {"vs": main_res["vs_heads"], "pe": main_res["pe_heads"]},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
