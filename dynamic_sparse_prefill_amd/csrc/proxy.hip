@@ -88,19 +88,48 @@ __global__ __launch_bounds__(256) void proxy_stats_kernel(const T* __restrict__ 
   if (g == 0) stats[((int64_t)h * nchunk + chunk) * BLK + qrow] = make_float2(M, L);
 }
 
-// Row normaliser of the proxy rows: M = max over chunks, 1/L with L rescaled to M.
-__global__ __launch_bounds__(128) void proxy_combine_kernel(const float2* __restrict__ stats,
-                                                            float2* __restrict__ rowstat, int nchunk, float sl2) {
-  const int h = blockIdx.x, r = threadIdx.x;
+// Row normaliser of the proxy rows: M = max over chunks, 1/L with L rescaled to
+// M.  Eight groups of 128 threads take every eighth chunk; their partial
+// (max, sum) pairs are merged in group order, so the result is reproducible.
+constexpr int CMB_GROUPS = 8;
+__global__ __launch_bounds__(BLK * CMB_GROUPS) void proxy_combine_kernel(const float2* __restrict__ stats,
+                                                                         float2* __restrict__ rowstat, int nchunk,
+                                                                         float sl2) {
+  __shared__ float2 part[CMB_GROUPS][BLK];
+  const int h = blockIdx.x, r = threadIdx.x % BLK, grp = threadIdx.x / BLK;
   const float2* p = stats + (int64_t)h * nchunk * BLK + r;
   float M = -1e30f;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[(int64_t)c * BLK].x);
+  for (int c = grp; c < nchunk; c += CMB_GROUPS) M = fmaxf(M, p[(int64_t)c * BLK].x);
   float L = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
+  for (int c = grp; c < nchunk; c += CMB_GROUPS) {
     const float2 v = p[(int64_t)c * BLK];
     L += v.y * fast_exp2((v.x - M) * sl2);
   }
-  rowstat[h * BLK + r] = make_float2(M, 1.f / L);
+  part[grp][r] = make_float2(M, L);
+  __syncthreads();
+  if (grp == 0) {
+    float Mt = -1e30f;
+    for (int q = 0; q < CMB_GROUPS; ++q) Mt = fmaxf(Mt, part[q][r].x);
+    float Lt = 0.f;
+    for (int q = 0; q < CMB_GROUPS; ++q) Lt += part[q][r].y * fast_exp2((part[q][r].x - Mt) * sl2);
+    rowstat[h * BLK + r] = make_float2(Mt, 1.f / Lt);
+  }
+}
+
+// Lower / upper sums of one interior tile for wave W (rows 32W .. 32W+31).
+template <int W>
+__device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, float mbl, int qrow, int g,
+                                              float& lo, float& up) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[t][i], sl2, -mbl));
+      if (t < W) lo += p;
+      else if (t > W) up += p;
+      else if (32 * t + mfma32_row(i, g) <= qrow) lo += p;
+      else up += p;
+    }
 }
 
 template <typename T>
@@ -111,7 +140,8 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(const T* __restrict__ Q
                                                          int64_t sk_n, int w_sink, int w_local, float sl2) {
   __shared__ __attribute__((aligned(16))) T sK[BLK * Tile<T>::KP];
   __shared__ float red[4][3];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the t-vs-w branches are scalar
   const int G = hq / hkv;
   const int chunk = blockIdx.x / hq, rem = blockIdx.x % hq;
   const int kvh = rem % hkv, h = kvh * G + rem / hkv;
@@ -119,7 +149,8 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(const T* __restrict__ Q
   typename Tile<T>::QFrag qf;
   Tile<T>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const float2 rsx = rowstat[h * BLK + qrow];
-  const float mb = rsx.x * sl2, invl = rsx.y;
+  // p = exp2(s sl2 - M sl2) / L = exp2(s sl2 - (M sl2 + log2 L)): one fma and one exp per score
+  const float mbl = rsx.x * sl2 - __log2f(rsx.y);
   const int kb0 = chunk * PCH, kb1 = min(nb, kb0 + PCH);
   for (int kb = kb0; kb < kb1; ++kb) {
     __syncthreads();
@@ -131,19 +162,37 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(const T* __restrict__ Q
     const int64_t j0 = (int64_t)kb * BLK;
     const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
     float lo = 0.f, up = 0.f, an = 0.f;
+    // key c = 32t + .. of this tile against this wave's rows 32w .. 32w+31:
+    // t < w all lower (c <= qrow), t > w all upper, t = w split per score; on the
+    // last tile the upper part is masked (keys after the query).  Interior
+    // tiles take a path specialised on w (no per-score selects off the diagonal
+    // block); the last tile and the anchor tiles take the general one.
+    if (!last && !touches_anchor) {
+      switch (w) {
+        case 0: interior_sums<0>(s, sl2, mbl, qrow, g, lo, up); break;
+        case 1: interior_sums<1>(s, sl2, mbl, qrow, g, lo, up); break;
+        case 2: interior_sums<2>(s, sl2, mbl, qrow, g, lo, up); break;
+        default: interior_sums<3>(s, sl2, mbl, qrow, g, lo, up); break;
+      }
+    } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        if (t > w && last) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = 32 * t + mfma32_row(i, g);
-        float p = fast_exp2(fmaf(s[t][i], sl2, -mb)) * invl;
-        if (last && c > qrow) p = 0.f;
-        if (c <= qrow) lo += p; else up += p;
-        if (touches_anchor) {
-          const int64_t j = j0 + c;
-          if (j < w_sink || j >= n - w_local) an += p;
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * t + mfma32_row(i, g);
+          const float p = fast_exp2(fmaf(s[t][i], sl2, -mbl));
+          bool lower = t < w;
+          if (t == w) lower = c <= qrow;
+          if (lower) lo += p;
+          else if (!last) up += p;
+          if (touches_anchor && (lower || !last)) {
+            const int64_t j = j0 + c;
+            if (j < w_sink || j >= n - w_local) an += p;
+          }
         }
       }
+    }
     lo = wave_sum(lo);
     up = wave_sum(up);
     an = wave_sum(an);
@@ -170,7 +219,7 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, int64_t n, int n
     proxy_stats_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (float2*)stats, kbar, nb, hq,
                                                   hkv, nchunk, st.q_h, st.q_n, st.k_h, st.k_n, sl2);
   }
-  proxy_combine_kernel<<<hq, 128, 0, s>>>((const float2*)stats, (float2*)rowstat, nchunk, sl2);
+  proxy_combine_kernel<<<hq, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, nchunk, sl2);
   if (fp32) {
     proxy_pool_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (const float2*)rowstat,
                                                   (float4*)tiles, n, nb, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n,

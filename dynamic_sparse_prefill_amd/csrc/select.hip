@@ -147,10 +147,15 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     if (ps_out) ps_out[(int64_t)h * nb + k] = sl;
   }
   if (tid == 0) {
+    // tiles touching [0, w_sink) or [n - w_local, n), ascending: the sink tiles,
+    // then the recency tiles not already counted
     float c = 0.f;
-    for (int kb = 0; kb < nb; ++kb) {
+    const int sink_end = (int)min<int64_t>(nb, (w_sink + BLK - 1) / BLK);
+    const int rec_begin = (int)max<int64_t>(sink_end, (n - w_local) / BLK);
+    for (int kb = 0; kb < sink_end; ++kb) c = __fadd_rn(c, T[kb].z);
+    for (int kb = rec_begin; kb < nb; ++kb) {
       const int64_t j0 = (int64_t)kb * BLK;
-      if (j0 < w_sink || j0 + BLK > n - w_local) c = __fadd_rn(c, T[kb].z);
+      if (j0 + BLK > n - w_local) c = __fadd_rn(c, T[kb].z);
     }
     c = __fmul_rn(c, inv_b);
     c_struct[h] = c;
@@ -621,13 +626,25 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
   __syncthreads();
   const uint32_t* bits = (const uint32_t*)(P + (int64_t)h * total);
   const int64_t a = (int64_t)blockIdx.x * PE_SLICE, b = min(total, a + PE_SLICE);
+  // neighbouring entries of a softmax row mostly fall into the same bucket:
+  // each thread merges runs of equal buckets in registers (over its strided
+  // entries) and commits a run with one pair of LDS atomics
+  uint32_t run_b = 0xffffffffu, run_c = 0;
+  unsigned long long run_m = 0;
   for (int64_t e = a + tid; e < b; e += 256) {
     const uint32_t x = bits[e];
     if (PASS > 0 && (x >> hi) != (prefix >> hi)) continue;
     const uint32_t bk = (x >> shift) & mask;
-    atomicAdd(&sc[bk], 1u);
-    atomicAdd(&sm[bk], fx_mass(x));
+    if (bk != run_b) {
+      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+      run_b = bk;
+      run_c = 0;
+      run_m = 0;
+    }
+    ++run_c;
+    run_m += fx_mass(x);
   }
+  if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
   __syncthreads();
   uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
@@ -635,28 +652,43 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
     if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
 }
 
+// One wave per head: lane L owns the buckets nbk-1-32L down to nbk-32-32L (from
+// the top); the lane sums are scanned across the wave and the lane in which the
+// running mass first reaches `need` walks its own buckets.  Integer sums, so
+// the result equals a sequential walk from the top bucket.
 template <int PASS>
-__global__ void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
-                               const unsigned long long* __restrict__ hmass, float gamma) {
-  const int h = blockIdx.x;
-  if (threadIdx.x != 0) return;
+__global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
+                                                     const unsigned long long* __restrict__ hmass, float gamma) {
+  const int h = blockIdx.x, lane = threadIdx.x;
   PeCut c = cut[h];
   if (!c.active) return;
   constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
   const uint32_t* hc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   const unsigned long long* hm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
-  const int nbk = 1 << width;
+  constexpr int nbk = 1 << width;
+  constexpr int per = nbk / 64;
+  const int top = nbk - 1 - per * lane;
+  unsigned long long mine = 0;
+  for (int i = 0; i < per; ++i) mine += hm[top - i];
+  unsigned long long incl = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
   if (PASS == 0) {
-    unsigned long long t = 0;
-    for (int i = 0; i < nbk; ++i) t += hm[i];
+    const unsigned long long t = __shfl(incl, 63, 64);
     c.total = t;
     c.target = (unsigned long long)ceil((double)gamma * (double)t);
     if (c.target == 0) c.target = 1;
     c.need = c.target;
   }
-  unsigned long long acc = 0;
-  int sel = 0;
-  for (int i = nbk - 1; i >= 0; --i) {
+  // first lane whose inclusive mass reaches need (the last lane if none does)
+  const unsigned long long hit = __ballot(incl >= c.need);
+  const int L = hit ? __builtin_ctzll(hit) : 63;
+  if (lane != L) return;
+  unsigned long long acc = incl - mine;
+  int sel = top - per + 1;
+  for (int i = top; i > top - per; --i) {
     if (acc + hm[i] >= c.need) { sel = i; break; }
     acc += hm[i];
     sel = i;
@@ -805,26 +837,42 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   if (!FILL && lane == 0) counts[row] = base;
 }
 
-// exclusive scan of the row counts into row_ptr (single work-group of 1024 threads)
+// exclusive scan of the row counts into row_ptr (single work-group of 1024
+// threads): the counts go through in tiles of 4096, four consecutive per
+// thread, with a carry between tiles (the total fits int32, checked on the host)
 __global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ row_ptr, int64_t rows) {
-  __shared__ long long sh[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (rows + 1023) / 1024;
-  const int64_t a = min(rows, tid * per), b = min(rows, a + per);
-  long long s = 0;
-  for (int64_t i = a; i < b; ++i) s += counts[i];
-  sh[tid] = s;
+  __shared__ int wsum[16];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) s_carry = 0;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const long long x = tid >= o ? sh[tid - o] : 0;
+  for (int64_t base = 0; base < rows; base += 4096) {
+    const int64_t i0 = base + 4 * tid;
+    int v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = i0 + e < rows ? counts[i0 + e] : 0;
+    const int own = v[0] + v[1] + v[2] + v[3];
+    int incl = own;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    sh[tid] += x;
+    int before = s_carry;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    int run = before + incl - own;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < rows) row_ptr[i0 + e] = run;
+      run += v[e];
+    }
+    __syncthreads();
+    if (tid == 1023) s_carry = run;
     __syncthreads();
   }
-  long long base = sh[tid] - s;
-  for (int64_t i = a; i < b; ++i) { row_ptr[i] = (int32_t)base; base += counts[i]; }
-  if (tid == 1023) row_ptr[rows] = (int32_t)sh[1023];
+  if (tid == 0) row_ptr[rows] = s_carry;
 }
 
 __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
