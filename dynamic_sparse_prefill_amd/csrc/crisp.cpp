@@ -62,7 +62,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
   size_t stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
-      total;
+      pepart, total;
 };
 
 SelectLayout select_layout(const crisp_shape* s) {
@@ -89,6 +89,7 @@ SelectLayout select_layout(const crisp_shape* s) {
   L.counts = take(hq * nb * 4);
   L.jsd = take(hq * 8);
   L.abar = take(hq * nb * 4);
+  L.pepart = take(hq * nb * (((nb + 31) / 32 + 31) / 32) * 8);   // segments of 32 tiles of 32 key blocks
   L.total = o;
   return L;
 }
@@ -168,6 +169,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.cut = w + L.cut;
   b.eqrow = (int32_t*)(w + L.eqrow);
   b.counts = (int32_t*)(w + L.counts);
+  b.pepart = w + L.pepart;
   b.route = out->route;
   b.c_struct = out->c_struct;
   b.row_ptr = out->row_ptr;

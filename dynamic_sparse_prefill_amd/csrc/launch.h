@@ -38,6 +38,7 @@ struct SelectBufs {
   int32_t *sv, *nv, *ss, *ns;
   uint32_t* hcnt;  unsigned long long* hmass;  void* cut;
   int32_t *eqrow, *counts;
+  void* pepart;                     // [hq * nb * nseg] float2: per-segment row max / sum of the pooled logits
   // caller outputs
   int32_t* route; float* c_struct; int32_t *row_ptr, *col_idx;
   float *pv_out, *ps_out; int32_t *sv_out, *nv_out, *ss_out, *ns_out;

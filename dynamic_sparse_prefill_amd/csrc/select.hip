@@ -6,8 +6,9 @@
 //              S_d = {k : p_k > alpha mu_d} U {0, N_b - 1} per direction
 //              [CRISP §4], compacted in ascending order; optional min budget.
 //  pool_q      block means of Q for Pooled-Estimation heads.
-//  pe_logits   pooled logits  Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb.
-//  pe_softmax  causal row softmax of the pooled logits [CRISP §2, PE path].
+//  pe_logits   pooled logits Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb (fp32
+//              MFMA), with per-segment row max / sum;
+//  pe_norm     the causal row softmax in one pass [CRISP §2, PE path].
 //  pe_hist/    global gamma-cut over the flattened causal matrix: a radix
 //  pe_scan     select on the float32 bit pattern (11+11+10 bits, three
 //              passes) with per-bucket mass in 2^-46 fixed point, so the sums
@@ -507,86 +508,123 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, co
   }
 }
 
-// ------------------------------------------------------------------ PE: pooled logits (64 x 64 tiles)
+// ------------------------------------------------------------------ PE: pooled probabilities
 
 __device__ __forceinline__ int64_t tri(int64_t qb) { return qb * (qb + 1) / 2; }
 
-__global__ __launch_bounds__(256) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                        const int32_t* __restrict__ route, float* __restrict__ P,
-                                                        int nb, int hq, int hkv, float scale) {
-  constexpr int TP = 64, PP = HD + 1;
-  __shared__ float sq[TP * PP];
-  __shared__ float sk[TP * PP];
-  const int h = blockIdx.y, tid = threadIdx.x;
+constexpr int PE_SEG = 32;  // 32-key-block tiles per logits work-group (1024 key blocks)
+
+// Logits: one wave per (32 query blocks rb, segment cs of PE_SEG key tiles,
+// Pooled-Estimation head).  L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb
+// is formed 32 key blocks at a time with v_mfma_f32_32x32x2f32 in the
+// transposed form L^T = Kbar Qbar^T (lane l owns query block 32 rb + l%32 and
+// 16 of the 32 key blocks; the d index of MFMA step s, lane half g is 64 g + s),
+// turned row-major through LDS and stored with whole 128-byte row segments.
+// The segment's row max and sum of exp(L - max) go to `part` for the softmax.
+__global__ __launch_bounds__(64) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                       const int32_t* __restrict__ route, float* __restrict__ P,
+                                                       float2* __restrict__ part, int nb, int hq, int hkv,
+                                                       int nseg, float scale) {
+  __shared__ float tileT[32][33];
+  const int nrb = (nb + 31) / 32;
+  const int rb = nrb - 1 - (int)blockIdx.x, cs = blockIdx.y, h = blockIdx.z;
+  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
   if (route[h] != 0) return;
-  // linear tile id -> (ti, tj), tj <= ti
-  const int lin = blockIdx.x;
-  int ti = (int)((sqrtf(8.f * lin + 1.f) - 1.f) * 0.5f);
-  while ((int64_t)(ti + 1) * (ti + 2) / 2 <= lin) ++ti;
-  while ((int64_t)ti * (ti + 1) / 2 > lin) --ti;
-  const int tj = lin - ti * (ti + 1) / 2;
+  const int last_row = min(nb - 1, rb * 32 + 31);
+  const int ntile = last_row / 32 + 1;
+  const int ct0 = cs * PE_SEG, ct1 = min(ntile, ct0 + PE_SEG);
+  if (ct0 >= ct1) return;
   const int kvh = h / (hq / hkv);
-  const float* qs = qbar + ((int64_t)h * nb + ti * TP) * HD;
-  const float* ks = kbar + ((int64_t)kvh * nb + tj * TP) * HD;
-  for (int e = tid; e < TP * HD; e += 256) {
-    const int r = e / HD, d = e % HD;
-    sq[r * PP + d] = (ti * TP + r < nb) ? qs[(int64_t)r * HD + d] : 0.f;
-    sk[r * PP + d] = (tj * TP + r < nb) ? ks[(int64_t)r * HD + d] : 0.f;
-  }
-  __syncthreads();
-  const int r0 = 4 * (tid / 16), c0 = 4 * (tid % 16);
-  float acc[4][4] = {};
-  for (int d = 0; d < HD; ++d) {
-    float a[4], b[4];
+  const int qb = rb * 32 + l32;
+  const bool row_ok = qb < nb;
+  float qv[64];
+  {
+    const float4* src = (const float4*)(qbar + ((int64_t)h * nb + (row_ok ? qb : 0)) * HD + 64 * g);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) { a[x] = sq[(r0 + x) * PP + d]; b[x] = sk[(c0 + x) * PP + d]; }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
-  }
-  float* Ph = P + (int64_t)h * tri(nb);
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int qb = ti * TP + r0 + x;
-    if (qb >= nb) continue;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int kb = tj * TP + c0 + y;
-      if (kb <= qb) Ph[tri(qb) + kb] = acc[x][y] * scale;
+    for (int i = 0; i < 16; ++i) {
+      const float4 x = row_ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      qv[4 * i] = x.x; qv[4 * i + 1] = x.y; qv[4 * i + 2] = x.z; qv[4 * i + 3] = x.w;
     }
   }
+  float* Ph = P + (int64_t)h * tri(nb);
+  float m = -INFINITY, l = 0.f;
+  // the key-block means of tile ct + 1 are loaded while the MFMAs of tile ct run
+  auto kload = [&](int ct, float4 (&kx)[16]) {
+    const int krow = ct * 32 + l32;
+    const float4* ksrc = (const float4*)(kbar + ((int64_t)kvh * nb + (krow < nb ? krow : 0)) * HD + 64 * g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kx[i] = ksrc[i];
+  };
+  float4 kcur[16], knext[16];
+  kload(ct0, kcur);
+  for (int ct = ct0; ct < ct1; ++ct) {
+    if (ct + 1 < ct1) kload(ct + 1, knext);
+    f32x16 acc = {};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc = mfma_f32(kcur[i].x, qv[4 * i], acc);
+      acc = mfma_f32(kcur[i].y, qv[4 * i + 1], acc);
+      acc = mfma_f32(kcur[i].z, qv[4 * i + 2], acc);
+      acc = mfma_f32(kcur[i].w, qv[4 * i + 3], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kcur[i] = knext[i];
+    float tmx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kb = ct * 32 + mfma32_row(r, g);
+      const float x = acc[r] * scale;
+      acc[r] = (row_ok && kb <= qb) ? x : -INFINITY;
+      tmx = fmaxf(tmx, acc[r]);
+      tileT[l32][mfma32_row(r, g)] = x;
+    }
+    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+    const float mn = fmaxf(m, tmx);
+    float se = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) se += (acc[r] == -INFINITY) ? 0.f : expf(acc[r] - mn);
+    se += __shfl_xor(se, 32, 64);
+    l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + se;
+    m = mn;
+    __builtin_amdgcn_wave_barrier();
+    // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = rb * 32 + 2 * j + g, kb = ct * 32 + l32;
+      if (q < nb && kb <= q) Ph[tri(q) + kb] = tileT[2 * j + g][l32];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (row_ok && g == 0) part[((int64_t)h * nb + qb) * nseg + cs] = make_float2(m, l);
 }
 
-// ------------------------------------------------------------------ PE: row softmax
-
-__global__ __launch_bounds__(256) void pe_softmax_kernel(const int32_t* __restrict__ route, float* __restrict__ P,
-                                                         int nb) {
-  __shared__ float sh[256];
+// Row softmax in place: one work-group per (query block, Pooled-Estimation
+// head) merges the row's segment maxima and sums, then P = exp(L - M) / S.
+__global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict__ route, const float2* __restrict__ part,
+                                                      float* __restrict__ P, int nb, int nseg) {
   const int qb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   if (route[h] != 0) return;
+  const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;   // segments this row block produced
+  const float2* pp = part + ((int64_t)h * nb + qb) * nseg;
+  float M = -INFINITY;
+  for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
+  float S = 0.f;
+  for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * expf(pp[c].x - M);
+  const float inv = 1.f / S;
   float* row = P + (int64_t)h * tri(nb) + tri(qb);
-  const int len = qb + 1;
-  float mx = -INFINITY;
-  for (int k = tid; k < len; k += 256) mx = fmaxf(mx, row[k]);
-  sh[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) sh[tid] = fmaxf(sh[tid], sh[tid + o]);
-    __syncthreads();
+  for (int k0 = 0; k0 <= qb; k0 += 2048) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kb = k0 + 256 * j + tid;
+      x[j] = kb <= qb ? row[kb] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kb = k0 + 256 * j + tid;
+      if (kb <= qb) row[kb] = expf(x[j] - M) * inv;
+    }
   }
-  mx = sh[0];
-  __syncthreads();
-  float s = 0.f;
-  for (int k = tid; k < len; k += 256) s += expf(row[k] - mx);
-  sh[tid] = s;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) sh[tid] += sh[tid + o];
-    __syncthreads();
-  }
-  const float inv = 1.f / sh[0];
-  for (int k = tid; k < len; k += 256) row[k] = expf(row[k] - mx) * inv;
 }
 
 // ------------------------------------------------------------------ PE: radix select of the gamma cut
@@ -920,10 +958,10 @@ hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb,
       pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
     else
       pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
-    const int T = (nb + 63) / 64;
-    pe_logits_kernel<<<dim3(T * (T + 1) / 2, hq), 256, 0, s>>>(b.qbar, b.kbar, b.route, b.P, nb, hq, hkv,
-                                                               1.f / sqrtf((float)HD));
-    pe_softmax_kernel<<<dim3(nb, hq), 256, 0, s>>>(b.route, b.P, nb);
+    const int nrb = (nb + 31) / 32, nseg = (nrb + PE_SEG - 1) / PE_SEG;
+    pe_logits_kernel<<<dim3(nrb, nseg, hq), 64, 0, s>>>(b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, nb, hq,
+                                                        hkv, nseg, 1.f / sqrtf((float)HD));
+    pe_norm_kernel<<<dim3(nb, hq), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, nb, nseg);
     pe_cut_init_kernel<<<hq, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
     const dim3 gh((unsigned)((total + PE_SLICE - 1) / PE_SLICE), hq);
     pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
