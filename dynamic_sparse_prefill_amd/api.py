@@ -27,7 +27,8 @@ FLAG_ROUTE_JSD, FLAG_VS_MEDIAN, FLAG_VS_COVERAGE = 1, 2, 4
 
 EXPORTS = ("crisp_select_workspace_bytes", "crisp_attn_workspace_bytes", "crisp_workspace_bytes",
            "crisp_col_capacity", "crisp_select", "crisp_sparse_attn", "crisp_dense_attn",
-           "crisp_prefill", "crisp_status_string")
+           "crisp_prefill", "crisp_status_string", "crisp_varlen_col_capacity", "crisp_varlen_workspace_bytes",
+           "crisp_prefill_varlen")
 
 
 class CrispShape(C.Structure):
@@ -82,6 +83,13 @@ def lib() -> C.CDLL:
             getattr(L, f).restype = C.c_int
         L.crisp_status_string.argtypes = [C.c_int]
         L.crisp_status_string.restype = C.c_char_p
+        i64p = C.POINTER(C.c_int64)
+        L.crisp_varlen_col_capacity.argtypes = [sp, C.c_int32, i64p]
+        L.crisp_varlen_col_capacity.restype = C.c_int64
+        L.crisp_varlen_workspace_bytes.argtypes = [sp, C.c_int32, i64p, pp]
+        L.crisp_varlen_workspace_bytes.restype = C.c_size_t
+        L.crisp_prefill_varlen.argtypes = [sp, C.c_int32, i64p, vp, vp, vp, pp, selp, vp, vp, C.c_size_t, vp]
+        L.crisp_prefill_varlen.restype = C.c_int
         _LIB = L
     return _LIB
 
@@ -268,4 +276,67 @@ def crisp_prefill(q, k, v, params: CrispParams | None = None, sel: Selection | N
                              C.byref(c_sel), o.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
     if st:
         raise CrispError(st, "crisp_prefill")
+    return o, sel
+
+
+# ------------------------------------------------------------------ packed batches (varlen)
+
+def _cu(cu_seqlens):
+    cu = [int(x) for x in cu_seqlens]
+    return (C.c_int64 * len(cu))(*cu), len(cu) - 1
+
+
+def varlen_col_capacity(shape: CrispShape, cu_seqlens) -> int:
+    arr, nseq = _cu(cu_seqlens)
+    return int(lib().crisp_varlen_col_capacity(C.byref(shape), nseq, arr))
+
+
+def varlen_workspace_bytes(shape: CrispShape, cu_seqlens, params: CrispParams) -> int:
+    arr, nseq = _cu(cu_seqlens)
+    return int(lib().crisp_varlen_workspace_bytes(C.byref(shape), nseq, arr, C.byref(params.c())))
+
+
+def new_varlen_selection(q: torch.Tensor, k: torch.Tensor, cu_seqlens, diagnostics: bool = True,
+                         pe_prob: bool = False) -> Selection:
+    """Buffers for crisp_prefill_varlen: sequence-major (see include/crisp.h)."""
+    shape = make_shape(q, k)
+    hq = q.shape[0]
+    nbs = [(int(b) - int(a)) // BLOCK for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:])]
+    nseq = len(nbs)
+    rows = hq * sum(nbs)
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    cap = varlen_col_capacity(shape, cu_seqlens)
+    sel = Selection(torch.empty(nseq * hq, **i32), torch.empty(nseq * hq, **f32), torch.empty(rows + nseq, **i32),
+                    torch.empty(max(cap, 1), **i32))
+    if diagnostics:
+        sel.pv, sel.ps = torch.empty(rows, **f32), torch.empty(rows, **f32)
+        sel.sv, sel.ss = torch.empty(rows, **i32), torch.empty(rows, **i32)
+        sel.nv, sel.ns = torch.empty(nseq * hq, **i32), torch.empty(nseq * hq, **i32)
+        sel.jsd = torch.zeros(nseq * hq, dtype=torch.float64, device=dev)
+        sel.abar = torch.zeros(rows, **f32)
+    if pe_prob:
+        sel.pe_prob = torch.empty(max(cap, 1), **f32)
+    sel.extra["cu_seqlens"] = [int(x) for x in cu_seqlens]
+    return sel
+
+
+def crisp_prefill_varlen(q, k, v, cu_seqlens, params: CrispParams | None = None, sel: Selection | None = None,
+                         o=None, ws=None, diagnostics: bool = True, pe_prob: bool = False):
+    """Several sequences packed along the token axis (cu_seqlens: host offsets,
+    multiples of 128); each is routed and selected on its own, attention is one
+    launch.  Returns (o, sel)."""
+    params = params or CrispParams()
+    o = torch.empty_like(q) if o is None else o
+    shape = make_shape(q, k, v, o)
+    sel = sel or new_varlen_selection(q, k, cu_seqlens, diagnostics, pe_prob)
+    arr, nseq = _cu(cu_seqlens)
+    ws = _workspace(varlen_workspace_bytes(shape, cu_seqlens, params), q.device, ws)
+    c_sel = sel.c()
+    st = lib().crisp_prefill_varlen(C.byref(shape), nseq, arr, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    C.byref(params.c()), C.byref(c_sel), o.data_ptr(), ws.data_ptr(), ws.numel(),
+                                    _stream())
+    if st:
+        raise CrispError(st, "crisp_prefill_varlen")
     return o, sel

@@ -164,13 +164,20 @@ constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 // queues until all are empty, which evens out groups of unequal work.  Only
 // locality depends on the placement; every item is taken exactly once.
 
-// t-th item of queue x -> (pair, kvh, h); false once the queue is exhausted
-__device__ inline bool queue_item(int x, int t, int npair, int hq, int hkv, int& pair, int& kvh, int& h) {
+// t-th item of queue x -> (sequence, pair, kvh, h); false once the queue is
+// exhausted.  Units are numbered sequence after sequence (each longest rows
+// first); with hkv dividing 8 a queue keeps one KV group in every sequence.
+__device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int hkv, int& seq, int& pair, int& kvh,
+                                  int& h) {
   const int G = hq / hkv;
   const int u = NQUEUE * (t / G) + x;                       // the queue's (t/G)-th unit
-  if (u >= npair * hkv) return false;
-  pair = npair - 1 - u / hkv;
-  kvh = u % hkv;
+  if (u >= sq.unit_off[sq.nseq]) return false;
+  int i = 0;
+  while (u >= sq.unit_off[i + 1]) ++i;
+  const int v = u - sq.unit_off[i];
+  seq = i;
+  pair = ((sq.nb[i] + 1) >> 1) - 1 - v / hkv;
+  kvh = v % hkv;
   h = kvh * G + t % G;
   return true;
 }
@@ -210,7 +217,7 @@ __device__ __forceinline__ void fa_bf16_item(
     char* smem, int pair, int kvh, int h,
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
-    int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, float sl2) {
+    int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, int64_t vt_h, float sl2) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = w >> 2, wq = w & 3;
@@ -254,7 +261,7 @@ __device__ __forceinline__ void fa_bf16_item(
   const uint32_t lbase = lds_addr(smem);
   const uint32_t krow = (uint32_t)(sk_n * 2);
   const char* Kh = (const char*)(K + (int64_t)kvh * sk_h);
-  const char* Vh = (const char*)(Vt + (int64_t)kvh * nb * (BLK * HD));
+  const char* Vh = (const char*)(Vt + (int64_t)kvh * vt_h);
   TileCopy kc, vc;
   kc.init(w, lane, krow);
   vc.init(w, lane, 256);
@@ -395,13 +402,13 @@ __device__ __forceinline__ void fa_bf16_item(
 template <bool DENSE>
 __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue, int nb,
-    int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n,
-    float sl2) {
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue,
+    const SeqTable sq, int nb_total, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n,
+    int64_t so_h, int64_t so_n, float sl2) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
   __shared__ int s_item;
-  const int npair = (nb + 1) >> 1;
   const int home = blockIdx.x % NQUEUE;
+  const int64_t vt_h = (int64_t)nb_total * (BLK * HD);
   for (int k = 0; k < NQUEUE; ++k) {
     const int x = (home + k) % NQUEUE;
     while (true) {
@@ -409,10 +416,12 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
       __syncthreads();                            // every wave is done with the last item's LDS
       if (threadIdx.x == 0) s_item = atomicAdd(queue + x, 1);
       __syncthreads();
-      int pair, kvh, h;
-      if (!queue_item(x, s_item, npair, hq, hkv, pair, kvh, h)) break;
-      fa_bf16_item<DENSE>(smem, pair, kvh, h, Q, K, Vt, O, row_ptr, col_idx, nb, hq, hkv, sq_h, sq_n, sk_h,
-                          sk_n, so_h, so_n, sl2);
+      int seq, pair, kvh, h;
+      if (!queue_item(x, s_item, sq, hq, hkv, seq, pair, kvh, h)) break;
+      const int64_t t0 = sq.tok[seq];
+      fa_bf16_item<DENSE>(smem, pair, kvh, h, Q + t0 * sq_n, K + t0 * sk_n, Vt + t0 * HD, O + t0 * so_n,
+                          row_ptr + sq.rp[seq], col_idx + sq.col[seq], sq.nb[seq], hq, hkv, sq_h, sq_n, sk_h,
+                          sk_n, so_h, so_n, vt_h, sl2);
     }
   }
 }
@@ -423,7 +432,7 @@ template <bool DENSE>
 __global__ __launch_bounds__(256, 1) void fa_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ Vt, float* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
-    int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, float sl2) {
+    int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, int64_t vt_h, float sl2) {
   constexpr int KP = Tile<float>::KP, VP = 132;
   __shared__ __attribute__((aligned(16))) float sK[BLK * KP];
   __shared__ __attribute__((aligned(16))) float sV[HD * VP];
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void fa_f32_kernel(
     if ((unsigned)kb > (unsigned)qb) continue;  // no key j <= i in a later block
     __syncthreads();
     Tile<float>::load_k(sK, K + (int64_t)kvh * sk_h + (int64_t)kb * BLK * sk_n, sk_n, tid);
-    Tile<float>::load_k(sV, Vt + ((int64_t)kvh * nb + kb) * (BLK * HD), BLK, tid);
+    Tile<float>::load_k(sV, Vt + (int64_t)kvh * vt_h + (int64_t)kb * (BLK * HD), BLK, tid);
     __syncthreads();
     f32x16 s[4];
     Tile<float>::st(s, sK, qf, l32, g);
@@ -532,20 +541,26 @@ static int cu_count() {
 }
 
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
-                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, int nb, int hq, int hkv,
-                            const Strides& st, hipStream_t s) {
+                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, const SeqTable& seqs,
+                            int nb_total, int hq, int hkv, const Strides& st, hipStream_t s) {
   const float sl2 = LOG2E / sqrtf((float)HD);
-  if (fp32) {
-    const dim3 grid((unsigned)((int64_t)nb * hq));
+  const int64_t vt_h = (int64_t)nb_total * (BLK * HD);
+  if (fp32) {  // one launch per sequence (the fp32 path serves small checking layers)
     auto k = dense ? fa_f32_kernel<true> : fa_f32_kernel<false>;
-    k<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (const float*)Vt, (float*)O, row_ptr, col_idx, nb,
-                           hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
+    for (int i = 0; i < seqs.nseq; ++i) {
+      const int64_t t0 = seqs.tok[i];
+      const dim3 grid((unsigned)((int64_t)seqs.nb[i] * hq));
+      k<<<grid, 256, 0, s>>>((const float*)Q + t0 * st.q_n, (const float*)K + t0 * st.k_n,
+                             (const float*)Vt + t0 * HD, (float*)O + t0 * st.o_n,
+                             row_ptr ? row_ptr + seqs.rp[i] : nullptr, col_idx ? col_idx + seqs.col[i] : nullptr,
+                             seqs.nb[i], hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, vt_h, sl2);
+    }
   } else {
-    const int64_t items = (int64_t)((nb + 1) / 2) * hq;
-    const dim3 grid((unsigned)std::min<int64_t>(items, cu_count()));
+    const int64_t items = (int64_t)seqs.unit_off[seqs.nseq] * (hq / hkv);
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, cu_count())));
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
-    k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, nb,
-                           hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
+    k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, seqs,
+                           nb_total, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   }
   return hipGetLastError();
 }

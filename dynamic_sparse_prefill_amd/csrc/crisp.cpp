@@ -188,15 +188,78 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
                                  p->alpha, p->gamma, p->min_blocks, b, stream));
 }
 
+SeqTable single_sequence(int nb, int hkv) {
+  SeqTable t;
+  t.nseq = 1;
+  t.unit_off[0] = 0;
+  t.unit_off[1] = ((nb + 1) / 2) * hkv;
+  t.nb[0] = nb;
+  t.tok[0] = 0;
+  t.rp[0] = 0;
+  t.col[0] = 0;
+  return t;
+}
+
 int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
-             const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream) {
+             const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream, const SeqTable* seqs = nullptr) {
   const int nb = (int)(s->n / BLK);
   const int fp32 = s->dtype == CRISP_FP32;
   int* queue = (int*)((char*)ws + vt_bytes(s));
   hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, queue, stream);
   if (e != hipSuccess) return CRISP_E_HIP;
-  return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, queue, nb, s->hq, s->hkv,
-                                    strides(s), stream));
+  const SeqTable one = single_sequence(nb, s->hkv);
+  return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, queue, seqs ? *seqs : one, nb,
+                                    s->hq, s->hkv, strides(s), stream));
+}
+
+// ---- packed batches (varlen)
+
+struct VarlenPlan {
+  int nseq;
+  int64_t len[MAX_SEQ], tok[MAX_SEQ];
+  int64_t rows_before[MAX_SEQ];   // hq * nb of the earlier sequences (diagnostic arrays)
+  int64_t rp_before[MAX_SEQ];     // row_ptr entries of the earlier sequences (hq * nb + 1 each)
+  int64_t col_before[MAX_SEQ];    // list capacity of the earlier sequences (hq * nb(nb+1)/2 each)
+  int64_t col_total;
+  size_t sel_ws;                  // selection workspace of the largest sequence (reused in turn)
+};
+
+crisp_shape sub_shape(const crisp_shape* s, int64_t len) {
+  crisp_shape t = *s;
+  t.n = len;
+  return t;
+}
+
+int plan_varlen(const crisp_shape* s, int32_t nseq, const int64_t* cu, const crisp_params* p, VarlenPlan* P) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (nseq < 1 || !cu) return CRISP_E_ARG;
+  if (nseq > MAX_SEQ) return CRISP_E_UNSUPPORTED;
+  if (cu[0] != 0 || cu[nseq] != s->n) return CRISP_E_ARG;
+  P->nseq = nseq;
+  int64_t rows = 0, rp = 0, col = 0;
+  size_t ws = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const int64_t len = cu[i + 1] - cu[i];
+    if (len <= 0 || len % BLK) return CRISP_E_ARG;
+    const crisp_shape t = sub_shape(s, len);
+    if ((st = check_shape(&t))) return st;
+    if (p && (st = check_params(&t, p))) return st;
+    const int64_t nb = len / BLK;
+    P->len[i] = len;
+    P->tok[i] = cu[i];
+    P->rows_before[i] = rows;
+    P->rp_before[i] = rp;
+    P->col_before[i] = col;
+    rows += s->hq * nb;
+    rp += s->hq * nb + 1;
+    col += s->hq * tri(nb);
+    const size_t w = select_layout(&t).total;
+    if (w > ws) ws = w;
+  }
+  P->col_total = col;
+  P->sel_ws = ws;
+  return CRISP_OK;
 }
 
 }  // namespace
@@ -262,6 +325,69 @@ int crisp_prefill(const crisp_shape* shape, const void* q, const void* k, const 
   st = run_select(shape, q, k, params, sel, workspace, stream);
   if (st) return st;
   return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream);
+}
+
+int64_t crisp_varlen_col_capacity(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens) {
+  VarlenPlan P;
+  if (plan_varlen(shape, nseq, cu_seqlens, nullptr, &P)) return 0;
+  return P.col_total;
+}
+
+size_t crisp_varlen_workspace_bytes(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens,
+                                    const crisp_params* params) {
+  VarlenPlan P;
+  if (!params || plan_varlen(shape, nseq, cu_seqlens, params, &P)) return 0;
+  return align256(P.sel_ws) + attn_ws(shape);
+}
+
+int crisp_prefill_varlen(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens, const void* q,
+                         const void* k, const void* v, const crisp_params* params, crisp_selection* sel, void* o,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  VarlenPlan P;
+  if (!params) return CRISP_E_ARG;
+  int st = plan_varlen(shape, nseq, cu_seqlens, params, &P);
+  if (st) return st;
+  if (!sel || !sel->route || !sel->c_struct || !sel->row_ptr || !sel->col_idx) return CRISP_E_ARG;
+  if (sel->col_capacity < P.col_total) return CRISP_E_WORKSPACE;
+  if ((st = check_qkv(shape, q, k, v, o))) return st;
+  if (!v || !o || !workspace || ((uintptr_t)workspace & 255)) return CRISP_E_ARG;
+  const size_t sel_bytes = align256(P.sel_ws);
+  if (workspace_bytes < sel_bytes + attn_ws(shape)) return CRISP_E_WORKSPACE;
+  const size_t esz = shape->dtype == CRISP_FP32 ? 4 : 2;
+  const int hq = shape->hq;
+  SeqTable seqs;
+  seqs.nseq = nseq;
+  seqs.unit_off[0] = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const crisp_shape t = sub_shape(shape, P.len[i]);
+    const int64_t nb = P.len[i] / BLK, t0 = P.tok[i];
+    crisp_selection w = *sel;
+    auto at = [](auto* base, int64_t off) { return base ? base + off : base; };
+    w.route = sel->route + (int64_t)i * hq;
+    w.c_struct = sel->c_struct + (int64_t)i * hq;
+    w.row_ptr = sel->row_ptr + P.rp_before[i];
+    w.col_idx = sel->col_idx + P.col_before[i];
+    w.col_capacity = hq * tri(nb);
+    w.pv = at(sel->pv, P.rows_before[i]);
+    w.ps = at(sel->ps, P.rows_before[i]);
+    w.sv = at(sel->sv, P.rows_before[i]);
+    w.ss = at(sel->ss, P.rows_before[i]);
+    w.nv = at(sel->nv, (int64_t)i * hq);
+    w.ns = at(sel->ns, (int64_t)i * hq);
+    w.pe_prob = at(sel->pe_prob, P.col_before[i]);
+    w.jsd = at(sel->jsd, (int64_t)i * hq);
+    w.abar = at(sel->abar, P.rows_before[i]);
+    st = run_select(&t, (const char*)q + t0 * shape->sq_n * esz, (const char*)k + t0 * shape->sk_n * esz, params,
+                    &w, workspace, stream);
+    if (st) return st;
+    seqs.nb[i] = (int)nb;
+    seqs.tok[i] = t0;
+    seqs.rp[i] = P.rp_before[i];
+    seqs.col[i] = P.col_before[i];
+    seqs.unit_off[i + 1] = seqs.unit_off[i] + (int)((nb + 1) / 2) * shape->hkv;
+  }
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)workspace + sel_bytes, stream,
+                  &seqs);
 }
 
 const char* crisp_status_string(int status) {

@@ -12,10 +12,26 @@ struct Strides { int64_t q_h, q_n, k_h, k_n, v_h, v_n, o_h, o_n; };
 // V [hkv][n][d] -> per-block transposed V^T; also zeroes *queue (may be NULL)
 hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv,
                               int64_t sv_h, int64_t sv_n, int* queue, hipStream_t s);
-// queue: the persistent kernel's work counter, zero at launch (set by launch_transpose_v)
+
+// Sequences of a packed batch (a single prefill is one sequence).  Passed by
+// value to the attention kernel.  Sequence i owns tokens [tok[i], tok[i] + 128
+// nb[i]) of Q, K, V^T and O, and its lists live at row_ptr + rp[i] (hq * nb[i]
+// + 1 entries, offsets relative to col_idx + col[i]).
+constexpr int MAX_SEQ = 64;
+struct SeqTable {
+  int nseq;
+  int unit_off[MAX_SEQ + 1];   // work units (query-block pairs x KV heads) before sequence i
+  int nb[MAX_SEQ];
+  int64_t tok[MAX_SEQ];
+  int64_t rp[MAX_SEQ];
+  int64_t col[MAX_SEQ];
+};
+
+// queue: the persistent kernel's work counter, zero at launch (set by launch_transpose_v).
+// nb_total: blocks of the whole packed V^T (its head stride).
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
-                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, int nb, int hq, int hkv,
-                            const Strides& st, hipStream_t s);
+                            const int32_t* row_ptr, const int32_t* col_idx, int* queue, const SeqTable& seqs,
+                            int nb_total, int hq, int hkv, const Strides& st, hipStream_t s);
 
 // ---- proxy (proxy.hip)
 int proxy_chunks(int nb);

@@ -159,6 +159,28 @@ int crisp_prefill(const crisp_shape *shape, const void *q, const void *k, const 
                   const crisp_params *params, crisp_selection *sel, void *o,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- packed batches (varlen) ------------------------------------------------
+ * nseq sequences (1 <= nseq <= 64) packed along the token axis of q, k, v, o:
+ * sequence i holds tokens [cu_seqlens[i], cu_seqlens[i+1]) and attends only
+ * within itself (causal).  cu_seqlens is a HOST array of nseq + 1 offsets with
+ * cu_seqlens[0] = 0, cu_seqlens[nseq] = shape->n, every length a positive
+ * multiple of 128.  Each sequence is routed and selected on its own, exactly as
+ * crisp_prefill would on it alone [the pages leave batching open; CRISP §2
+ * defines every step per head and per prompt]; the attention of all sequences
+ * is one launch.  Selection outputs are sequence-major: route, c_struct, nv,
+ * ns, jsd hold hq entries per sequence; pv, ps, sv, ss, abar hq * N_b(i) per
+ * sequence; row_ptr holds hq * N_b(i) + 1 entries per sequence, relative to the
+ * sequence's col_idx segment, which starts after hq * N_b(j)(N_b(j)+1)/2 entries
+ * for every earlier sequence j (pe_prob is laid out the same way).  Errors as
+ * for crisp_prefill; nseq > 64 is CRISP_E_UNSUPPORTED. */
+int64_t crisp_varlen_col_capacity(const crisp_shape *shape, int32_t nseq, const int64_t *cu_seqlens);
+size_t crisp_varlen_workspace_bytes(const crisp_shape *shape, int32_t nseq, const int64_t *cu_seqlens,
+                                    const crisp_params *params);
+int crisp_prefill_varlen(const crisp_shape *shape, int32_t nseq, const int64_t *cu_seqlens,
+                         const void *q, const void *k, const void *v, const crisp_params *params,
+                         crisp_selection *sel, void *o, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Static description of a status code. */
 const char *crisp_status_string(int status);
 

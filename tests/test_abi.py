@@ -105,3 +105,27 @@ def test_attention_entry_points_validate():
     assert L.crisp_prefill(C.byref(s), 16, 16, 16, C.byref(dsp.CrispParams().c()), None, 16, 256, 1 << 40,
                            None) == -1
     assert dsp.api.status_string(-3).startswith("workspace")
+
+
+def test_varlen_queries_and_validation():
+    L = dsp.lib()
+    n = 4096 + 1024 + 256
+    s = _shape(n=n)
+    p = dsp.CrispParams()
+    cu = [0, 4096, 5120, n]
+    nbs = [32, 8, 2]
+    assert dsp.varlen_col_capacity(s, cu) == sum(4 * nb * (nb + 1) // 2 for nb in nbs)
+    assert dsp.varlen_workspace_bytes(s, cu, p) > dsp.attn_workspace_bytes(s)
+    for bad in ([0, 4096, n - 64, n], [64, 4096, n], [0, 4096, 4096, n], [0, 4096, 5120, n + 128]):
+        assert dsp.varlen_col_capacity(s, bad) == 0
+    arr = (C.c_int64 * 4)(*cu)
+    sel = api.CrispSelectionC(16, 16, 16, 16, 1 << 40)
+    args = (16, 16, 16, C.byref(p.c()), C.byref(sel), 16, 256, 1 << 40, None)
+    assert L.crisp_prefill_varlen(C.byref(s), 0, arr, *args) == -1
+    assert L.crisp_prefill_varlen(C.byref(s), 3, None, *args) == -1
+    big = (C.c_int64 * 66)(*([128 * i for i in range(65)] + [0]))
+    s65 = _shape(n=128 * 65)
+    assert L.crisp_prefill_varlen(C.byref(s65), 65, big, *args) == -2
+    small = api.CrispSelectionC(16, 16, 16, 16, 10)
+    assert L.crisp_prefill_varlen(C.byref(s), 3, arr, 16, 16, 16, C.byref(p.c()), C.byref(small), 16, 256,
+                                  1 << 40, None) == -3

@@ -357,3 +357,61 @@ def test_flexprefill_configuration_llama_128k():
     blocks = synth.sample_blocks(cfg.nb, 4, 5)
     mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), heads, blocks)
     P.log(f"[flex 128k] attention max {mx:.2e} mean {mean:.2e}")
+
+
+# ------------------------------------------------------------------ packed batches (varlen)
+
+@pytest.mark.parametrize("flags", [0, dsp.FLAG_ROUTE_JSD | dsp.FLAG_VS_COVERAGE])
+def test_varlen_batch_equals_single_calls(flags):
+    """Three sequences of different lengths (one short enough for the dense
+    path) packed into one call: every selection output and every output row is
+    bitwise equal to running each sequence alone; one sequence's outputs are
+    also checked against the oracle."""
+    lens = [8192, 2048, 256, 4096]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    hq, hkv = 8, 2
+    parts = []
+    for i, n in enumerate(lens):
+        cfg = synth.custom_config(f"varlen{i}", n, hq, hkv, seed=60 + i, conc_frac=0.5)
+        spec = synth.make_spec(cfg)
+        parts.append((spec,) + synth.generate(spec))
+    Q = np.concatenate([p[1] for p in parts], axis=1)
+    K = np.concatenate([p[2] for p in parts], axis=1)
+    V = np.concatenate([p[3] for p in parts], axis=1)
+    spec0 = parts[0][0]
+    q, k, v = P.to_device(spec0, Q), P.to_device(spec0, K), P.to_device(spec0, V)
+    params = P.params_of(spec0.cfg, tau=0.01 if flags else 0.3, flags=flags)
+    o, sel = dsp.crisp_prefill_varlen(q, k, v, cu, params, pe_prob=True)
+    torch.cuda.synchronize()
+    rows0, rp0, col0 = 0, 0, 0
+    for i, n in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        nb = n // 128
+        qi, ki, vi = q[:, a:b].contiguous(), k[:, a:b].contiguous(), v[:, a:b].contiguous()
+        oi, si = dsp.crisp_prefill(qi, ki, vi, params, pe_prob=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, a:b], oi), f"sequence {i}: output differs"
+        assert torch.equal(sel.route[i * hq:(i + 1) * hq], si.route)
+        assert torch.equal(sel.c_struct[i * hq:(i + 1) * hq], si.c_struct)
+        assert torch.equal(sel.row_ptr[rp0:rp0 + hq * nb + 1], si.row_ptr)
+        m = int(si.row_ptr[-1])
+        assert torch.equal(sel.col_idx[col0:col0 + m], si.col_idx[:m])
+        if si.route[0].item() != -1:
+            assert torch.equal(sel.pv[rows0:rows0 + hq * nb], si.pv)
+            if flags:
+                assert torch.equal(sel.jsd[i * hq:(i + 1) * hq], si.jsd)
+        rows0 += hq * nb
+        rp0 += hq * nb + 1
+        col0 += hq * nb * (nb + 1) // 2
+    # the first sequence against the oracle: decisions from its own scores and sampled rows
+    n0, nb0 = lens[0], lens[0] // 128
+    sub = dsp.Selection(sel.route[:hq], sel.c_struct[:hq], sel.row_ptr[:hq * nb0 + 1], sel.col_idx,
+                        sel.pv[:hq * nb0], sel.ps[:hq * nb0], sel.sv[:hq * nb0], sel.nv[:hq], sel.ss[:hq * nb0],
+                        sel.ns[:hq], sel.pe_prob, sel.jsd[:hq], sel.abar[:hq * nb0])
+    rep = P.check_decisions(sub, hq, nb0, params)
+    P.log(f"[varlen flags={flags}] decisions", rep)
+    rp, col = P.gpu_lists(sub, hq, nb0)
+    lists = lambda h, qb: col[rp[h * nb0 + qb]: rp[h * nb0 + qb + 1]]
+    mx, mean = P.check_attention_blocks(parts[0][0], parts[0][1], parts[0][2], parts[0][3], o[:, :n0], lists,
+                                        range(hq), synth.sample_blocks(nb0, 6, 7))
+    P.log(f"[varlen] attention max {mx:.2e} mean {mean:.2e}")
