@@ -20,10 +20,12 @@ gamma 0.95, length-compensated generator).  Printed as one JSON line:
                  median floor, universal configuration, FlexPrefill's pair
   cpu_baseline   the CPU oracle on a bounded sample of the same layer,
                  extrapolated to ms per layer
-  extra          the 128k layers (Llama and Qwen shaped) and an 8k-64k
-                 length sweep (CRISP vs dense, the length gate)
+  extra          the 128k layers (Llama and Qwen shaped), a 4k-64k
+                 length sweep (CRISP vs dense, the length gate) and packed
+                 batches of 512k tokens (one varlen call vs one call each)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra] [--no-compare] [--no-sweep]
+                       [--no-varlen]
 """
 from __future__ import annotations
 
@@ -170,8 +172,8 @@ def compare_rules(cfg, q, k, v, dsp, torch, steps, dense_ms):
     return out
 
 
-def length_sweep(dsp, torch, synth, ns=(8192, 16384, 32768, 65536), steps=3):
-    """CRISP vs dense ms per layer on Llama-shaped layers of growing length:
+def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=3):
+    """CRISP vs dense ms per layer on Llama-shaped layers of growing length (4k-64k):
     where sparse prefill starts to pay (the length gate)."""
     res = {}
     for n in ns:
@@ -192,6 +194,50 @@ def length_sweep(dsp, torch, synth, ns=(8192, 16384, 32768, 65536), steps=3):
                   "density": round(int(sel.row_ptr[-1].item()) / (32 * nb * (nb + 1) // 2), 4)}
         log(f"[bench] length {n}: {res[n]}")
         del q, k, v, o, sel, ws, aws
+        torch.cuda.empty_cache()
+    return res
+
+
+def varlen_batches(dsp, torch, synth, steps=3):
+    """Packed batches of Llama-shaped sequences (512k tokens in total): one
+    crisp_prefill_varlen call against the same sequences one call each."""
+    res = {}
+    for name, lens in (("8x64k", [65536] * 8), ("64x8k", [8192] * 64),
+                       ("mixed-128k..16k", [131072] + [65536] * 2 + [32768] * 4 + [16384] * 8)):
+        parts = []
+        for i, n in enumerate(lens):
+            cfg = synth.custom_config(f"batch-{i}", n, 32, 8, seed=100 + i, conc_frac=0.6)
+            parts.append(synth.generate(synth.make_spec(cfg), threads=16))
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        q = to_dev(np.concatenate([p[0] for p in parts], axis=1))
+        k = to_dev(np.concatenate([p[1] for p in parts], axis=1))
+        v = to_dev(np.concatenate([p[2] for p in parts], axis=1))
+        del parts
+        cu = [0] + np.cumsum(lens).tolist()
+        p = dsp.CrispParams()
+        o = torch.empty_like(q)
+        sel = dsp.new_varlen_selection(q, k, cu, diagnostics=False)
+        ws = torch.empty(dsp.varlen_workspace_bytes(dsp.make_shape(q, k, v, o), cu, p), dtype=torch.uint8,
+                         device="cuda")
+        ms = timed(lambda: dsp.crisp_prefill_varlen(q, k, v, cu, p, sel=sel, o=o, ws=ws), steps, 1, torch)
+        singles = []
+        for a, b in zip(cu[:-1], cu[1:]):
+            qi, ki, vi = q[:, a:b], k[:, a:b], v[:, a:b]
+            si = dsp.new_selection(qi, ki, diagnostics=False)
+            wi = torch.empty(dsp.workspace_bytes(dsp.make_shape(qi, ki, vi, o[:, a:b]), p), dtype=torch.uint8,
+                             device="cuda")
+            singles.append((qi, ki, vi, si, wi, o[:, a:b]))
+
+        def one_by_one():
+            for qi, ki, vi, si, wi, oi in singles:
+                dsp.crisp_prefill(qi, ki, vi, p, sel=si, o=oi, ws=wi)
+
+        ms1 = timed(one_by_one, steps, 1, torch)
+        tok = cu[-1]
+        res[name] = {"sequences": len(lens), "tokens": tok, "batch_ms": round(ms, 3), "one_call_each_ms": round(ms1, 3),
+                     "batch_tokens_per_s": round(tok / (ms * 1e-3)), "speedup_over_calls": round(ms1 / ms, 3)}
+        log(f"[bench] varlen {name}: {res[name]}")
+        del q, k, v, o, sel, ws, singles
         torch.cuda.empty_cache()
     return res
 
@@ -325,7 +371,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline (counter-collection runs)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the decision-rule comparison (median floor, universal config, FlexPrefill)")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the 8k-64k length sweep (length gate)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 4k-64k length sweep (length gate)")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch (varlen) measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -349,6 +396,8 @@ def main():
     extra = {}
     if not args.no_sweep:
         extra["length_sweep"] = length_sweep(dsp, torch, synth)
+    if not args.no_varlen:
+        extra["varlen"] = varlen_batches(dsp, torch, synth)
     if not args.no_extra:
         for cid in (2, 3):
             if cid == args.workload:
