@@ -117,7 +117,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Four 16-byte LDS reads at addr + OFF + {0, 8, 16, 24} KB (rows 0, 32, 64, 96
 // of a tile for this lane), completed inside the same asm block.  Written by
 // hand so that the compiler does not add a wait on the in-flight global->LDS
-// copy of the next tile before them.
+// copy of the next tile before them.  The outputs are early-clobber: a read's
+// result may land while later reads of the block still need the address
+// registers, so no output may share a register with an address.
 template <int OFF>
 __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
   asm volatile(
@@ -126,7 +128,7 @@ __device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
       "ds_read_b128 %2, %4 offset:%7\n\t"
       "ds_read_b128 %3, %4 offset:%8\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(a[0]), "=v"(a[1]), "=v"(a[2]), "=v"(a[3])
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
       : "v"(addr), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
       : "memory");
 }
@@ -146,7 +148,7 @@ __device__ __forceinline__ void lds_read8(bf16x8 (&a)[4], bf16x8 (&b)[4], uint32
       "ds_read_b128 %6, %9 offset:%12\n\t"
       "ds_read_b128 %7, %9 offset:%13\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(a[0]), "=v"(a[1]), "=v"(a[2]), "=v"(a[3]), "=v"(b[0]), "=v"(b[1]), "=v"(b[2]), "=v"(b[3])
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
       : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
       : "memory");
 }
