@@ -61,7 +61,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
-  size_t stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
+  size_t tstat, stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
       pepart, total;
 };
 
@@ -70,6 +70,7 @@ SelectLayout select_layout(const crisp_shape* s) {
   SelectLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.tstat = take(hq * nb * BLK * 16);
   L.stats = take(hq * nch * BLK * 8);
   L.rowstat = take(hq * BLK * 8);
   L.tiles = take(hq * nb * 16);
@@ -149,8 +150,8 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   const bool dense = dense_path(s, p);
   const Strides st = strides(s);
   if (!dense) {
-    hipError_t e = launch_proxy(fp32, q, k, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, w + L.stats,
-                                w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
+    hipError_t e = launch_proxy(fp32, q, k, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, w + L.tstat,
+                                w + L.stats, w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
     if (e != hipSuccess) return CRISP_E_HIP;
   }
   SelectBufs b;

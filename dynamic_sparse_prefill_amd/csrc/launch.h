@@ -34,11 +34,12 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
                             int nb_total, int hq, int hkv, const Strides& st, hipStream_t s);
 
 // ---- proxy (proxy.hip)
-int proxy_chunks(int nb);
+int proxy_chunks(int nb);   // row-statistics chunks of the proxy
 hipError_t launch_proxy(int fp32, const void* Q, const void* K, int64_t n, int nb, int hq, int hkv,
                         const Strides& st, int w_sink, int w_local,
-                        void* stats /*[hq*nchunk*128] float2*/, void* rowstat /*[hq*128] float2*/,
-                        void* tiles /*[hq*nb] float4*/, float* kbar /*[hkv*nb*128]*/, hipStream_t s);
+                        void* tstat /*[hq*nb*128] float4*/, void* stats /*[hq*nchunk*128] float2*/,
+                        void* rowstat /*[hq*128] float2*/, void* tiles /*[hq*nb] float4*/,
+                        float* kbar /*[hkv*nb*128]*/, hipStream_t s);
 
 // ---- selection (select.hip)
 struct PeCut;                       // per-head radix-select state (select.hip)
