@@ -115,12 +115,12 @@ def selection_roofline(cfg, route, tiles, sel_ms):
     """Selection as a whole against max(HBM, MFMA): algorithmic bytes = K once,
     Q of the Pooled-Estimation heads once, the pooled matrix of those heads
     written once and read twice (softmax + cut), the lists written once; flops =
-    the two proxy passes over K (2 * 128 * n * d * hq each)."""
+    one pass of the proxy scores over K (2 * 128 * n * d * hq)."""
     nb = cfg.n // 128
     h_pe = int((route == 0).sum())
     tri = nb * (nb + 1) // 2
     nbytes = cfg.hkv * cfg.n * 128 * 2 + h_pe * cfg.n * 128 * 2 + 3 * 4 * tri * h_pe + 4 * tiles
-    flops = 2 * (2 * 128 * cfg.n * 128 * cfg.hq)
+    flops = 2 * 128 * cfg.n * 128 * cfg.hq
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
     return {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "bytes": int(nbytes), "flops": int(flops),
