@@ -65,35 +65,56 @@ struct SelectLayout {
       pepart, total;
 };
 
-SelectLayout select_layout(const crisp_shape* s) {
-  const int64_t nb = s->n / BLK, hq = s->hq, hkv = s->hkv, nch = proxy_chunks((int)nb);
+SeqList one_sequence(const crisp_shape* s) {
+  SeqList L;
+  L.nseq = 1;
+  L.nb[0] = (int)(s->n / BLK);
+  return L;
+}
+
+// Packed per-row arrays hold every sequence's hq * N_b rows; per-head scratch
+// of fixed size is indexed by virtual head (sequence, query head) and sized
+// for the longest sequence.
+SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
+  const int64_t hq = s->hq, hkv = s->hkv, vh = seqs.nseq * hq;
+  int64_t rows = 0, kvrows = 0, tris = 0, nb_max = 0;
+  for (int i = 0; i < seqs.nseq; ++i) {
+    const int64_t nb = seqs.nb[i];
+    rows += hq * nb;
+    kvrows += hkv * nb;
+    tris += hq * tri(nb);
+    if (nb > nb_max) nb_max = nb;
+  }
+  const int64_t nch = proxy_chunks((int)nb_max);
+  const int64_t nseg = ((nb_max + 31) / 32 + 31) / 32;   // segments of 32 tiles of 32 key blocks
   SelectLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
-  L.tstat = take(hq * nb * BLK * 16);
-  L.stats = take(hq * nch * BLK * 8);
-  L.rowstat = take(hq * BLK * 8);
-  L.tiles = take(hq * nb * 16);
-  L.pv = take(hq * nb * 4);
-  L.ps = take(hq * nb * 4);
-  L.sv = take(hq * nb * 4);
-  L.ss = take(hq * nb * 4);
-  L.nv = take(hq * 4);
-  L.ns = take(hq * 4);
-  L.kbar = take(hkv * nb * HD * 4);
-  L.qbar = take(hq * nb * HD * 4);
-  L.P = take(hq * tri(nb) * 4);
-  L.hcnt = take(hq * 3 * PE_BUCKETS * 4);
-  L.hmass = take(hq * 3 * PE_BUCKETS * 8);
-  L.cut = take(hq * pe_cut_state_bytes());
-  L.eqrow = take(hq * nb * 4);
-  L.counts = take(hq * nb * 4);
-  L.jsd = take(hq * 8);
-  L.abar = take(hq * nb * 4);
-  L.pepart = take(hq * nb * (((nb + 31) / 32 + 31) / 32) * 8);   // segments of 32 tiles of 32 key blocks
+  L.tstat = take(rows * BLK * 16);
+  L.stats = take(vh * nch * BLK * 8);
+  L.rowstat = take(vh * BLK * 8);
+  L.tiles = take(rows * 16);
+  L.pv = take(rows * 4);
+  L.ps = take(rows * 4);
+  L.sv = take(rows * 4);
+  L.ss = take(rows * 4);
+  L.nv = take(vh * 4);
+  L.ns = take(vh * 4);
+  L.kbar = take(kvrows * HD * 4);
+  L.qbar = take(rows * HD * 4);
+  L.P = take(tris * 4);
+  L.hcnt = take(vh * 3 * PE_BUCKETS * 4);
+  L.hmass = take(vh * 3 * PE_BUCKETS * 8);
+  L.cut = take(vh * pe_cut_state_bytes());
+  L.eqrow = take(rows * 4);
+  L.counts = take(rows * 4);
+  L.jsd = take(vh * 8);
+  L.abar = take(rows * 4);
+  L.pepart = take(rows * nseg * 8);
   L.total = o;
   return L;
 }
+SelectLayout select_layout(const crisp_shape* s) { return select_layout(s, one_sequence(s)); }
 
 // Attention workspace: re-laid-out V^T, then the work-queue counter.
 size_t vt_bytes(const crisp_shape* s) {
@@ -102,10 +123,6 @@ size_t vt_bytes(const crisp_shape* s) {
 }
 size_t attn_ws(const crisp_shape* s) { return vt_bytes(s) + 256; }
 
-bool dense_path(const crisp_shape* s, const crisp_params* p) {
-  const int64_t nb = s->n / BLK;
-  return nb <= 2 || (p->dense_below_n > 0 && s->n < p->dense_below_n);
-}
 
 int status_of(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_E_HIP; }
 
@@ -141,19 +158,18 @@ int validate_attn(const crisp_shape* s, const void* q, const void* k, const void
   return CRISP_OK;
 }
 
+// Selection of every sequence in `seqs` (one prefill: one sequence), all at once.
 int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
-               void* ws, hipStream_t stream) {
-  const SelectLayout L = select_layout(s);
+               void* ws, hipStream_t stream, const SeqList& seqs) {
+  const SelectLayout L = select_layout(s, seqs);
   char* w = (char*)ws;
-  const int nb = (int)(s->n / BLK);
+  int nb_max = 0;
+  for (int i = 0; i < seqs.nseq; ++i) nb_max = seqs.nb[i] > nb_max ? seqs.nb[i] : nb_max;
   const int fp32 = s->dtype == CRISP_FP32;
-  const bool dense = dense_path(s, p);
   const Strides st = strides(s);
-  if (!dense) {
-    hipError_t e = launch_proxy(fp32, q, k, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, w + L.tstat,
-                                w + L.stats, w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
-    if (e != hipSuccess) return CRISP_E_HIP;
-  }
+  hipError_t e = launch_proxy(fp32, q, k, seqs, nb_max, s->hq, s->hkv, st, p->sink, p->local, p->dense_below_n,
+                              w + L.tstat, w + L.stats, w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
+  if (e != hipSuccess) return CRISP_E_HIP;
   SelectBufs b;
   b.tiles = w + L.tiles;
   b.kbar = (const float*)(w + L.kbar);
@@ -185,8 +201,12 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.abar = out->abar ? out->abar : (float*)(w + L.abar);
   b.router = (p->flags & CRISP_FLAG_ROUTE_JSD) ? 1 : 0;
   b.vs_budget = (p->flags & CRISP_FLAG_VS_MEDIAN) ? 1 : ((p->flags & CRISP_FLAG_VS_COVERAGE) ? 2 : 0);
-  return status_of(launch_select(fp32, dense, q, s->n, nb, s->hq, s->hkv, st, p->sink, p->local, p->tau,
-                                 p->alpha, p->gamma, p->min_blocks, b, stream));
+  return status_of(launch_select(fp32, q, seqs, nb_max, s->hq, s->hkv, st, p->sink, p->local, p->tau, p->alpha,
+                                 p->gamma, p->min_blocks, p->dense_below_n, b, stream));
+}
+int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
+               void* ws, hipStream_t stream) {
+  return run_select(s, q, k, p, out, ws, stream, one_sequence(s));
 }
 
 SeqTable single_sequence(int nb, int hkv) {
@@ -222,7 +242,8 @@ struct VarlenPlan {
   int64_t rp_before[MAX_SEQ];     // row_ptr entries of the earlier sequences (hq * nb + 1 each)
   int64_t col_before[MAX_SEQ];    // list capacity of the earlier sequences (hq * nb(nb+1)/2 each)
   int64_t col_total;
-  size_t sel_ws;                  // selection workspace of the largest sequence (reused in turn)
+  SeqList seqs;
+  size_t sel_ws;                  // selection workspace of the whole batch
 };
 
 crisp_shape sub_shape(const crisp_shape* s, int64_t len) {
@@ -239,7 +260,6 @@ int plan_varlen(const crisp_shape* s, int32_t nseq, const int64_t* cu, const cri
   if (cu[0] != 0 || cu[nseq] != s->n) return CRISP_E_ARG;
   P->nseq = nseq;
   int64_t rows = 0, rp = 0, col = 0;
-  size_t ws = 0;
   for (int i = 0; i < nseq; ++i) {
     const int64_t len = cu[i + 1] - cu[i];
     if (len <= 0 || len % BLK) return CRISP_E_ARG;
@@ -255,11 +275,11 @@ int plan_varlen(const crisp_shape* s, int32_t nseq, const int64_t* cu, const cri
     rows += s->hq * nb;
     rp += s->hq * nb + 1;
     col += s->hq * tri(nb);
-    const size_t w = select_layout(&t).total;
-    if (w > ws) ws = w;
+    P->seqs.nb[i] = (int)nb;
   }
   P->col_total = col;
-  P->sel_ws = ws;
+  P->seqs.nseq = nseq;
+  P->sel_ws = select_layout(s, P->seqs).total;
   return CRISP_OK;
 }
 
@@ -354,35 +374,16 @@ int crisp_prefill_varlen(const crisp_shape* shape, int32_t nseq, const int64_t* 
   if (!v || !o || !workspace || ((uintptr_t)workspace & 255)) return CRISP_E_ARG;
   const size_t sel_bytes = align256(P.sel_ws);
   if (workspace_bytes < sel_bytes + attn_ws(shape)) return CRISP_E_WORKSPACE;
-  const size_t esz = shape->dtype == CRISP_FP32 ? 4 : 2;
-  const int hq = shape->hq;
+  // selection of every sequence at once (virtual heads = sequence x query head)
+  st = run_select(shape, q, k, params, sel, workspace, stream, P.seqs);
+  if (st) return st;
   SeqTable seqs;
   seqs.nseq = nseq;
   seqs.unit_off[0] = 0;
   for (int i = 0; i < nseq; ++i) {
-    const crisp_shape t = sub_shape(shape, P.len[i]);
-    const int64_t nb = P.len[i] / BLK, t0 = P.tok[i];
-    crisp_selection w = *sel;
-    auto at = [](auto* base, int64_t off) { return base ? base + off : base; };
-    w.route = sel->route + (int64_t)i * hq;
-    w.c_struct = sel->c_struct + (int64_t)i * hq;
-    w.row_ptr = sel->row_ptr + P.rp_before[i];
-    w.col_idx = sel->col_idx + P.col_before[i];
-    w.col_capacity = hq * tri(nb);
-    w.pv = at(sel->pv, P.rows_before[i]);
-    w.ps = at(sel->ps, P.rows_before[i]);
-    w.sv = at(sel->sv, P.rows_before[i]);
-    w.ss = at(sel->ss, P.rows_before[i]);
-    w.nv = at(sel->nv, (int64_t)i * hq);
-    w.ns = at(sel->ns, (int64_t)i * hq);
-    w.pe_prob = at(sel->pe_prob, P.col_before[i]);
-    w.jsd = at(sel->jsd, (int64_t)i * hq);
-    w.abar = at(sel->abar, P.rows_before[i]);
-    st = run_select(&t, (const char*)q + t0 * shape->sq_n * esz, (const char*)k + t0 * shape->sk_n * esz, params,
-                    &w, workspace, stream);
-    if (st) return st;
+    const int64_t nb = P.len[i] / BLK;
     seqs.nb[i] = (int)nb;
-    seqs.tok[i] = t0;
+    seqs.tok[i] = P.tok[i];
     seqs.rp[i] = P.rp_before[i];
     seqs.col[i] = P.col_before[i];
     seqs.unit_off[i + 1] = seqs.unit_off[i] + (int)((nb + 1) / 2) * shape->hkv;

@@ -27,6 +27,41 @@ struct SeqTable {
   int64_t col[MAX_SEQ];
 };
 
+// Sequences of a selection batch (a single prefill is one sequence), by
+// value in the selection kernels: a kernel working on "virtual head"
+// vh = s * hq + h finds where sequence s starts in the packed arrays with
+// seq_pos.  Per-row arrays ([hq * N_b] per sequence) are sequence-major, the
+// pooled matrices ([hq * N_b(N_b+1)/2]) and the row pointers ([hq * N_b + 1])
+// likewise.
+struct SeqList {
+  int nseq;
+  int nb[MAX_SEQ];
+};
+struct SeqPos {
+  int nb;
+  int64_t tok;     // first token
+  int64_t rows;    // hq * N_b of the earlier sequences
+  int64_t tri;     // hq * N_b(N_b+1)/2 of the earlier sequences
+  int64_t rp;      // row pointers of the earlier sequences (hq * N_b + 1 each)
+  int64_t kvrows;  // hkv * N_b of the earlier sequences (K-bar rows)
+};
+__host__ __device__ inline SeqPos seq_pos(const SeqList& L, int s, int hq, int hkv) {
+  SeqPos p{L.nb[s], 0, 0, 0, 0, 0};
+  for (int i = 0; i < s; ++i) {
+    const int64_t b = L.nb[i];
+    p.tok += b * 128;
+    p.rows += hq * b;
+    p.tri += hq * b * (b + 1) / 2;
+    p.rp += hq * b + 1;
+    p.kvrows += hkv * b;
+  }
+  return p;
+}
+// the dense path of a sequence: N_b <= 2 (mu undefined) or shorter than the length gate
+__host__ __device__ inline bool seq_dense(int nb, int dense_below_n) {
+  return nb <= 2 || (dense_below_n > 0 && (int64_t)nb * 128 < dense_below_n);
+}
+
 // queue: the persistent kernel's work counter, zero at launch (set by launch_transpose_v).
 // nb_total: blocks of the whole packed V^T (its head stride).
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
@@ -35,11 +70,12 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
 
 // ---- proxy (proxy.hip)
 int proxy_chunks(int nb);   // row-statistics chunks of the proxy
-hipError_t launch_proxy(int fp32, const void* Q, const void* K, int64_t n, int nb, int hq, int hkv,
-                        const Strides& st, int w_sink, int w_local,
-                        void* tstat /*[hq*nb*128] float4*/, void* stats /*[hq*nchunk*128] float2*/,
-                        void* rowstat /*[hq*128] float2*/, void* tiles /*[hq*nb] float4*/,
-                        float* kbar /*[hkv*nb*128]*/, hipStream_t s);
+// nb_max: the longest sequence's N_b; stats holds proxy_chunks(nb_max) chunks per virtual head
+hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& seqs, int nb_max, int hq, int hkv,
+                        const Strides& st, int w_sink, int w_local, int dense_below_n,
+                        void* tstat /*[rows*128] float4*/, void* stats /*[nseq*hq*nchunk*128] float2*/,
+                        void* rowstat /*[nseq*hq*128] float2*/, void* tiles /*[rows] float4*/,
+                        float* kbar /*[kvrows*128]*/, hipStream_t s);
 
 // ---- selection (select.hip)
 struct PeCut;                       // per-head radix-select state (select.hip)
@@ -64,8 +100,9 @@ struct SelectBufs {
   int router, vs_budget;
 };
 
-hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,
+// nb_max: the longest sequence's N_b (grid extents, per-head scratch sizes)
+hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_max, int hq, int hkv,
                          const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
-                         int min_blocks, const SelectBufs& b, hipStream_t s);
+                         int min_blocks, int dense_below_n, const SelectBufs& b, hipStream_t s);
 
 }  // namespace crisp

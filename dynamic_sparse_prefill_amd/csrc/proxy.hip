@@ -32,6 +32,7 @@ constexpr int PCH = 8;        // key blocks per score work-group
 constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 
 int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
+__device__ __forceinline__ int rs_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
 
 // Lower / upper sums of one interior tile for wave W (rows 32W .. 32W+31),
 // p = exp2(s sl2 - mb).
@@ -57,9 +58,9 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
 template <typename T>
 __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           float4* __restrict__ tstat, float* __restrict__ kbar,
-                                                          int64_t n, int nb, int hq, int hkv, int64_t sq_h,
+                                                          const SeqList seqs, int hq, int hkv, int64_t sq_h,
                                                           int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
-                                                          int w_local, float sl2) {
+                                                          int w_local, int dense_below_n, float sl2) {
   __shared__ __attribute__((aligned(16))) T sK[BLK * Tile<T>::KP];
   __shared__ float red[2][HD];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -67,6 +68,14 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
   const int G = hq / hkv;
   const int chunk = blockIdx.x / hq, rem = blockIdx.x % hq;
   const int kvh = rem % hkv, hig = rem / hkv, h = kvh * G + hig;
+  const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
+  const int nb = sp.nb;
+  const int64_t n = (int64_t)nb * BLK;
+  if (chunk * PCH >= nb || seq_dense(nb, dense_below_n)) return;
+  Q += sp.tok * sq_n;
+  K += sp.tok * sk_n;
+  tstat += (sp.rows + (int64_t)h * nb) * BLK;
+  kbar += sp.kvrows * HD;
   const int qrow = 32 * w + l32;
   typename Tile<T>::QFrag qf;
   Tile<T>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
@@ -135,20 +144,25 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
     lo += __shfl_xor(lo, 32, 64);
     up += __shfl_xor(up, 32, 64);
     an += __shfl_xor(an, 32, 64);
-    if (g == 0) tstat[((int64_t)h * nb + kb) * BLK + qrow] = make_float4(mx, lo, up, an);
+    if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
   }
 }
 
 // Row statistics over RS_TILES tiles: M = max of the tile maxima, L = sum of
 // the tile sums rescaled to M (online, in tile order).
 __global__ __launch_bounds__(BLK) void proxy_rowstat_kernel(const float4* __restrict__ tstat,
-                                                            float2* __restrict__ stats, int nb, int nchunk,
-                                                            float sl2) {
-  const int chunk = blockIdx.x, h = blockIdx.y, r = threadIdx.x;
+                                                            float2* __restrict__ stats, const SeqList seqs, int hq,
+                                                            int hkv, int nchunk, int dense_below_n, float sl2) {
+  const int chunk = blockIdx.x, vh = blockIdx.y, r = threadIdx.x;
+  const int h = vh % hq;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (seq_dense(nb, dense_below_n)) return;
   const int t0 = chunk * RS_TILES, t1 = min(nb, t0 + RS_TILES);
+  tstat += (sp.rows + (int64_t)h * nb) * BLK;
   float M = -1e30f, L = 0.f;
   for (int t = t0; t < t1; ++t) {
-    const float4 v = tstat[((int64_t)h * nb + t) * BLK + r];
+    const float4 v = tstat[(int64_t)t * BLK + r];
     const float tot = v.y + v.z;
     if (v.x > M) {
       L = L * fast_exp2((M - v.x) * sl2) + tot;
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(BLK) void proxy_rowstat_kernel(const float4* __rest
       L += tot * fast_exp2((v.x - M) * sl2);
     }
   }
-  stats[((int64_t)h * nchunk + chunk) * BLK + r] = make_float2(M, L);
+  stats[((int64_t)vh * nchunk + chunk) * BLK + r] = make_float2(M, L);
 }
 
 // Row normaliser of the proxy rows: M = max over chunks, 1/L with L rescaled to
@@ -165,15 +179,19 @@ __global__ __launch_bounds__(BLK) void proxy_rowstat_kernel(const float4* __rest
 // (max, sum) pairs are merged in group order, so the result is reproducible.
 constexpr int CMB_GROUPS = 8;
 __global__ __launch_bounds__(BLK * CMB_GROUPS) void proxy_combine_kernel(const float2* __restrict__ stats,
-                                                                         float2* __restrict__ rowstat, int nchunk,
-                                                                         float sl2) {
+                                                                         float2* __restrict__ rowstat,
+                                                                         const SeqList seqs, int hq, int nchunk,
+                                                                         int dense_below_n, float sl2) {
   __shared__ float2 part[CMB_GROUPS][BLK];
-  const int h = blockIdx.x, r = threadIdx.x % BLK, grp = threadIdx.x / BLK;
+  const int h = blockIdx.x, r = threadIdx.x % BLK, grp = threadIdx.x / BLK;   // h: virtual head
+  const int nb = seqs.nb[h / hq];
+  if (seq_dense(nb, dense_below_n)) return;
+  const int nc = rs_chunks(nb);
   const float2* p = stats + (int64_t)h * nchunk * BLK + r;
   float M = -1e30f;
-  for (int c = grp; c < nchunk; c += CMB_GROUPS) M = fmaxf(M, p[(int64_t)c * BLK].x);
+  for (int c = grp; c < nc; c += CMB_GROUPS) M = fmaxf(M, p[(int64_t)c * BLK].x);
   float L = 0.f;
-  for (int c = grp; c < nchunk; c += CMB_GROUPS) {
+  for (int c = grp; c < nc; c += CMB_GROUPS) {
     const float2 v = p[(int64_t)c * BLK];
     L += v.y * fast_exp2((v.x - M) * sl2);
   }
@@ -192,16 +210,20 @@ __global__ __launch_bounds__(BLK * CMB_GROUPS) void proxy_combine_kernel(const f
 // rescales the stored sums by exp(m - M) / L of the row.
 __global__ __launch_bounds__(256) void proxy_tilesum_kernel(const float4* __restrict__ tstat,
                                                             const float2* __restrict__ rowstat,
-                                                            float4* __restrict__ tiles, int nb, float sl2) {
-  const int h = blockIdx.y, lane = threadIdx.x & 63;
+                                                            float4* __restrict__ tiles, const SeqList seqs, int hq,
+                                                            int hkv, int dense_below_n, float sl2) {
+  const int vh = blockIdx.y, lane = threadIdx.x & 63, h = vh % hq;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= nb) return;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (t >= nb || seq_dense(nb, dense_below_n)) return;
+  const int64_t rowb = sp.rows + (int64_t)h * nb;
   float lo = 0.f, up = 0.f, an = 0.f;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int r = lane + 64 * k;
-    const float4 v = tstat[((int64_t)h * nb + t) * BLK + r];
-    const float2 rs = rowstat[h * BLK + r];
+    const float4 v = tstat[(rowb + t) * BLK + r];
+    const float2 rs = rowstat[(int64_t)vh * BLK + r];
     const float wgt = fast_exp2((v.x - rs.x) * sl2) * rs.y;
     lo += v.y * wgt;
     up += v.z * wgt;
@@ -210,26 +232,33 @@ __global__ __launch_bounds__(256) void proxy_tilesum_kernel(const float4* __rest
   lo = wave_sum(lo);
   up = wave_sum(up);
   an = wave_sum(an);
-  if (lane == 0) tiles[(int64_t)h * nb + t] = make_float4(lo, up, an, 0.f);
+  if (lane == 0) tiles[rowb + t] = make_float4(lo, up, an, 0.f);
 }
 
-hipError_t launch_proxy(int fp32, const void* Q, const void* K, int64_t n, int nb, int hq, int hkv,
-                        const Strides& st, int w_sink, int w_local, void* tstat, void* stats, void* rowstat,
-                        void* tiles, float* kbar, hipStream_t s) {
+hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& seqs, int nb_max, int hq, int hkv,
+                        const Strides& st, int w_sink, int w_local, int dense_below_n, void* tstat, void* stats,
+                        void* rowstat, void* tiles, float* kbar, hipStream_t s) {
   const float sl2 = LOG2E / sqrtf((float)HD);
-  const dim3 grid((unsigned)(((nb + PCH - 1) / PCH) * hq));
+  const int nseq = seqs.nseq;
+  const dim3 grid((unsigned)(((nb_max + PCH - 1) / PCH) * hq), (unsigned)nseq);
   if (fp32) {
-    proxy_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, n, nb,
-                                                   hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local, sl2);
+    proxy_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
+                                                   hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
+                                                   dense_below_n, sl2);
   } else {
-    proxy_tiles_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar, n, nb, hq,
-                                                  hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local, sl2);
+    proxy_tiles_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar, seqs, hq,
+                                                  hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
+                                                  dense_below_n, sl2);
   }
-  const int nchunk = proxy_chunks(nb);
-  proxy_rowstat_kernel<<<dim3(nchunk, hq), BLK, 0, s>>>((const float4*)tstat, (float2*)stats, nb, nchunk, sl2);
-  proxy_combine_kernel<<<hq, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, nchunk, sl2);
-  proxy_tilesum_kernel<<<dim3((nb + 3) / 4, hq), 256, 0, s>>>((const float4*)tstat, (const float2*)rowstat,
-                                                              (float4*)tiles, nb, sl2);
+  const int nchunk = proxy_chunks(nb_max);
+  const unsigned vheads = (unsigned)(nseq * hq);
+  proxy_rowstat_kernel<<<dim3(nchunk, vheads), BLK, 0, s>>>((const float4*)tstat, (float2*)stats, seqs, hq, hkv,
+                                                             nchunk, dense_below_n, sl2);
+  proxy_combine_kernel<<<vheads, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, seqs, hq, nchunk,
+                                                           dense_below_n, sl2);
+  proxy_tilesum_kernel<<<dim3((nb_max + 3) / 4, vheads), 256, 0, s>>>((const float4*)tstat, (const float2*)rowstat,
+                                                                      (float4*)tiles, seqs, hq, hkv, dense_below_n,
+                                                                      sl2);
   return hipGetLastError();
 }
 

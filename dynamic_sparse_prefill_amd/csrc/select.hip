@@ -118,23 +118,28 @@ __device__ void top_up(uint8_t* flag, const float* p, int nb, int want, float* s
   }
 }
 
+// One work-group per virtual head (sequence, query head).
 __global__ __launch_bounds__(256) void vs_select_kernel(
-    const float4* __restrict__ tiles, int64_t n, int nb, int w_sink, int w_local, float tau, float alpha,
-    int min_blocks, int dense, const double* __restrict__ jsd, int vs_budget, int32_t* __restrict__ route,
-    float* __restrict__ c_struct, float* __restrict__ pv, float* __restrict__ ps, int32_t* __restrict__ sv,
-    int32_t* __restrict__ nv, int32_t* __restrict__ ss, int32_t* __restrict__ ns, float* pv_out, float* ps_out) {
+    const float4* __restrict__ tiles, const SeqList seqs, int hq, int hkv, int w_sink, int w_local, float tau,
+    float alpha, int min_blocks, int dense_below_n, const double* __restrict__ jsd, int vs_budget,
+    int32_t* __restrict__ route, float* __restrict__ c_struct, float* __restrict__ pv, float* __restrict__ ps,
+    int32_t* __restrict__ sv, int32_t* __restrict__ nv, int32_t* __restrict__ ss, int32_t* __restrict__ ns,
+    float* pv_out, float* ps_out) {
   extern __shared__ uint8_t flag[];  // nb bytes
   __shared__ int shi[256];
   __shared__ float shv[256];
   __shared__ int s_route;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  if (dense) {
+  const int h = blockIdx.x, tid = threadIdx.x;   // h: virtual head
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  const int64_t n = (int64_t)nb * BLK, rowb = sp.rows + (int64_t)(h % hq) * nb;
+  if (seq_dense(nb, dense_below_n)) {
     if (tid == 0) { route[h] = -1; c_struct[h] = 0.f; nv[h] = 0; ns[h] = 0; }
     return;
   }
-  const float4* T = tiles + (int64_t)h * nb;
-  float* PV = pv + (int64_t)h * nb;
-  float* PS = ps + (int64_t)h * nb;
+  const float4* T = tiles + rowb;
+  float* PV = pv + rowb;
+  float* PS = ps + rowb;
   const float inv_b = 1.f / BLK;  // exact power of two
   for (int k = tid; k < nb; k += 256) {
     const float4 t = T[k];
@@ -144,8 +149,8 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     const float sl = __fmul_rn(__fadd_rn(lo, up), inv_b);
     PV[k] = v;
     PS[k] = sl;
-    if (pv_out) pv_out[(int64_t)h * nb + k] = v;
-    if (ps_out) ps_out[(int64_t)h * nb + k] = sl;
+    if (pv_out) pv_out[rowb + k] = v;
+    if (ps_out) ps_out[rowb + k] = sl;
   }
   if (tid == 0) {
     // tiles touching [0, w_sink) or [n - w_local, n), ascending: the sink tiles,
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     for (int k = tid; k < nb; k += 256) flag[k] = (p[k] > thr) || k == 0 || k == nb - 1;
     __syncthreads();
     if (min_blocks > 0) top_up(flag, p, nb, min(min_blocks, nb), shv, shi);
-    compact_flags(flag, nb, (dir == 0 ? sv : ss) + (int64_t)h * nb, (dir == 0 ? nv : ns) + h, shi);
+    compact_flags(flag, nb, (dir == 0 ? sv : ss) + rowb, (dir == 0 ? nv : ns) + h, shi);
   }
 }
 
@@ -222,14 +227,26 @@ __device__ V block256_sum(V v, V* sh) {
 template <typename T>
 __global__ __launch_bounds__(256) void jsd_route_kernel(const T* __restrict__ Q, const float4* __restrict__ tiles,
                                                         const float* __restrict__ kbar, float* __restrict__ abar,
-                                                        double* __restrict__ jsd, int nb, int hq, int hkv,
-                                                        int64_t sq_h, int64_t sq_n, float scale) {
+                                                        double* __restrict__ jsd, const SeqList seqs, int hq,
+                                                        int hkv, int64_t sq_h, int64_t sq_n, int dense_below_n,
+                                                        float scale) {
   __shared__ float qm[HD];
   __shared__ float red[2][HD];
   __shared__ float shf[256];
   __shared__ double shd[256];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int vh = blockIdx.x, tid = threadIdx.x;
+  const int h = vh % hq;
   const int kvh = h / (hq / hkv);
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (seq_dense(nb, dense_below_n)) {
+    if (tid == 0) jsd[vh] = 0.0;
+    return;
+  }
+  Q += sp.tok * sq_n;
+  tiles += sp.rows;
+  kbar += sp.kvrows * HD;
+  abar += sp.rows;
   {
     const int d = tid & (HD - 1), half = tid >> 7;
     const T* base = Q + (int64_t)h * sq_h + ((int64_t)(nb - 1) * BLK + 64 * half) * sq_n + d;
@@ -271,7 +288,7 @@ __global__ __launch_bounds__(256) void jsd_route_kernel(const T* __restrict__ Q,
     if (b > 0.f) acc += (double)b * log((double)b / m);
   }
   acc = block256_sum(acc, shd);
-  if (tid == 0) jsd[h] = 0.5 * acc;
+  if (tid == 0) jsd[vh] = 0.5 * acc;
 }
 
 // ------------------------------------------------------------------ variant: median floor / coverage budget
@@ -375,10 +392,10 @@ __device__ uint32_t radix_pick(const float* __restrict__ p, int lo, int hi, unsi
 // Then the anchors 0 and N_b - 1, the optional min budget, ascending compaction.
 template <bool MEDIAN>
 __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict__ route, const float* __restrict__ pv,
-                                                       const float* __restrict__ ps, int nb, float alpha, float gamma,
-                                                       int min_blocks, int32_t* __restrict__ sv,
-                                                       int32_t* __restrict__ nv, int32_t* __restrict__ ss,
-                                                       int32_t* __restrict__ ns) {
+                                                       const float* __restrict__ ps, const SeqList seqs, int hq,
+                                                       int hkv, float alpha, float gamma, int min_blocks,
+                                                       int32_t* __restrict__ sv, int32_t* __restrict__ nv,
+                                                       int32_t* __restrict__ ss, int32_t* __restrict__ ns) {
   extern __shared__ uint8_t flag[];  // nb bytes
   // radix histograms; outside the radix passes the same memory serves the
   // block reductions (shi: 1024 ints over cnt, shv: 1024 floats over mass)
@@ -386,9 +403,12 @@ __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict
   __shared__ unsigned long long mass[PE_BUCKETS];
   int* shi = (int*)cnt;
   float* shv = (float*)mass;
-  const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;   // h: virtual head
   if (route[h] != 1) return;
-  const float* p = (dir == 0 ? pv : ps) + (int64_t)h * nb;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  const int64_t rowb = sp.rows + (int64_t)(h % hq) * nb;
+  const float* p = (dir == 0 ? pv : ps) + rowb;
   if (MEDIAN) {
     const int m = nb - 2;
     float med;
@@ -469,7 +489,7 @@ __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict
   for (int k = a; k < b; ++k) c += flag[k];
   int tot;
   int pos = block1k_excl_scan(c, shi, &tot);
-  int32_t* out = (dir == 0 ? sv : ss) + (int64_t)h * nb;
+  int32_t* out = (dir == 0 ? sv : ss) + rowb;
   for (int k = a; k < b; ++k)
     if (flag[k]) out[pos++] = k;
   if (tid == 0) (dir == 0 ? nv : ns)[h] = tot;
@@ -479,15 +499,20 @@ __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict
 
 template <typename T>
 __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, const int32_t* __restrict__ route,
-                                                     float* __restrict__ qbar, int nb, int64_t sq_h, int64_t sq_n) {
+                                                     float* __restrict__ qbar, const SeqList seqs, int hq, int hkv,
+                                                     int64_t sq_h, int64_t sq_n) {
   constexpr int E = 16 / sizeof(T);         // elements per 16-byte load
   constexpr int CPR = HD / E;               // 16-byte chunks per row
   constexpr int RG = 256 / CPR;             // row groups
   __shared__ float red[RG][HD];
-  const int qb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  if (route[h] != 0) return;
+  const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
+  if (route[vh] != 0) return;
+  const int h = vh % hq;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (qb >= nb) return;
   const int ch = tid % CPR, rg = tid / CPR;
-  const T* base = Q + (int64_t)h * sq_h + (int64_t)qb * BLK * sq_n + ch * E;
+  const T* base = Q + (int64_t)h * sq_h + (sp.tok + (int64_t)qb * BLK) * sq_n + ch * E;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -504,7 +529,7 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, co
   if (tid < HD) {
     float s = 0.f;
     for (int q = 0; q < RG; ++q) s += red[q][tid];
-    qbar[((int64_t)h * nb + qb) * HD + tid] = s * (1.f / BLK);
+    qbar[(sp.rows + (int64_t)h * nb + qb) * HD + tid] = s * (1.f / BLK);
   }
 }
 
@@ -523,13 +548,22 @@ constexpr int PE_SEG = 32;  // 32-key-block tiles per logits work-group (1024 ke
 // The segment's row max and sum of exp(L - max) go to `part` for the softmax.
 __global__ __launch_bounds__(64) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                        const int32_t* __restrict__ route, float* __restrict__ P,
-                                                       float2* __restrict__ part, int nb, int hq, int hkv,
-                                                       int nseg, float scale) {
+                                                       float2* __restrict__ part, const SeqList seqs, int hq,
+                                                       int hkv, int nseg, float scale) {
   __shared__ float tileT[32][33];
+  const int vh = blockIdx.z;
+  if (route[vh] != 0) return;
+  const int h = vh % hq;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
   const int nrb = (nb + 31) / 32;
-  const int rb = nrb - 1 - (int)blockIdx.x, cs = blockIdx.y, h = blockIdx.z;
+  const int rb = nrb - 1 - (int)blockIdx.x, cs = blockIdx.y;
   const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-  if (route[h] != 0) return;
+  if (rb < 0) return;
+  qbar += sp.rows * HD;
+  kbar += sp.kvrows * HD;
+  P += sp.tri;
+  part += sp.rows * nseg;
   const int last_row = min(nb - 1, rb * 32 + 31);
   const int ntile = last_row / 32 + 1;
   const int ct0 = cs * PE_SEG, ct1 = min(ntile, ct0 + PE_SEG);
@@ -601,11 +635,17 @@ __global__ __launch_bounds__(64) void pe_logits_kernel(const float* __restrict__
 // Row softmax in place: one work-group per (query block, Pooled-Estimation
 // head) merges the row's segment maxima and sums, then P = exp(L - M) / S.
 __global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict__ route, const float2* __restrict__ part,
-                                                      float* __restrict__ P, int nb, int nseg) {
-  const int qb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  if (route[h] != 0) return;
+                                                      float* __restrict__ P, const SeqList seqs, int hq, int hkv,
+                                                      int nseg) {
+  const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
+  if (route[vh] != 0) return;
+  const int h = vh % hq;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (qb >= nb) return;
+  P += sp.tri;
   const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;   // segments this row block produced
-  const float2* pp = part + ((int64_t)h * nb + qb) * nseg;
+  const float2* pp = part + (sp.rows + (int64_t)h * nb + qb) * nseg;
   float M = -INFINITY;
   for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
   float S = 0.f;
@@ -651,18 +691,23 @@ __host__ __device__ constexpr int pe_width(int pass) { return pass == 2 ? 10 : 1
 template <int PASS>
 __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
                                                       uint32_t* __restrict__ hcnt,
-                                                      unsigned long long* __restrict__ hmass, int64_t total) {
+                                                      unsigned long long* __restrict__ hmass, const SeqList seqs,
+                                                      int hq, int hkv) {
   __shared__ uint32_t sc[PE_BUCKETS];
   __shared__ unsigned long long sm[PE_BUCKETS];
-  const int h = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x;   // h: virtual head
   if (!cut[h].active) return;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int64_t total = tri(sp.nb);
+  if ((int64_t)blockIdx.x * PE_SLICE >= total) return;
+  P += sp.tri + (int64_t)(h % hq) * total;
   constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
   constexpr uint32_t mask = (1u << width) - 1;
   constexpr int hi = shift + width;
   const uint32_t prefix = cut[h].prefix;
   for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
   __syncthreads();
-  const uint32_t* bits = (const uint32_t*)(P + (int64_t)h * total);
+  const uint32_t* bits = (const uint32_t*)P;
   const int64_t a = (int64_t)blockIdx.x * PE_SLICE, b = min(total, a + PE_SLICE);
   // neighbouring entries of a softmax row mostly fall into the same bucket:
   // each thread merges runs of equal buckets in registers (over its strided
@@ -747,25 +792,31 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
 // count of entries equal to the cut value per row, then an exclusive scan per head (only when the cut
 // splits a run of equal values)
 __global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
-                                                          int32_t* __restrict__ eqrow, int nb) {
-  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                                          int32_t* __restrict__ eqrow, const SeqList seqs, int hq,
+                                                          int hkv) {
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
   const int qb = blockIdx.x * 4 + w;
   const PeCut c = cut[h];
-  if (!c.active || c.take >= c.eq_cnt || qb >= nb) return;
-  const uint32_t* row = (const uint32_t*)(P + (int64_t)h * tri(nb) + tri(qb));
+  if (!c.active || c.take >= c.eq_cnt) return;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  if (qb >= nb) return;
+  const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
   int cnt = 0;
   for (int k = lane; k <= qb; k += 64) cnt += (row[k] == c.vstar);
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-  if (lane == 0) eqrow[(int64_t)h * nb + qb] = cnt;
+  if (lane == 0) eqrow[sp.rows + (int64_t)(h % hq) * nb + qb] = cnt;
 }
 
 __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict__ cut, int32_t* __restrict__ eqrow,
-                                                         int nb) {
+                                                         const SeqList seqs, int hq, int hkv) {
   __shared__ int sh[256];
-  const int h = blockIdx.x;
+  const int h = blockIdx.x;   // virtual head
   const PeCut c = cut[h];
   if (!c.active || c.take >= c.eq_cnt) return;
-  int32_t* e = eqrow + (int64_t)h * nb;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  int32_t* e = eqrow + sp.rows + (int64_t)(h % hq) * nb;
   const int per = (nb + 255) / 256;
   const int a = min(nb, (int)threadIdx.x * per), b = min(nb, a + per);
   int s = 0;
@@ -790,14 +841,18 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
                                                    const float* __restrict__ P, const PeCut* __restrict__ cut,
                                                    const int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
-                                                   int nb, int pe_all) {
-  extern __shared__ uint32_t bitmap[];  // 4 waves x ceil(nb/32) words
-  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                                   const SeqList seqs, int hq, int hkv, int nb_max, int pe_all) {
+  extern __shared__ uint32_t bitmap[];  // 4 waves x ceil(nb_max/32) words
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
   const int qb = blockIdx.x * 4 + w;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
   if (qb >= nb) return;
-  const int64_t row = (int64_t)h * nb + qb;
+  const int hl = h % hq;                                     // query head within the sequence
+  const int64_t row = sp.rows + (int64_t)hl * nb + qb;       // packed per-row arrays
   const int r = route[h];
-  int32_t* out = FILL ? col + row_ptr[row] : nullptr;
+  // the sequence's own CSR: row pointers at rp, relative to its column segment at tri
+  int32_t* out = FILL ? col + sp.tri + row_ptr[sp.rp + (int64_t)hl * nb + qb] : nullptr;
   if (r == -1 || (r == 0 && pe_all)) {
     if (!FILL) { if (lane == 0) counts[row] = qb + 1; }
     else for (int k = lane; k <= qb; k += 64) out[k] = k;
@@ -805,7 +860,7 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   }
   if (r == 0) {
     const PeCut c = cut[h];
-    const uint32_t* bits = (const uint32_t*)(P + (int64_t)h * tri(nb) + tri(qb));
+    const uint32_t* bits = (const uint32_t*)(P + sp.tri + (int64_t)hl * tri(nb) + tri(qb));
     const bool split = c.take < c.eq_cnt;
     int base = 0;
     long long eqb = split ? eqrow[row] : 0;
@@ -834,8 +889,8 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   for (int i = lane; i < words; i += 64) bm[i] = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  const int32_t* svh = sv + (int64_t)h * nb;
-  const int32_t* ssh = ss + (int64_t)h * nb;
+  const int32_t* svh = sv + sp.rows + (int64_t)hl * nb;
+  const int32_t* ssh = ss + sp.rows + (int64_t)hl * nb;
   const int cv = nv[h], cs = ns[h];
   for (int i = lane; i < cv; i += 64) {
     const int k = svh[i];
@@ -875,14 +930,20 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   if (!FILL && lane == 0) counts[row] = base;
 }
 
-// exclusive scan of the row counts into row_ptr (single work-group of 1024
-// threads): the counts go through in tiles of 4096, four consecutive per
-// thread, with a carry between tiles (the total fits int32, checked on the host)
+// exclusive scan of one sequence's row counts into its row pointers (one
+// work-group of 1024 threads per sequence): the counts go through in tiles of
+// 4096, four consecutive per thread, with a carry between tiles (a sequence's
+// total fits int32, checked on the host)
 __global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ row_ptr, int64_t rows) {
+                                                         int32_t* __restrict__ row_ptr, const SeqList seqs, int hq,
+                                                         int hkv) {
   __shared__ int wsum[16];
   __shared__ int s_carry;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const SeqPos sp = seq_pos(seqs, blockIdx.x, hq, hkv);
+  const int64_t rows = (int64_t)hq * sp.nb;
+  counts += sp.rows;
+  row_ptr += sp.rp;
   if (tid == 0) s_carry = 0;
   __syncthreads();
   for (int64_t base = 0; base < rows; base += 4096) {
@@ -914,76 +975,78 @@ __global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restri
 }
 
 __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
-                                 const int32_t* __restrict__ ss, const int32_t* __restrict__ ns,
-                                 int32_t* sv_out, int32_t* nv_out, int32_t* ss_out, int32_t* ns_out, int nb) {
-  const int h = blockIdx.x;
+                                 const int32_t* __restrict__ ss, const int32_t* __restrict__ ns, int32_t* sv_out,
+                                 int32_t* nv_out, int32_t* ss_out, int32_t* ns_out, const SeqList seqs, int hq,
+                                 int hkv) {
+  const int h = blockIdx.x;   // virtual head
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int64_t rowb = sp.rows + (int64_t)(h % hq) * sp.nb;
   const int a = nv[h], b = ns[h];
   if (threadIdx.x == 0) { if (nv_out) nv_out[h] = a; if (ns_out) ns_out[h] = b; }
-  for (int i = threadIdx.x; i < a; i += blockDim.x) if (sv_out) sv_out[(int64_t)h * nb + i] = sv[(int64_t)h * nb + i];
-  for (int i = threadIdx.x; i < b; i += blockDim.x) if (ss_out) ss_out[(int64_t)h * nb + i] = ss[(int64_t)h * nb + i];
+  for (int i = threadIdx.x; i < a; i += blockDim.x) if (sv_out) sv_out[rowb + i] = sv[rowb + i];
+  for (int i = threadIdx.x; i < b; i += blockDim.x) if (ss_out) ss_out[rowb + i] = ss[rowb + i];
 }
 
 // ------------------------------------------------------------------ launcher
 
-hipError_t launch_select(int fp32, bool dense, const void* Q, int64_t n, int nb, int hq, int hkv,
+hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_max, int hq, int hkv,
                          const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
-                         int min_blocks, const SelectBufs& b, hipStream_t s) {
-  const bool jsd_on = b.router == 1 && !dense;
+                         int min_blocks, int dense_below_n, const SelectBufs& b, hipStream_t s) {
+  const unsigned vh = (unsigned)(seqs.nseq * hq);   // virtual heads: (sequence, query head)
+  const bool jsd_on = b.router == 1;
   if (jsd_on) {
     const float scale = 1.f / sqrtf((float)HD);
     if (fp32)
-      jsd_route_kernel<float><<<hq, 256, 0, s>>>((const float*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd,
-                                                 nb, hq, hkv, st.q_h, st.q_n, scale);
+      jsd_route_kernel<float><<<vh, 256, 0, s>>>((const float*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd,
+                                                 seqs, hq, hkv, st.q_h, st.q_n, dense_below_n, scale);
     else
-      jsd_route_kernel<bf16><<<hq, 256, 0, s>>>((const bf16*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd, nb,
-                                                hq, hkv, st.q_h, st.q_n, scale);
+      jsd_route_kernel<bf16><<<vh, 256, 0, s>>>((const bf16*)Q, (const float4*)b.tiles, b.kbar, b.abar, b.jsd, seqs,
+                                                hq, hkv, st.q_h, st.q_n, dense_below_n, scale);
   }
-  vs_select_kernel<<<hq, 256, nb, s>>>((const float4*)b.tiles, n, nb, w_sink, w_local, tau, alpha, min_blocks,
-                                       dense ? 1 : 0, jsd_on ? b.jsd : nullptr, b.vs_budget, b.route, b.c_struct,
-                                       b.pv, b.ps, b.sv, b.nv, b.ss, b.ns, b.pv_out, b.ps_out);
-  if (!dense && b.vs_budget != 0) {
+  vs_select_kernel<<<vh, 256, nb_max, s>>>((const float4*)b.tiles, seqs, hq, hkv, w_sink, w_local, tau, alpha,
+                                           min_blocks, dense_below_n, jsd_on ? b.jsd : nullptr, b.vs_budget,
+                                           b.route, b.c_struct, b.pv, b.ps, b.sv, b.nv, b.ss, b.ns, b.pv_out,
+                                           b.ps_out);
+  if (b.vs_budget != 0) {
     if (b.vs_budget == 1)
-      vs_rank_kernel<true><<<dim3(hq, 2), 1024, nb, s>>>(b.route, b.pv, b.ps, nb, alpha, gamma, min_blocks, b.sv,
-                                                         b.nv, b.ss, b.ns);
+      vs_rank_kernel<true><<<dim3(vh, 2), 1024, nb_max, s>>>(b.route, b.pv, b.ps, seqs, hq, hkv, alpha, gamma,
+                                                             min_blocks, b.sv, b.nv, b.ss, b.ns);
     else
-      vs_rank_kernel<false><<<dim3(hq, 2), 1024, nb, s>>>(b.route, b.pv, b.ps, nb, alpha, gamma, min_blocks, b.sv,
-                                                          b.nv, b.ss, b.ns);
+      vs_rank_kernel<false><<<dim3(vh, 2), 1024, nb_max, s>>>(b.route, b.pv, b.ps, seqs, hq, hkv, alpha, gamma,
+                                                              min_blocks, b.sv, b.nv, b.ss, b.ns);
   }
   PeCut* cut = (PeCut*)b.cut;
-  const int64_t total = (int64_t)nb * (nb + 1) / 2;
+  const int64_t total_max = (int64_t)nb_max * (nb_max + 1) / 2;
   const int pe_all = gamma >= 1.f ? 1 : 0;
-  if (!dense) {
-    const dim3 gq(nb, hq);
-    if (fp32)
-      pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
-    else
-      pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, nb, st.q_h, st.q_n);
-    const int nrb = (nb + 31) / 32, nseg = (nrb + PE_SEG - 1) / PE_SEG;
-    pe_logits_kernel<<<dim3(nrb, nseg, hq), 64, 0, s>>>(b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, nb, hq,
-                                                        hkv, nseg, 1.f / sqrtf((float)HD));
-    pe_norm_kernel<<<dim3(nb, hq), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, nb, nseg);
-    pe_cut_init_kernel<<<hq, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
-    const dim3 gh((unsigned)((total + PE_SLICE - 1) / PE_SLICE), hq);
-    pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
-    pe_scan_kernel<0><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-    pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
-    pe_scan_kernel<1><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-    pe_hist_kernel<2><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, total);
-    pe_scan_kernel<2><<<hq, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-    pe_eq_count_kernel<<<dim3((nb + 3) / 4, hq), 256, 0, s>>>(b.P, cut, b.eqrow, nb);
-    pe_eq_scan_kernel<<<hq, 256, 0, s>>>(cut, b.eqrow, nb);
-  } else {
-    pe_cut_init_kernel<<<hq, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
-  }
-  const dim3 gl((nb + 3) / 4, hq);
-  const size_t bm_bytes = 4 * ((nb + 31) / 32) * sizeof(uint32_t);
+  const dim3 gq(nb_max, vh);
+  if (fp32)
+    pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
+  else
+    pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
+  const int nrb = (nb_max + 31) / 32, nseg = (nrb + PE_SEG - 1) / PE_SEG;
+  pe_logits_kernel<<<dim3(nrb, nseg, vh), 64, 0, s>>>(b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv,
+                                                      nseg, 1.f / sqrtf((float)HD));
+  pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
+  pe_cut_init_kernel<<<vh, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
+  const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
+  pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+  pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+  pe_hist_kernel<2><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+  pe_eq_count_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.eqrow, seqs, hq, hkv);
+  pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
+  const dim3 gl((nb_max + 3) / 4, vh);
+  const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);
   list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
-                                               b.row_ptr, b.col_idx, nb, pe_all);
-  scan_rows_kernel<<<1, 1024, 0, s>>>(b.counts, b.row_ptr, (int64_t)hq * nb);
+                                               b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
+  scan_rows_kernel<<<seqs.nseq, 1024, 0, s>>>(b.counts, b.row_ptr, seqs, hq, hkv);
   list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
-                                              b.row_ptr, b.col_idx, nb, pe_all);
+                                              b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
   if (b.sv_out || b.nv_out || b.ss_out || b.ns_out)
-    copy_sets_kernel<<<hq, 256, 0, s>>>(b.sv, b.nv, b.ss, b.ns, b.sv_out, b.nv_out, b.ss_out, b.ns_out, nb);
+    copy_sets_kernel<<<vh, 256, 0, s>>>(b.sv, b.nv, b.ss, b.ns, b.sv_out, b.nv_out, b.ss_out, b.ns_out, seqs, hq,
+                                        hkv);
   return hipGetLastError();
 }
 
