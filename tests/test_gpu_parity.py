@@ -415,3 +415,35 @@ def test_varlen_batch_equals_single_calls(flags):
     mx, mean = P.check_attention_blocks(parts[0][0], parts[0][1], parts[0][2], parts[0][3], o[:, :n0], lists,
                                         range(hq), synth.sample_blocks(nb0, 6, 7))
     P.log(f"[varlen] attention max {mx:.2e} mean {mean:.2e}")
+
+
+def test_varlen_fp32_and_gqa7():
+    """Packed batch on the fp32 path (per-sequence attention launches) and with
+    GQA 7:1: outputs and lists bitwise equal to single calls."""
+    for dtype, hq, hkv, lens in (("fp32", 2, 2, [1024, 384, 2048]), ("bf16", 7, 1, [1664, 4096, 128])):
+        cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+        parts = []
+        for i, n in enumerate(lens):
+            cfg = synth.custom_config(f"vl-{dtype}-{i}", n, hq, hkv, dtype=dtype, seed=80 + i, conc_frac=0.5)
+            spec = synth.make_spec(cfg)
+            parts.append((spec,) + synth.generate(spec))
+        spec0 = parts[0][0]
+        q = P.to_device(spec0, np.concatenate([p[1] for p in parts], axis=1))
+        k = P.to_device(spec0, np.concatenate([p[2] for p in parts], axis=1))
+        v = P.to_device(spec0, np.concatenate([p[3] for p in parts], axis=1))
+        params = P.params_of(spec0.cfg)
+        o, sel = dsp.crisp_prefill_varlen(q, k, v, cu, params)
+        torch.cuda.synchronize()
+        rp0, col0 = 0, 0
+        for i, n in enumerate(lens):
+            a, b = cu[i], cu[i + 1]
+            nb = n // 128
+            oi, si = dsp.crisp_prefill(q[:, a:b].contiguous(), k[:, a:b].contiguous(), v[:, a:b].contiguous(), params)
+            torch.cuda.synchronize()
+            assert torch.equal(o[:, a:b], oi), f"{dtype} sequence {i}: output differs"
+            assert torch.equal(sel.route[i * hq:(i + 1) * hq], si.route)
+            assert torch.equal(sel.row_ptr[rp0:rp0 + hq * nb + 1], si.row_ptr)
+            m = int(si.row_ptr[-1])
+            assert torch.equal(sel.col_idx[col0:col0 + m], si.col_idx[:m])
+            rp0 += hq * nb + 1
+            col0 += hq * nb * (nb + 1) // 2
