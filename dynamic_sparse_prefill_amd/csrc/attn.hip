@@ -22,9 +22,10 @@
 //    16-byte reads, double-buffered so the next block streams in during a
 //    whole iteration; one barrier per key block.
 //  * Scheduling: a persistent grid (one work-group per CU) pulls (pair, head)
-//    items from 8 per-XCD queues, longest rows first, the heads of one KV
-//    group on one XCD, stealing from other queues at the end: every CU stays
-//    busy whatever the list lengths and K/V is shared through L2.
+//    items from 8 per-XCD queues, two KV groups at a time, longest rows
+//    first, stealing from other queues at the end: every CU stays busy
+//    whatever the list lengths, and K/V is shared through L2 and the
+//    last-level cache.
 #include <algorithm>
 
 #include "common.h"
@@ -157,18 +158,20 @@ constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
 
 // Work queues.  The kernel is persistent (one work-group per CU).  A unit of
-// work is one (query-block pair, KV head) with its G query heads.  Units are
-// numbered u = pair' * hkv + kvh with pair' counted from the longest rows, and
-// unit u belongs to queue u % 8: with 8 KV heads each queue holds one KV
-// group, so the items running together on an XCD stream the same K/V through
-// its L2.  Work-group b starts on queue b % 8 (dispatch places it on XCD
-// b % 8), takes items from it longest first, then steals from the other
-// queues until all are empty, which evens out groups of unequal work.  Only
-// locality depends on the placement; every item is taken exactly once.
+// work is one (query-block pair, KV head) with its G query heads, whose items
+// are consecutive in a queue so they run side by side and share each K/V tile
+// through L2.  Units are numbered two KV groups at a time (see queue_item),
+// longest rows first, and unit u belongs to queue u % 8: every XCD works on
+// the same two groups at once, keeping the K/V working set small.  Work-group
+// b starts on queue b % 8 (dispatch places it on XCD b % 8), takes items from
+// it, then steals from the other queues until all are empty.  Only locality
+// depends on the placement; every item is taken exactly once.
 
 // t-th item of queue x -> (sequence, pair, kvh, h); false once the queue is
-// exhausted.  Units are numbered sequence after sequence (each longest rows
-// first); with hkv dividing 8 a queue keeps one KV group in every sequence.
+// exhausted.  Units are numbered sequence after sequence; within a sequence,
+// KV groups go two at a time (2j, 2j+1 alternating unit by unit, longest rows
+// first; a last odd group alone), so all queues stream the K/V of the same
+// two groups at any moment: a working set that stays in the last-level cache.
 __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int hkv, int& seq, int& pair, int& kvh,
                                   int& h) {
   const int G = hq / hkv;
@@ -177,9 +180,16 @@ __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int 
   int i = 0;
   while (u >= sq.unit_off[i + 1]) ++i;
   const int v = u - sq.unit_off[i];
+  const int np = (sq.nb[i] + 1) >> 1;
+  const int gp = v / (2 * np), r = v % (2 * np);
   seq = i;
-  pair = ((sq.nb[i] + 1) >> 1) - 1 - v / hkv;
-  kvh = v % hkv;
+  if (2 * gp + 1 < hkv) {
+    kvh = 2 * gp + (r & 1);
+    pair = np - 1 - (r >> 1);
+  } else {                                                  // odd group count: the last group alone
+    kvh = 2 * gp;
+    pair = np - 1 - r;
+  }
   h = kvh * G + t % G;
   return true;
 }
