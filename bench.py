@@ -311,7 +311,7 @@ def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True, compare
     return out, spec, route
 
 
-def cpu_baseline(spec, route, tiles_total, budget_s=25.0):
+def cpu_baseline(spec, route, tiles_total, budget_s=20.0):
     """The oracle as it stands, on a bounded sample of the layer, scaled to ms per layer."""
     from oracle import crisp_oracle as O
     from workloads import synth
@@ -343,7 +343,8 @@ def cpu_baseline(spec, route, tiles_total, budget_s=25.0):
     v = synth.as_f64(spec, synth.rows(spec, "v", h // G, 0, cfg.n))
     done_tiles, t_att = 0, 0.0
     blocks = []
-    for qb in [cfg.nb - 1, cfg.nb // 2, cfg.nb // 4, 3 * cfg.nb // 4, cfg.nb // 8]:
+    # seeded query blocks (the last one first) until about budget_s of host time is spent
+    for qb in [cfg.nb - 1] + [b for b in synth.sample_blocks(cfg.nb, 64, 17) if b != cfg.nb - 1]:
         if time.time() - t_start > budget_s:
             break
         t = time.time()
