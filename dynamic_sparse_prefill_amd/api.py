@@ -19,6 +19,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcrisp.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libcrisp_probe.so")   # attainable-peak probe (include/crisp_probe.h)
 
 BLOCK = 128
 BF16, FP32 = 0, 1
@@ -57,6 +58,22 @@ class CrispError(RuntimeError):
 
 
 _LIB = None
+
+
+_PROBE = None
+
+
+def probe_lib() -> C.CDLL:
+    """Load libcrisp_probe.so, the MFMA peak probe the benchmark times (raises if not built)."""
+    global _PROBE
+    if _PROBE is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build it with dynamic_sparse_prefill_amd.build.build()")
+        L = C.CDLL(PROBE_LIB_PATH)
+        L.crisp_probe_mfma_bf16.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+        L.crisp_probe_mfma_bf16.restype = C.c_int
+        _PROBE = L
+    return _PROBE
 
 
 def lib() -> C.CDLL:

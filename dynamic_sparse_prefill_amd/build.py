@@ -18,6 +18,8 @@ LIB = os.path.join(HERE, "libcrisp.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["crisp.cpp", "attn.hip", "proxy.hip", "select.hip"]
+PROBE_LIB = os.path.join(HERE, "libcrisp_probe.so")   # attainable-peak probe used by the benchmark
+PROBE_SOURCES = ["probe.hip"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
@@ -35,7 +37,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
@@ -47,12 +49,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0), verbose)
     for p in procs:
         _wait(p, verbose)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *DEVICE_FLAGS, "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    main_objs = [o for o, s in zip(objs, SOURCES + PROBE_SOURCES) if s in SOURCES]
+    probe_objs = [o for o, s in zip(objs, SOURCES + PROBE_SOURCES) if s in PROBE_SOURCES]
+    for lib, lobjs in ((LIB, main_objs), (PROBE_LIB, probe_objs)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), *DEVICE_FLAGS, "-shared", "-fPIC", "-o", tmp, *lobjs]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -13,10 +13,10 @@ from dynamic_sparse_prefill_amd import api
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "crisp.h")).read()
+def declared_functions(header="crisp.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(crisp_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(crisp_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_and_exports_agree():
@@ -25,6 +25,18 @@ def test_header_and_exports_agree():
     L = dsp.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_probe_header_and_exports_agree():
+    names = declared_functions("crisp_probe.h")
+    assert names == ["crisp_probe_mfma_bf16"]
+    L = api.probe_lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # host-side validation: nothing is launched for invalid arguments
+    assert L.crisp_probe_mfma_bf16(None, 1, 1, None) == -1
+    assert L.crisp_probe_mfma_bf16(C.c_void_p(16), 0, 1, None) == -1
+    assert L.crisp_probe_mfma_bf16(C.c_void_p(16), 1, 0, None) == -1
 
 
 def _shape(n=4096, hq=4, hkv=2, d=128, dtype=0):
