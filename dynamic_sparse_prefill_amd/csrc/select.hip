@@ -539,35 +539,50 @@ __device__ __forceinline__ int64_t tri(int64_t qb) { return qb * (qb + 1) / 2; }
 
 constexpr int PE_SEG = 32;  // 32-key-block tiles per logits work-group (1024 key blocks)
 
-// Logits: one wave per (32 query blocks rb, segment cs of PE_SEG key tiles,
-// Pooled-Estimation head).  L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb
-// is formed 32 key blocks at a time with v_mfma_f32_32x32x2f32 in the
-// transposed form L^T = Kbar Qbar^T (lane l owns query block 32 rb + l%32 and
-// 16 of the 32 key blocks; the d index of MFMA step s, lane half g is 64 g + s),
-// turned row-major through LDS and stored with whole 128-byte row segments.
-// The segment's row max and sum of exp(L - max) go to `part` for the softmax.
-__global__ __launch_bounds__(64) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                       const int32_t* __restrict__ route, float* __restrict__ P,
-                                                       float2* __restrict__ part, const SeqList seqs, int hq,
-                                                       int hkv, int nseg, float scale) {
-  __shared__ float tileT[32][33];
+constexpr int PE_RB = 4;     // 32-query-block row blocks (one wave each) per logits work-group
+
+// e^x of the pooled softmax as v_exp_f32 (2^x) of x log2(e): relative error
+// about |x| 2^-24 beyond the instruction's own, far below the probabilities'
+// use (they are compared to 1e-5 and cut on their own float32 values).
+__device__ __forceinline__ float pe_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+constexpr int KT_PITCH = 132; // LDS pitch (floats) of a key-block-mean row: conflict-free 16-byte reads
+
+// Logits: one work-group per (PE_RB row blocks of 32 query blocks, segment cs
+// of PE_SEG key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
+// L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb is formed 32 key blocks
+// at a time with v_mfma_f32_32x32x2f32 in the transposed form L^T = Kbar Qbar^T
+// (lane l owns query block 32 rb + l%32 and 16 of the 32 key blocks; the d
+// index of MFMA step s, lane half g is 64 g + s).  The 32 key-block means of a
+// tile are staged once in LDS (double-buffered, the next tile's copy in flight
+// during the MFMAs) and shared by the work-group's waves.  Each tile is turned
+// row-major through LDS and stored with whole 128-byte row segments; the
+// segment's row max and sum of exp(L - max) go to `part` for the softmax.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                        const int32_t* __restrict__ route, float* __restrict__ P,
+                                                        float2* __restrict__ part, const SeqList seqs, int hq,
+                                                        int hkv, int nseg, float scale) {
+  __shared__ __attribute__((aligned(16))) float kt[2][32 * KT_PITCH];
+  __shared__ float tileT[PE_RB][32][33];
   const int vh = blockIdx.z;
   if (route[vh] != 0) return;
   const int h = vh % hq;
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
   const int nb = sp.nb;
-  const int nrb = (nb + 31) / 32;
-  const int rb = nrb - 1 - (int)blockIdx.x, cs = blockIdx.y;
-  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-  if (rb < 0) return;
+  const int nrb = (nb + 31) / 32, nrg = (nrb + PE_RB - 1) / PE_RB;
+  const int rg = nrg - 1 - (int)blockIdx.x, cs = blockIdx.y;
+  if (rg < 0) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int rb = rg * PE_RB + w;
+  // tiles this wave needs: key tiles 0 .. ntile - 1 of its row block (none past nb)
+  const int ntile = rb < nrb ? min(nb - 1, rb * 32 + 31) / 32 + 1 : 0;
+  const int rb_top = min(nrb - 1, rg * PE_RB + PE_RB - 1);
+  const int ntile_top = min(nb - 1, rb_top * 32 + 31) / 32 + 1;
+  const int ct0 = cs * PE_SEG, ct1 = min(ntile_top, ct0 + PE_SEG);
+  if (ct0 >= ct1) return;
   qbar += sp.rows * HD;
   kbar += sp.kvrows * HD;
   P += sp.tri;
   part += sp.rows * nseg;
-  const int last_row = min(nb - 1, rb * 32 + 31);
-  const int ntile = last_row / 32 + 1;
-  const int ct0 = cs * PE_SEG, ct1 = min(ntile, ct0 + PE_SEG);
-  if (ct0 >= ct1) return;
   const int kvh = h / (hq / hkv);
   const int qb = rb * 32 + l32;
   const bool row_ok = qb < nb;
@@ -581,55 +596,79 @@ __global__ __launch_bounds__(64) void pe_logits_kernel(const float* __restrict__
     }
   }
   float* Ph = P + (int64_t)h * tri(nb);
-  float m = -INFINITY, l = 0.f;
-  // the key-block means of tile ct + 1 are loaded while the MFMAs of tile ct run
-  auto kload = [&](int ct, float4 (&kx)[16]) {
-    const int krow = ct * 32 + l32;
-    const float4* ksrc = (const float4*)(kbar + ((int64_t)kvh * nb + (krow < nb ? krow : 0)) * HD + 64 * g);
+  const float* kh = kbar + (int64_t)kvh * nb * HD;
+  // 256 threads copy a tile's 32 x 128 floats: thread t holds row t / 8, floats 16 (t % 8) .. + 15
+  const int cr = tid >> 3, cc = (tid & 7) * 16;
+  f32x4 stg[4];   // a register vector type: float4 struct copies would go through scratch
+  auto kfetch = [&](int ct) {
+    const int krow = ct * 32 + cr;
+    const f32x4* src = (const f32x4*)(kh + (int64_t)(krow < nb ? krow : 0) * HD + cc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kx[i] = ksrc[i];
+    for (int i = 0; i < 4; ++i) stg[i] = src[i];
   };
-  float4 kcur[16], knext[16];
-  kload(ct0, kcur);
+  auto kstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(f32x4*)&kt[buf][cr * KT_PITCH + cc + 4 * i] = stg[i];
+  };
+  kfetch(ct0);
+  kstore(0);
+  __syncthreads();
+  float m = -INFINITY, l = 0.f;
   for (int ct = ct0; ct < ct1; ++ct) {
-    if (ct + 1 < ct1) kload(ct + 1, knext);
-    f32x16 acc = {};
+    const int buf = (ct - ct0) & 1;
+    if (ct + 1 < ct1) kfetch(ct + 1);
+    if (ct < ntile) {
+      // two independent chains (d slices 4i..4i+1 and 4i+2..4i+3) keep the
+      // matrix unit fed from one wave; summed at the end
+      f32x16 acc = {}, acc2 = {};
+      const float* ka = &kt[buf][l32 * KT_PITCH + 64 * g];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc = mfma_f32(kcur[i].x, qv[4 * i], acc);
-      acc = mfma_f32(kcur[i].y, qv[4 * i + 1], acc);
-      acc = mfma_f32(kcur[i].z, qv[4 * i + 2], acc);
-      acc = mfma_f32(kcur[i].w, qv[4 * i + 3], acc);
+      for (int i = 0; i < 16; ++i) {
+        const float4 a = *(const float4*)(ka + 4 * i);
+        acc = mfma_f32(a.x, qv[4 * i], acc);
+        acc2 = mfma_f32(a.z, qv[4 * i + 2], acc2);
+        acc = mfma_f32(a.y, qv[4 * i + 1], acc);
+        acc2 = mfma_f32(a.w, qv[4 * i + 3], acc2);
+      }
+      acc += acc2;
+      float tmx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kb = ct * 32 + mfma32_row(r, g);
+        const float x = acc[r] * scale;
+        acc[r] = (row_ok && kb <= qb) ? x : -INFINITY;
+        tmx = fmaxf(tmx, acc[r]);
+        tileT[w][l32][mfma32_row(r, g)] = x;
+      }
+      tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+      const float mn = fmaxf(m, tmx);
+      float se = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) se += (acc[r] == -INFINITY) ? 0.f : pe_exp(acc[r] - mn);
+      se += __shfl_xor(se, 32, 64);
+      l = (m == -INFINITY ? 0.f : l * pe_exp(m - mn)) + se;
+      m = mn;
+      __builtin_amdgcn_wave_barrier();
+      // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row
+      {
+        const int kb = ct * 32 + l32;
+        int q = rb * 32 + g;
+        int64_t tq = tri(q);                 // tri(q + 2) = tri(q) + 2q + 3
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (q < nb && kb <= q) Ph[tq + kb] = tileT[w][2 * j + g][l32];
+          tq += 2 * q + 3;
+          q += 2;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kcur[i] = knext[i];
-    float tmx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kb = ct * 32 + mfma32_row(r, g);
-      const float x = acc[r] * scale;
-      acc[r] = (row_ok && kb <= qb) ? x : -INFINITY;
-      tmx = fmaxf(tmx, acc[r]);
-      tileT[l32][mfma32_row(r, g)] = x;
+    if (ct + 1 < ct1) {
+      kstore(buf ^ 1);   // the other buffer was last read before the previous barrier
+      __syncthreads();
     }
-    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
-    const float mn = fmaxf(m, tmx);
-    float se = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) se += (acc[r] == -INFINITY) ? 0.f : expf(acc[r] - mn);
-    se += __shfl_xor(se, 32, 64);
-    l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + se;
-    m = mn;
-    __builtin_amdgcn_wave_barrier();
-    // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int q = rb * 32 + 2 * j + g, kb = ct * 32 + l32;
-      if (q < nb && kb <= q) Ph[tri(q) + kb] = tileT[2 * j + g][l32];
-    }
-    __builtin_amdgcn_wave_barrier();
   }
-  if (row_ok && g == 0) part[((int64_t)h * nb + qb) * nseg + cs] = make_float2(m, l);
+  if (row_ok && g == 0 && ct0 < ntile) part[((int64_t)h * nb + qb) * nseg + cs] = make_float2(m, l);
 }
 
 // Row softmax in place: one work-group per (query block, Pooled-Estimation
@@ -649,7 +688,7 @@ __global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict_
   float M = -INFINITY;
   for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
   float S = 0.f;
-  for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * expf(pp[c].x - M);
+  for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * pe_exp(pp[c].x - M);
   const float inv = 1.f / S;
   float* row = P + (int64_t)h * tri(nb) + tri(qb);
   for (int k0 = 0; k0 <= qb; k0 += 2048) {
@@ -662,7 +701,7 @@ __global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kb = k0 + 256 * j + tid;
-      if (kb <= qb) row[kb] = expf(x[j] - M) * inv;
+      if (kb <= qb) row[kb] = pe_exp(x[j] - M) * inv;
     }
   }
 }
@@ -714,18 +753,28 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
   // entries) and commits a run with one pair of LDS atomics
   uint32_t run_b = 0xffffffffu, run_c = 0;
   unsigned long long run_m = 0;
-  for (int64_t e = a + tid; e < b; e += 256) {
-    const uint32_t x = bits[e];
-    if (PASS > 0 && (x >> hi) != (prefix >> hi)) continue;
-    const uint32_t bk = (x >> shift) & mask;
-    if (bk != run_b) {
-      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
-      run_b = bk;
-      run_c = 0;
-      run_m = 0;
+  // four strided entries are loaded before any is used (memory-level
+  // parallelism); they are then taken in the same order as one at a time
+  constexpr int U = 4;
+  for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
+    uint32_t xs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? bits[e0 + 256 * u] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t x = xs[u];
+      if (e0 + 256 * u >= b) break;
+      if (PASS > 0 && (x >> hi) != (prefix >> hi)) continue;
+      const uint32_t bk = (x >> shift) & mask;
+      if (bk != run_b) {
+        if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+        run_b = bk;
+        run_c = 0;
+        run_m = 0;
+      }
+      ++run_c;
+      run_m += fx_mass(x);
     }
-    ++run_c;
-    run_m += fx_mass(x);
   }
   if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
   __syncthreads();
@@ -1024,8 +1073,8 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   else
     pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
   const int nrb = (nb_max + 31) / 32, nseg = (nrb + PE_SEG - 1) / PE_SEG;
-  pe_logits_kernel<<<dim3(nrb, nseg, vh), 64, 0, s>>>(b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv,
-                                                      nseg, 1.f / sqrtf((float)HD));
+  pe_logits_kernel<<<dim3((nrb + PE_RB - 1) / PE_RB, nseg, vh), 256, 0, s>>>(
+      b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD));
   pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
   pe_cut_init_kernel<<<vh, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
   const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
