@@ -34,21 +34,35 @@ constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
 __device__ __forceinline__ int rs_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
 
-// Lower / upper sums of one interior tile for wave W (rows 32W .. 32W+31),
-// p = exp2(s sl2 - mb).
-template <int W>
-__device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, float mb, int qrow, int g,
+// Lower / upper sums of one interior tile for the wave owning rows 32w ..
+// 32w+31, p = exp2(s sl2 - mb): key sub-tile t < w lies wholly below the
+// diagonal of every row of the wave, t > w wholly above it (w is wave-uniform,
+// so those are scalar branches), and only the diagonal sub-tile t = w is split
+// per score.  Each sub-tile is summed on its own, then added in t order.
+__device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, float mb, int w, int l32, int g,
                                               float& lo, float& up) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    float a = 0.f, b = 0.f;
+    if (t == w) {
+      int lim = l32 - 4 * g;               // key 32t + 8(i/4) + 4g + i%4 <= row 32w + l32
+      asm volatile("" : "+v"(lim));        // the 16 compares stay here (not hoisted into SGPR masks)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
-      if (t < W) lo += p;
-      else if (t > W) up += p;
-      else if (32 * t + mfma32_row(i, g) <= qrow) lo += p;
-      else up += p;
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
+        if (8 * (i >> 2) + (i & 3) <= lim) a += p;
+        else b += p;
+      }
+      lo += a;
+      up += b;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a += fast_exp2(fmaf(s[t][i], sl2, -mb));
+      const bool below = t < w;             // value selects (a pointer select would go to scratch)
+      lo += below ? a : 0.f;
+      up += below ? 0.f : a;
     }
+  }
 }
 
 // Scores of the last query block against PCH key blocks; per (tile, row):
@@ -56,12 +70,16 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
 // column <= row: slash bin N_b-1-kb), the upper part (bin N_b-2-kb) and the
 // anchor windows.
 template <typename T>
-__global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proxy_tiles_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           float4* __restrict__ tstat, float* __restrict__ kbar,
                                                           const SeqList seqs, int hq, int hkv, int64_t sq_h,
                                                           int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
                                                           int w_local, int dense_below_n, float sl2) {
-  __shared__ __attribute__((aligned(16))) T sK[BLK * Tile<T>::KP];
+  // bf16: two K tiles (the next one is written while the current one is read);
+  // fp32 keeps one (its staging would not fit in registers)
+  constexpr bool PIPE = sizeof(T) == 2;
+  constexpr int TILE = BLK * Tile<T>::KP;
+  __shared__ __attribute__((aligned(16))) T sK[(PIPE ? 2 : 1) * TILE];
   __shared__ float red[2][HD];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the t-vs-w branches are scalar
@@ -80,27 +98,41 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
   typename Tile<T>::QFrag qf;
   Tile<T>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const int kb0 = chunk * PCH, kb1 = min(nb, kb0 + PCH);
+  const T* Kh = K + (int64_t)kvh * sk_h;
+  typename Tile<bf16>::KStage stg;
+  if constexpr (PIPE) {
+    Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)kb0 * BLK * sk_n, sk_n, tid);
+    Tile<bf16>::store_k((bf16*)sK, stg, tid);
+    __syncthreads();
+  }
   for (int kb = kb0; kb < kb1; ++kb) {
-    __syncthreads();
-    Tile<T>::load_k(sK, K + (int64_t)kvh * sk_h + (int64_t)kb * BLK * sk_n, sk_n, tid);
-    __syncthreads();
+    T* cur = sK + (PIPE ? ((kb - kb0) & 1) * TILE : 0);
+    if constexpr (PIPE) {
+      if (kb + 1 < kb1) Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)(kb + 1) * BLK * sk_n, sk_n, tid);
+    } else {
+      __syncthreads();
+      Tile<T>::load_k(cur, Kh + (int64_t)kb * BLK * sk_n, sk_n, tid);
+      __syncthreads();
+    }
     if (hig == 0) {  // block mean of K for Pooled Estimation, once per KV head
       const int d = tid & 127, half = tid >> 7;
       float sum = 0.f;
-      for (int r = 0; r < 64; ++r) sum += to_f32(sK[(64 * half + r) * Tile<T>::KP + d]);
+      for (int r = 0; r < 64; ++r) sum += to_f32(cur[(64 * half + r) * Tile<T>::KP + d]);
       red[half][d] = sum;
       __syncthreads();
       if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][d] + red[1][d]) * (1.f / BLK);
     }
     f32x16 s[4];
-    Tile<T>::st(s, sK, qf, l32, g);
+    Tile<T>::st(s, cur, qf, l32, g);
     const bool last = (kb == nb - 1);
     if (last) {
+      int lim = qrow;
+      asm volatile("" : "+v"(lim));   // compares stay in this once-per-row branch (no hoisted SGPR masks)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * t + mfma32_row(i, g) > qrow) s[t][i] = -INFINITY;
+          if (32 * t + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -113,16 +145,13 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
     const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
     float lo = 0.f, up = 0.f, an = 0.f;
     // key c = 32t + .. against this wave's rows 32w .. 32w+31: t < w all lower,
-    // t > w all upper, t = w split per score; interior tiles take a path
-    // specialised on w, the last tile and the anchor tiles the general one
+    // t > w all upper, t = w split per score; interior tiles take the short
+    // path, the last tile and the anchor tiles the general one
     if (!last && !touches_anchor) {
-      switch (w) {
-        case 0: interior_sums<0>(s, sl2, mb, qrow, g, lo, up); break;
-        case 1: interior_sums<1>(s, sl2, mb, qrow, g, lo, up); break;
-        case 2: interior_sums<2>(s, sl2, mb, qrow, g, lo, up); break;
-        default: interior_sums<3>(s, sl2, mb, qrow, g, lo, up); break;
-      }
+      interior_sums(s, sl2, mb, w, l32, g, lo, up);
     } else {
+      int lim = qrow;
+      asm volatile("" : "+v"(lim));   // as above: the per-score compares stay in this branch
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t > w && last) continue;
@@ -131,7 +160,7 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
           const int c = 32 * t + mfma32_row(i, g);
           const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
           bool lower = t < w;
-          if (t == w) lower = c <= qrow;
+          if (t == w) lower = c <= lim;
           if (lower) lo += p;
           else if (!last) up += p;
           if (touches_anchor && (lower || !last)) {
@@ -145,6 +174,13 @@ __global__ __launch_bounds__(256) void proxy_tiles_kernel(const T* __restrict__ 
     up += __shfl_xor(up, 32, 64);
     an += __shfl_xor(an, 32, 64);
     if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
+    if constexpr (PIPE) {
+      // the other buffer was last read before the previous barrier
+      if (kb + 1 < kb1) {
+        Tile<bf16>::store_k((bf16*)sK + (((kb - kb0) & 1) ^ 1) * TILE, stg, tid);
+        __syncthreads();
+      }
+    }
   }
 }
 

@@ -21,6 +21,24 @@ template <> struct Tile<bf16> {
 #pragma unroll
     for (int c = 0; c < 8; ++c) f.v[c] = *(const bf16x8*)(row + 16 * c + 8 * g);
   }
+  // the same copy split in two, so that the next tile's global loads can be in
+  // flight (in 32 registers) while the current tile is used
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  struct KStage { u32x4 v[8]; };
+  __device__ static void fetch_k(KStage& st, const bf16* kbase, int64_t ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
+      st.v[i] = *(const u32x4*)(kbase + (int64_t)r * ld + gr * 8);
+    }
+  }
+  __device__ static void store_k(bf16* sK, const KStage& st, int tid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
+      *(u32x4*)(sK + r * KP + gr * 8) = st.v[i];
+    }
+  }
   // 128 x 128 tile, rows kbase[r * ld] -> sK[r * KP]
   __device__ static void load_k(bf16* sK, const bf16* kbase, int64_t ld, int tid) {
 #pragma unroll
