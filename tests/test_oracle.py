@@ -466,3 +466,35 @@ def test_jsd_router_threshold_and_variants_on_tiny_layer():
     for tau in [0.0, min(js), max(js), max(js) + 1e-9]:
         vs = [O.route_jsd(j, tau) for j in js]
         assert vs == [j >= float(np.float32(tau)) for j in js]
+
+
+def test_coverage_budget_grows_with_n_noise_floor_stays_flat():
+    """The mass-cliff argument (CRISP §4): on a concentrated head whose anchors hold
+    less than gamma of the proxy mass, a cumulative-coverage budget must take
+    background blocks, whose per-block mass falls as 1/n, so it grows linearly in
+    n; the noise floor (threshold at the mean non-anchor block) keeps the planted
+    blocks only.  Head: the second concentrated query head of a KV group (its
+    recency block is aligned with the group's first head, so its anchors are
+    weaker), length-compensated generator, n = 4k .. 32k."""
+    from workloads import synth
+    cov_sizes = []
+    for n in (4096, 8192, 16384, 32768):
+        cfg = synth.custom_config("conc-pair", n, 2, 1, "fp32", seed=11, conc_frac=1.0, sink=(6.0, 6.0),
+                                  needles=(3, 3))
+        spec = synth.make_spec(cfg)
+        assert spec.lead[0] == 0 and spec.concentrated[1]
+        q = synth.rows(spec, "q", 1, n - 128, n).astype(np.float64)
+        k = synth.rows(spec, "k", 0, 0, n).astype(np.float64)
+        A = O.proxy_attention(q, k)
+        pv = O.vertical_scores(A, 128).astype(np.float32)
+        assert O.route_decision(np.float32(O.c_struct(A, 128, 128)), cfg.tau)   # a Vertical-Slash head
+        floor = O.vs_select_direction(pv, cfg.alpha)
+        planted = sorted({0, cfg.nb - 1, *spec.needle_blocks[0]})
+        assert floor.tolist() == planted                                        # flat: the planted blocks
+        cov = O.vs_select_coverage(pv, cfg.gamma)
+        cov = cov[0] if isinstance(cov, tuple) else cov
+        assert set(planted) <= set(np.asarray(cov).tolist())
+        cov_sizes.append(len(cov))
+    for a, b in zip(cov_sizes, cov_sizes[1:]):
+        assert b >= 1.8 * a, cov_sizes                                          # ~doubles with n
+    assert cov_sizes[0] > len(planted)
