@@ -194,22 +194,51 @@ __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int 
   return true;
 }
 
+// An ascending key-block list read through a window of 64 entries, one per
+// lane of a VGPR, with the next window already loaded: an entry costs one
+// v_readlane instead of a dependent scalar load per key block, and a window's
+// load is consumed only 64 entries later.  Loads use a clamped index (no
+// select on the loaded value, which would wait for it at once).
+struct ListWindow {
+  const int32_t* l;
+  int n, base, cur, nxt;
+  __device__ void init(const int32_t* list, int len, int lane) {
+    l = list;
+    n = len;
+    base = 0;
+    cur = nxt = 0;
+    if (n > 0) {
+      cur = l[min(lane, n - 1)];
+      nxt = l[min(64 + lane, n - 1)];
+    }
+  }
+  // entry i, 0 <= i < n, i never below a previous call's (the walk is forward)
+  __device__ int at(int i, int lane) {
+    while (i - base >= 64) {                 // wave-uniform
+      base += 64;
+      cur = nxt;
+      nxt = l[min(base + 64 + lane, n - 1)];
+    }
+    return __builtin_amdgcn_readlane(cur, i - base);
+  }
+};
+
 // Walks the union of the ascending key-block lists of the two query blocks of
 // a work-group.  Entries outside [0, qb] of their own block are skipped.
 struct PairCursor {
-  const int32_t* a;  const int32_t* b;
-  int na, nb_, ia, ib, qa, qb;
-  __device__ int head(const int32_t* l, int n, int& i, int q) const {
-    while (i < n) {
-      const int k = __builtin_amdgcn_readfirstlane(l[__builtin_amdgcn_readfirstlane(i)]);
+  ListWindow a, b;
+  int ia, ib, qa, qb;
+  __device__ int head(ListWindow& l, int& i, int q, int lane) {
+    while (i < l.n) {
+      const int k = l.at(i, lane);
       if ((unsigned)k <= (unsigned)q) return k;
       ++i;
     }
     return 0x7fffffff;
   }
   // next block of the union (-1 when done) and which halves list it
-  __device__ int next(bool& in_a, bool& in_b) {
-    const int x = head(a, na, ia, qa), y = head(b, nb_, ib, qb);
+  __device__ int next(bool& in_a, bool& in_b, int lane) {
+    const int x = head(a, ia, qa, lane), y = head(b, ib, qb, lane);
     const int k = min(x, y);
     in_a = (x == k) && k != 0x7fffffff;
     in_b = (y == k) && k != 0x7fffffff;
@@ -245,15 +274,12 @@ __device__ __forceinline__ void fa_bf16_item(
   cur.ia = cur.ib = 0;
   if (!DENSE) {
     const int64_t ra = (int64_t)h * nb + qlo;
-    cur.a = col_idx + row_ptr[ra];
-    cur.na = row_ptr[ra + 1] - row_ptr[ra];
-    if (hi_ok) {
-      cur.b = col_idx + row_ptr[ra + 1];
-      cur.nb_ = row_ptr[ra + 2] - row_ptr[ra + 1];
-    } else {
-      cur.b = cur.a;
-      cur.nb_ = 0;
-    }
+    const int32_t p0 = row_ptr[ra], p1 = row_ptr[ra + 1];
+    cur.a.init(col_idx + p0, p1 - p0, lane);
+    if (hi_ok)
+      cur.b.init(col_idx + p1, row_ptr[ra + 2] - p1, lane);
+    else
+      cur.b.init(col_idx + p0, 0, lane);
   }
   int dense_next = 0;
   auto next_block = [&](bool& ia, bool& ib) -> int {
@@ -264,7 +290,7 @@ __device__ __forceinline__ void fa_bf16_item(
       ib = hi_ok && k <= qhi;
       return k <= top ? k : -1;
     }
-    return cur.next(ia, ib);
+    return cur.next(ia, ib, lane);
   };
 
   const int qrow = 32 * wq + l32;
@@ -306,9 +332,11 @@ __device__ __forceinline__ void fa_bf16_item(
   while (kb >= 0) {
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);       // this wave's share of the tiles of kb has landed
     block_barrier();                            // all of them have; every wave left the other stage
-    if (kb1 >= 0) issue(kb1, stage ^ 1);
+    // the list lookup comes before the copy is issued: a window refill then has
+    // nothing in flight to wait for (all loads completed at the wait above)
     bool a2 = false, b2 = false;
-    const int kb2 = kb1 >= 0 ? next_block(a2, b2) : -1;   // list lookup overlaps the MFMAs
+    const int kb2 = kb1 >= 0 ? next_block(a2, b2) : -1;
+    if (kb1 >= 0) issue(kb1, stage ^ 1);
     const bool active = half ? b0 : a0;
     if (active) {
       const uint32_t so = stage * STAGE_BYTES;
