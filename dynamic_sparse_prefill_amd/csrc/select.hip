@@ -852,7 +852,13 @@ __global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restric
   if (qb >= nb) return;
   const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
   int cnt = 0;
-  for (int k = lane; k <= qb; k += 64) cnt += (row[k] == c.vstar);
+  for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
+    uint32_t xs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : ~c.vstar;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cnt += (xs[u] == c.vstar);
+  }
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
   if (lane == 0) eqrow[sp.rows + (int64_t)(h % hq) * nb + qb] = cnt;
 }
@@ -913,20 +919,32 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
     const bool split = c.take < c.eq_cnt;
     int base = 0;
     long long eqb = split ? eqrow[row] : 0;
-    for (int k0 = 0; k0 <= qb; k0 += 64) {
-      const int k = k0 + lane;
-      const bool valid = k <= qb;
-      const uint32_t x = valid ? bits[k] : 0u;
-      bool sel = valid && ((x > c.vstar) || k == 0 || k == qb || (!split && x == c.vstar));
-      if (split) {  // the cut splits a run of equal values: take them in flat order
-        const bool eq = valid && x == c.vstar;
-        const unsigned long long em = __ballot(eq);
-        if (eq && (unsigned long long)(eqb + lane_prefix(em)) < c.take) sel = true;
-        eqb += __popcll(em);
+    // four 64-entry pieces are loaded before any is used, then taken in order
+    for (int k00 = 0; k00 <= qb; k00 += 256) {
+      uint32_t xs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k00 + 64 * u + lane;
+        xs[u] = k <= qb ? bits[k] : 0u;
       }
-      const unsigned long long m = __ballot(sel);
-      if (FILL && sel) out[base + lane_prefix(m)] = k;
-      base += __popcll(m);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k0 = k00 + 64 * u;
+        if (k0 > qb) break;
+        const int k = k0 + lane;
+        const bool valid = k <= qb;
+        const uint32_t x = xs[u];
+        bool sel = valid && ((x > c.vstar) || k == 0 || k == qb || (!split && x == c.vstar));
+        if (split) {  // the cut splits a run of equal values: take them in flat order
+          const bool eq = valid && x == c.vstar;
+          const unsigned long long em = __ballot(eq);
+          if (eq && (unsigned long long)(eqb + lane_prefix(em)) < c.take) sel = true;
+          eqb += __popcll(em);
+        }
+        const unsigned long long m = __ballot(sel);
+        if (FILL && sel) out[base + lane_prefix(m)] = k;
+        base += __popcll(m);
+      }
     }
     if (!FILL && lane == 0) counts[row] = base;
     return;
