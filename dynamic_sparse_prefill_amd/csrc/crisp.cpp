@@ -86,7 +86,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
     if (nb > nb_max) nb_max = nb;
   }
   const int64_t nch = proxy_chunks((int)nb_max);
-  const int64_t nseg = ((nb_max + 31) / 32 + 31) / 32;   // segments of 32 tiles of 32 key blocks
+  const int64_t nseg = pe_segments(nb_max);
   SelectLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };

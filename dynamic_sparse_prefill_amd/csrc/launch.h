@@ -18,6 +18,10 @@ hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv
 // nb[i]) of Q, K, V^T and O, and its lists live at row_ptr + rp[i] (hq * nb[i]
 // + 1 entries, offsets relative to col_idx + col[i]).
 constexpr int MAX_SEQ = 64;
+// Pooled-estimation logits are produced in segments of PE_SEG tiles of 32 key
+// blocks (one work-group each); every row keeps one (max, sum) pair per segment.
+constexpr int PE_SEG = 8;
+inline int pe_segments(int nb) { return ((nb + 31) / 32 + PE_SEG - 1) / PE_SEG; }
 struct SeqTable {
   int nseq;
   int unit_off[MAX_SEQ + 1];   // work units (query-block pairs x KV heads) before sequence i

@@ -537,9 +537,19 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, co
 
 __device__ __forceinline__ int64_t tri(int64_t qb) { return qb * (qb + 1) / 2; }
 
-constexpr int PE_SEG = 32;  // 32-key-block tiles per logits work-group (1024 key blocks)
 
 constexpr int PE_RB = 4;     // 32-query-block row blocks (one wave each) per logits work-group
+
+// max / sum of a lane's value and that of lane ^ 32 (one v_permlane32_swap,
+// no LDS round trip); both lanes of a pair get the same result
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // e^x of the pooled softmax as v_exp_f32 (2^x) of x log2(e): relative error
 // about |x| 2^-24 beyond the instruction's own, far below the probabilities'
@@ -640,23 +650,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         tmx = fmaxf(tmx, acc[r]);
         tileT[w][l32][mfma32_row(r, g)] = x;
       }
-      tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+      tmx = pair_max(tmx);
       const float mn = fmaxf(m, tmx);
       float se = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) se += (acc[r] == -INFINITY) ? 0.f : pe_exp(acc[r] - mn);
-      se += __shfl_xor(se, 32, 64);
+      se = pair_sum(se);
       l = (m == -INFINITY ? 0.f : l * pe_exp(m - mn)) + se;
       m = mn;
       __builtin_amdgcn_wave_barrier();
       // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row
       {
+        // all 16 reads first (one wait), then the stores
+        float vals[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) vals[j] = tileT[w][2 * j + g][l32];
         const int kb = ct * 32 + l32;
         int q = rb * 32 + g;
         int64_t tq = tri(q);                 // tri(q + 2) = tri(q) + 2q + 3
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (q < nb && kb <= q) Ph[tq + kb] = tileT[w][2 * j + g][l32];
+          if (q < nb && kb <= q) Ph[tq + kb] = vals[j];
           tq += 2 * q + 3;
           q += 2;
         }
@@ -1090,7 +1104,7 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
     pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
   else
     pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
-  const int nrb = (nb_max + 31) / 32, nseg = (nrb + PE_SEG - 1) / PE_SEG;
+  const int nrb = (nb_max + 31) / 32, nseg = pe_segments(nb_max);
   pe_logits_kernel<<<dim3((nrb + PE_RB - 1) / PE_RB, nseg, vh), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD));
   pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
