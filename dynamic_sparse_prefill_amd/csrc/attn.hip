@@ -83,6 +83,13 @@ __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// max of a lane's value and that of lane ^ 32 with one v_permlane32_swap (no
+// LDS round trip): both lanes of the pair get the result
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A 128-row x 256-byte tile goes to LDS as 16-byte chunks, chunk c of row r at
 // physical chunk c ^ (r & 15): 16 lanes reading the same logical chunk of 16
 // consecutive rows hit 16 different bank groups.  With 8 waves, wave w copies
@@ -117,8 +124,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Four 16-byte LDS reads at addr + OFF + {0, 8, 16, 24} KB (rows 0, 32, 64, 96
 // of a tile for this lane), completed inside the same asm block.  Written by
-// hand so that the compiler does not add a wait on the in-flight global->LDS
-// copy of the next tile before them.  The outputs are early-clobber: a read's
+// hand: while a global->LDS copy is in flight the compiler can only follow its
+// own LDS reads with a full lgkmcnt(0) wait, so grouping the reads of a step
+// under one wait is done here explicitly.  The outputs are early-clobber: a read's
 // result may land while later reads of the block still need the address
 // registers, so no output may share a register with an address.
 template <int OFF>
@@ -373,7 +381,7 @@ __device__ __forceinline__ void fa_bf16_item(
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = pair_max(mx);
       // Lazy running max: m is raised only when a row's tile max exceeds it by
       // more than 2^8 in probability, so most tiles skip rescaling O and l.
       // Exact softmax either way: p = exp2((s - m) sl2) <= 2^8 in fp32 / bf16.
@@ -517,7 +525,7 @@ __global__ __launch_bounds__(256, 1) void fa_f32_kernel(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = pair_max(mx);
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2((m - mn) * sl2);
     const float mb = mn * sl2;
