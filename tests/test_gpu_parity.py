@@ -170,6 +170,15 @@ def test_dense_fallback_paths():
     assert sel2.route.cpu().tolist() == [-1, -1]
     rp = sel2.row_ptr.cpu().numpy()
     assert np.array_equal(np.diff(rp), np.tile(np.arange(1, 17), 2))
+    # one block (n = b): no noise floor exists (N_b - 2 < 1), every head takes the dense path
+    cfg3 = synth.custom_config("one-block", 128, 4, 2, seed=5)
+    spec3 = synth.make_spec(cfg3)
+    Q3, K3, V3 = synth.generate(spec3)
+    _, _, _, o3, sel3 = _run_layer(spec3, Q3, K3, V3, P.params_of(cfg3))
+    assert sel3.route.cpu().tolist() == [-1] * 4
+    assert sel3.row_ptr.cpu().tolist() == [0, 1, 2, 3, 4]
+    assert sel3.col_idx[:4].cpu().tolist() == [0, 0, 0, 0]
+    P.check_attention_blocks(spec3, Q3, K3, V3, o3, lambda h, qb: [0], range(4), [0])
 
 
 def test_parameter_sweep_and_min_blocks():
