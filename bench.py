@@ -418,7 +418,7 @@ def main():
                     help="also run one plain copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding (by KV group) is not built",
+        print(json.dumps({"error": "the path runs on one GPU; sharding by KV group over several GPUs is not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
