@@ -445,7 +445,7 @@ __device__ __forceinline__ void fa_bf16_item(
     }
 }
 
-// Persistent driver: one work-group per CU takes items from the queues until
+// Persistent loop: one work-group per CU takes items from the queues until
 // all are empty.  `queue` holds NQUEUE counters, zero at launch.
 template <bool DENSE>
 __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
