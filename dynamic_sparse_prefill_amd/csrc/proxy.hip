@@ -23,6 +23,7 @@
 // KV head) so the G query heads sharing a K chunk run on one XCD and share
 // its L2.
 #include "common.h"
+#include "lanes.h"
 #include "launch.h"
 #include "tile.h"
 
@@ -65,6 +66,20 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
   }
 }
 
+// K-bar partials of a staged bf16 tile for wave w: column sums over the
+// wave's 32 rows (4w + k + 16i), the lanes that share columns added pairwise
+// (lane ^ 16, then lane ^ 32), written by lanes 0..15 to dst[w][0..127].
+__device__ __forceinline__ void kbar_partials(float (*dst)[HD], const Tile<bf16>::KStage& stg, int w, int lane) {
+  float cs[8];
+  Tile<bf16>::col_sums(cs, stg);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cs[j] = pair_sum(row_pair_sum(cs[j]));
+  if (lane < 16) {
+    *(f32x4*)&dst[w][8 * lane] = f32x4{cs[0], cs[1], cs[2], cs[3]};
+    *(f32x4*)&dst[w][8 * lane + 4] = f32x4{cs[4], cs[5], cs[6], cs[7]};
+  }
+}
+
 // Scores of the last query block against PCH key blocks; per (tile, row):
 // tile max m of the row and the sums of exp(s - m) over the lower part (key
 // column <= row: slash bin N_b-1-kb), the upper part (bin N_b-2-kb) and the
@@ -80,12 +95,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr bool PIPE = sizeof(T) == 2;
   constexpr int TILE = BLK * Tile<T>::KP;
   __shared__ __attribute__((aligned(16))) T sK[(PIPE ? 2 : 1) * TILE];
-  __shared__ float red[2][HD];
+  // K-bar partial column sums: bf16 per (tile parity, wave), fp32 per half tile
+  __shared__ __attribute__((aligned(16))) float red[2][4][HD];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the t-vs-w branches are scalar
   const int G = hq / hkv;
   const int chunk = blockIdx.x / hq, rem = blockIdx.x % hq;
   const int kvh = rem % hkv, hig = rem / hkv, h = kvh * G + hig;
+  const bool kbar_wg = hig == 0;   // block means of K, once per KV head
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
   const int64_t n = (int64_t)nb * BLK;
@@ -103,10 +120,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if constexpr (PIPE) {
     Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)kb0 * BLK * sk_n, sk_n, tid);
     Tile<bf16>::store_k((bf16*)sK, stg, tid);
+    if (kbar_wg) kbar_partials(red[0], stg, w, lane);
     __syncthreads();
   }
   for (int kb = kb0; kb < kb1; ++kb) {
-    T* cur = sK + (PIPE ? ((kb - kb0) & 1) * TILE : 0);
+    const int par = (kb - kb0) & 1;
+    T* cur = sK + (PIPE ? par * TILE : 0);
     if constexpr (PIPE) {
       if (kb + 1 < kb1) Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)(kb + 1) * BLK * sk_n, sk_n, tid);
     } else {
@@ -114,13 +133,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       Tile<T>::load_k(cur, Kh + (int64_t)kb * BLK * sk_n, sk_n, tid);
       __syncthreads();
     }
-    if (hig == 0) {  // block mean of K for Pooled Estimation, once per KV head
-      const int d = tid & 127, half = tid >> 7;
-      float sum = 0.f;
-      for (int r = 0; r < 64; ++r) sum += to_f32(cur[(64 * half + r) * Tile<T>::KP + d]);
-      red[half][d] = sum;
-      __syncthreads();
-      if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][d] + red[1][d]) * (1.f / BLK);
+    if (kbar_wg) {  // block mean of K for Pooled Estimation
+      if constexpr (PIPE) {
+        // the partials of this tile were written before the last barrier
+        if (tid < HD)
+          kbar[((int64_t)kvh * nb + kb) * HD + tid] =
+              (((red[par][0][tid] + red[par][1][tid]) + red[par][2][tid]) + red[par][3][tid]) * (1.f / BLK);
+      } else {
+        const int d = tid & 127, half = tid >> 7;
+        float sum = 0.f;
+        for (int r = 0; r < 64; ++r) sum += to_f32(cur[(64 * half + r) * Tile<T>::KP + d]);
+        red[0][half][d] = sum;
+        __syncthreads();
+        if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][0][d] + red[0][1][d]) * (1.f / BLK);
+      }
     }
     f32x16 s[4];
     Tile<T>::st(s, cur, qf, l32, g);
@@ -139,7 +165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));   // every row keeps at least its diagonal key: finite
+    mx = pair_max(mx);   // every row keeps at least its diagonal key: finite
     const float mb = mx * sl2;
     const int64_t j0 = (int64_t)kb * BLK;
     const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
@@ -170,14 +196,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
       }
     }
-    lo += __shfl_xor(lo, 32, 64);
-    up += __shfl_xor(up, 32, 64);
-    an += __shfl_xor(an, 32, 64);
+    lo = pair_sum(lo);
+    up = pair_sum(up);
+    an = pair_sum(an);
     if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
     if constexpr (PIPE) {
-      // the other buffer was last read before the previous barrier
+      // the other buffer and the other partials were last read before the
+      // previous barrier
       if (kb + 1 < kb1) {
-        Tile<bf16>::store_k((bf16*)sK + (((kb - kb0) & 1) ^ 1) * TILE, stg, tid);
+        Tile<bf16>::store_k((bf16*)sK + (par ^ 1) * TILE, stg, tid);
+        if (kbar_wg) kbar_partials(red[par ^ 1], stg, w, lane);
         __syncthreads();
       }
     }

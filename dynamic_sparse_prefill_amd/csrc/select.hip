@@ -33,6 +33,7 @@
 // round-to-nearest float32 operations in a fixed order so that it can be
 // reproduced exactly on the host from the same float32 scores.
 #include "common.h"
+#include "lanes.h"
 #include "launch.h"
 
 namespace crisp {
@@ -539,17 +540,6 @@ __device__ __forceinline__ int64_t tri(int64_t qb) { return qb * (qb + 1) / 2; }
 
 
 constexpr int PE_RB = 4;     // 32-query-block row blocks (one wave each) per logits work-group
-
-// max / sum of a lane's value and that of lane ^ 32 (one v_permlane32_swap,
-// no LDS round trip); both lanes of a pair get the same result
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // e^x of the pooled softmax as v_exp_f32 (2^x) of x log2(e): relative error
 // about |x| 2^-24 beyond the instruction's own, far below the probabilities'

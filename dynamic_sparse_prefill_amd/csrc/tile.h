@@ -39,6 +39,20 @@ template <> struct Tile<bf16> {
       *(u32x4*)(sK + r * KP + gr * 8) = st.v[i];
     }
   }
+  // column sums of the staged copy: thread tid holds rows tid/16 + 16i
+  // (i = 0..7) of columns 8(tid%16) .. +7; cs[j] = sum over its rows, in i order
+  __device__ static void col_sums(float (&cs)[8], const KStage& st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cs[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const unsigned u = st.v[i][p];               // columns 2p (low half) and 2p + 1
+        cs[2 * p] += __uint_as_float(u << 16);
+        cs[2 * p + 1] += __uint_as_float(u & 0xffff0000u);
+      }
+  }
   // 128 x 128 tile, rows kbase[r * ld] -> sK[r * KP]
   __device__ static void load_k(bf16* sK, const bf16* kbase, int64_t ld, int tid) {
 #pragma unroll
