@@ -10,6 +10,18 @@
 
 using namespace crisp;
 
+int crisp::device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 namespace {
 constexpr int BLK = 128;   // block size b: pooling, selection and attention tile edge
 constexpr int HD = 128;    // head dim d
@@ -62,7 +74,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
   size_t tstat, stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
-      pepart, total;
+      pepart, peq, total;
 };
 
 SeqList one_sequence(const crisp_shape* s) {
@@ -111,6 +123,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
   L.jsd = take(vh * 8);
   L.abar = take(rows * 4);
   L.pepart = take(rows * nseg * 8);
+  L.peq = take(sizeof(int));
   L.total = o;
   return L;
 }
@@ -187,6 +200,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.eqrow = (int32_t*)(w + L.eqrow);
   b.counts = (int32_t*)(w + L.counts);
   b.pepart = w + L.pepart;
+  b.peq = (int*)(w + L.peq);
   b.route = out->route;
   b.c_struct = out->c_struct;
   b.row_ptr = out->row_ptr;

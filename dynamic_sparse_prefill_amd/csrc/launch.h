@@ -81,6 +81,9 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
                         void* rowstat /*[nseq*hq*128] float2*/, void* tiles /*[rows] float4*/,
                         float* kbar /*[kvrows*128]*/, hipStream_t s);
 
+// compute units of the current device (cached per device)
+int device_cu_count();
+
 // ---- selection (select.hip)
 struct PeCut;                       // per-head radix-select state (select.hip)
 size_t pe_cut_state_bytes();
@@ -96,6 +99,7 @@ struct SelectBufs {
   uint32_t* hcnt;  unsigned long long* hmass;  void* cut;
   int32_t *eqrow, *counts;
   void* pepart;                     // [hq * nb * nseg] float2: per-segment row max / sum of the pooled logits
+  int* peq;                         // work counter of the pooled-logits kernel
   // caller outputs
   int32_t* route; float* c_struct; int32_t *row_ptr, *col_idx;
   float *pv_out, *ps_out; int32_t *sv_out, *nv_out, *ss_out, *ns_out;

@@ -32,6 +32,8 @@
 // The decision arithmetic (route, mu, threshold) is written with explicit
 // round-to-nearest float32 operations in a fixed order so that it can be
 // reproduced exactly on the host from the same float32 scores.
+#include <algorithm>
+
 #include "common.h"
 #include "lanes.h"
 #include "launch.h"
@@ -501,12 +503,13 @@ __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict
 template <typename T>
 __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, const int32_t* __restrict__ route,
                                                      float* __restrict__ qbar, const SeqList seqs, int hq, int hkv,
-                                                     int64_t sq_h, int64_t sq_n) {
+                                                     int64_t sq_h, int64_t sq_n, int* __restrict__ queue) {
   constexpr int E = 16 / sizeof(T);         // elements per 16-byte load
   constexpr int CPR = HD / E;               // 16-byte chunks per row
   constexpr int RG = 256 / CPR;             // row groups
   __shared__ float red[RG][HD];
   const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
+  if (queue && qb == 0 && vh == 0 && tid == 0) *queue = 0;   // the logits kernel's work counter
   if (route[vh] != 0) return;
   const int h = vh % hq;
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
@@ -547,8 +550,8 @@ constexpr int PE_RB = 4;     // 32-query-block row blocks (one wave each) per lo
 __device__ __forceinline__ float pe_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 constexpr int KT_PITCH = 132; // LDS pitch (floats) of a key-block-mean row: conflict-free 16-byte reads
 
-// Logits: one work-group per (PE_RB row blocks of 32 query blocks, segment cs
-// of PE_SEG key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
+// Logits: one item per (PE_RB row blocks of 32 query blocks, segment cs of
+// PE_SEG key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
 // L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb is formed 32 key blocks
 // at a time with v_mfma_f32_32x32x2f32 in the transposed form L^T = Kbar Qbar^T
 // (lane l owns query block 32 rb + l%32 and 16 of the 32 key blocks; the d
@@ -557,19 +560,16 @@ constexpr int KT_PITCH = 132; // LDS pitch (floats) of a key-block-mean row: con
 // during the MFMAs) and shared by the work-group's waves.  Each tile is turned
 // row-major through LDS and stored with whole 128-byte row segments; the
 // segment's row max and sum of exp(L - max) go to `part` for the softmax.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                        const int32_t* __restrict__ route, float* __restrict__ P,
-                                                        float2* __restrict__ part, const SeqList seqs, int hq,
-                                                        int hkv, int nseg, float scale) {
-  __shared__ __attribute__((aligned(16))) float kt[2][32 * KT_PITCH];
-  __shared__ float tileT[PE_RB][32][33];
-  const int vh = blockIdx.z;
-  if (route[vh] != 0) return;
+// The item's row group rg counts from the top of the sequence's triangle.
+__device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], float (&tileT)[PE_RB][32][33],
+                                               const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                               float* __restrict__ P, float2* __restrict__ part, const SeqList& seqs,
+                                               int hq, int hkv, int nseg, float scale, int vh, int rg_top, int cs) {
   const int h = vh % hq;
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
   const int nb = sp.nb;
   const int nrb = (nb + 31) / 32, nrg = (nrb + PE_RB - 1) / PE_RB;
-  const int rg = nrg - 1 - (int)blockIdx.x, cs = blockIdx.y;
+  const int rg = nrg - 1 - rg_top;
   if (rg < 0) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int rb = rg * PE_RB + w;
@@ -620,16 +620,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     if (ct < ntile) {
       // two independent chains (d slices 4i..4i+1 and 4i+2..4i+3) keep the
       // matrix unit fed from one wave; summed at the end
+      // matrix operands read one step ahead of the four MFMAs that use them
+      // (the order is pinned: left to itself the compiler waits on each read
+      // just before its use)
       f32x16 acc = {}, acc2 = {};
       const float* ka = &kt[buf][l32 * KT_PITCH + 64 * g];
+      __builtin_amdgcn_sched_barrier(0);
+      float4 a = *(const float4*)ka;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float4 a = *(const float4*)(ka + 4 * i);
+        float4 an = a;
+        if (i < 15) an = *(const float4*)(ka + 4 * (i + 1));
         acc = mfma_f32(a.x, qv[4 * i], acc);
         acc2 = mfma_f32(a.z, qv[4 * i + 2], acc2);
         acc = mfma_f32(a.y, qv[4 * i + 1], acc);
         acc2 = mfma_f32(a.w, qv[4 * i + 3], acc2);
+        a = an;
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // four MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // the next read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
       acc += acc2;
       float tmx = -INFINITY;
 #pragma unroll
@@ -673,6 +688,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   }
   if (row_ok && g == 0 && ct0 < ntile) part[((int64_t)h * nb + qb) * nseg + cs] = make_float2(m, l);
+}
+
+// Persistent: gridDim.x work-groups (three per CU) take items from *queue
+// (zeroed by pool_q) until none is left.  Item it: virtual head it % nvh
+// fastest, then segment, then row group from the top of the triangle (the
+// longest rows first); items of other routes or past a triangle are skipped.
+// The row groups of one head differ in work up to 8x, so a fixed grid left
+// whole XCDs idle at the end.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pe_logits_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, const int32_t* __restrict__ route,
+    float* __restrict__ P, float2* __restrict__ part, const SeqList seqs, int hq, int hkv, int nseg, float scale,
+    int* __restrict__ queue, int nvh, int nitems) {
+  __shared__ __attribute__((aligned(16))) float kt[2][32 * KT_PITCH];
+  __shared__ float tileT[PE_RB][32][33];
+  __shared__ int s_item;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item's indices stay scalar
+    __syncthreads();   // read by every thread before the next item is fetched
+    if (it >= nitems) break;
+    const int vh = it % nvh, rest = it / nvh;
+    if (route[vh] != 0) continue;
+    pe_logits_item(kt, tileT, qbar, kbar, P, part, seqs, hq, hkv, nseg, scale, vh, rest / nseg, rest % nseg);
+  }
 }
 
 // Row softmax in place: one work-group per (query block, Pooled-Estimation
@@ -1091,12 +1131,14 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   const int pe_all = gamma >= 1.f ? 1 : 0;
   const dim3 gq(nb_max, vh);
   if (fp32)
-    pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
+    pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq);
   else
-    pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n);
+    pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq);
   const int nrb = (nb_max + 31) / 32, nseg = pe_segments(nb_max);
-  pe_logits_kernel<<<dim3((nrb + PE_RB - 1) / PE_RB, nseg, vh), 256, 0, s>>>(
-      b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD));
+  const int pe_items = ((nrb + PE_RB - 1) / PE_RB) * nseg * vh;
+  pe_logits_kernel<<<std::min(pe_items, 3 * device_cu_count()), 256, 0, s>>>(
+      b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
+      pe_items);
   pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
   pe_cut_init_kernel<<<vh, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
   const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
