@@ -33,6 +33,7 @@
 // round-to-nearest float32 operations in a fixed order so that it can be
 // reproduced exactly on the host from the same float32 scores.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "lanes.h"
@@ -646,26 +647,31 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_sched_barrier(0);
       acc += acc2;
-      float tmx = -INFINITY;
+      // an interior tile (below the diagonal tile, rows inside the sequence)
+      // needs no causal mask, no -inf test and no per-row store predicate: the
+      // same values by a shorter path (a scalar branch: rb and ct are
+      // wave-uniform)
+      auto epilogue = [&](auto interior) {
+        constexpr bool IN = decltype(interior)::value;
+        float tmx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kb = ct * 32 + mfma32_row(r, g);
-        const float x = acc[r] * scale;
-        acc[r] = (row_ok && kb <= qb) ? x : -INFINITY;
-        tmx = fmaxf(tmx, acc[r]);
-        tileT[w][l32][mfma32_row(r, g)] = x;
-      }
-      tmx = pair_max(tmx);
-      const float mn = fmaxf(m, tmx);
-      float se = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int kb = ct * 32 + mfma32_row(r, g);
+          const float x = acc[r] * scale;
+          acc[r] = (IN || (row_ok && kb <= qb)) ? x : -INFINITY;
+          tmx = fmaxf(tmx, acc[r]);
+          tileT[w][l32][mfma32_row(r, g)] = x;
+        }
+        tmx = pair_max(tmx);
+        const float mn = fmaxf(m, tmx);
+        float se = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) se += (acc[r] == -INFINITY) ? 0.f : pe_exp(acc[r] - mn);
-      se = pair_sum(se);
-      l = (m == -INFINITY ? 0.f : l * pe_exp(m - mn)) + se;
-      m = mn;
-      __builtin_amdgcn_wave_barrier();
-      // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row
-      {
+        for (int r = 0; r < 16; ++r) se += (!IN && acc[r] == -INFINITY) ? 0.f : pe_exp(acc[r] - mn);
+        se = pair_sum(se);
+        l = (m == -INFINITY ? 0.f : l * pe_exp(m - mn)) + se;
+        m = mn;
+        __builtin_amdgcn_wave_barrier();
+        // rows 2j + g of the tile, key block ct*32 + l32: 128 contiguous bytes per row;
         // all 16 reads first (one wait), then the stores
         float vals[16];
 #pragma unroll
@@ -675,11 +681,13 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
         int64_t tq = tri(q);                 // tri(q + 2) = tri(q) + 2q + 3
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (q < nb && kb <= q) Ph[tq + kb] = vals[j];
+          if (IN || (q < nb && kb <= q)) Ph[tq + kb] = vals[j];
           tq += 2 * q + 3;
           q += 2;
         }
-      }
+      };
+      if (ct < rb && rb * 32 + 31 < nb) epilogue(std::true_type{});
+      else epilogue(std::false_type{});
       __builtin_amdgcn_wave_barrier();
     }
     if (ct + 1 < ct1) {
@@ -690,13 +698,13 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
   if (row_ok && g == 0 && ct0 < ntile) part[((int64_t)h * nb + qb) * nseg + cs] = make_float2(m, l);
 }
 
-// Persistent: gridDim.x work-groups (three per CU) take items from *queue
+// Persistent: gridDim.x work-groups (two per CU) take items from *queue
 // (zeroed by pool_q) until none is left.  Item it: virtual head it % nvh
 // fastest, then segment, then row group from the top of the triangle (the
 // longest rows first); items of other routes or past a triangle are skipped.
 // The row groups of one head differ in work up to 8x, so a fixed grid left
 // whole XCDs idle at the end.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pe_logits_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pe_logits_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, const int32_t* __restrict__ route,
     float* __restrict__ P, float2* __restrict__ part, const SeqList seqs, int hq, int hkv, int nseg, float scale,
     int* __restrict__ queue, int nvh, int nitems) {
@@ -1136,7 +1144,7 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
     pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq);
   const int nrb = (nb_max + 31) / 32, nseg = pe_segments(nb_max);
   const int pe_items = ((nrb + PE_RB - 1) / PE_RB) * nseg * vh;
-  pe_logits_kernel<<<std::min(pe_items, 3 * device_cu_count()), 256, 0, s>>>(
+  pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
       pe_items);
   pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
