@@ -29,7 +29,7 @@
 
 namespace crisp {
 
-constexpr int PCH = 8;        // key blocks per score work-group
+constexpr int PCH = 16;       // key blocks per score work-group
 constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 
 int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
