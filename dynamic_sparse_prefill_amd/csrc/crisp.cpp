@@ -74,7 +74,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
   size_t tstat, stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
-      pepart, peq, total;
+      pepart, peq, rtsum, total;
 };
 
 SeqList one_sequence(const crisp_shape* s) {
@@ -124,6 +124,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
   L.abar = take(rows * 4);
   L.pepart = take(rows * nseg * 8);
   L.peq = take(sizeof(int));
+  L.rtsum = take((size_t)seqs.nseq * row_tiles(hq * nb_max) * 4);
   L.total = o;
   return L;
 }
@@ -201,6 +202,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.counts = (int32_t*)(w + L.counts);
   b.pepart = w + L.pepart;
   b.peq = (int*)(w + L.peq);
+  b.rtsum = (int32_t*)(w + L.rtsum);
   b.route = out->route;
   b.c_struct = out->c_struct;
   b.row_ptr = out->row_ptr;

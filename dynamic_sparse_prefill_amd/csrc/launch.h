@@ -88,6 +88,7 @@ int device_cu_count();
 struct PeCut;                       // per-head radix-select state (select.hip)
 size_t pe_cut_state_bytes();
 constexpr int PE_BUCKETS = 2048;    // histogram size of one radix pass
+int row_tiles(int64_t rows);        // tiles of the row-pointer scan
 
 struct SelectBufs {
   // inputs from the proxy
@@ -100,6 +101,7 @@ struct SelectBufs {
   int32_t *eqrow, *counts;
   void* pepart;                     // [hq * nb * nseg] float2: per-segment row max / sum of the pooled logits
   int* peq;                         // work counter of the pooled-logits kernel
+  int32_t* rtsum;                   // [nseq * row_tiles(hq * nb_max)]: sums of tiles of row counts
   // caller outputs
   int32_t* route; float* c_struct; int32_t *row_ptr, *col_idx;
   float *pv_out, *ps_out; int32_t *sv_out, *nv_out, *ss_out, *ns_out;

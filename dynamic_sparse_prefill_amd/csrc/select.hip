@@ -1049,48 +1049,76 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   if (!FILL && lane == 0) counts[row] = base;
 }
 
-// exclusive scan of one sequence's row counts into its row pointers (one
-// work-group of 1024 threads per sequence): the counts go through in tiles of
-// 4096, four consecutive per thread, with a carry between tiles (a sequence's
-// total fits int32, checked on the host)
-__global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ row_ptr, const SeqList seqs, int hq,
-                                                         int hkv) {
+// Exclusive scan of each sequence's row counts into its row pointers (a
+// sequence's total fits int32, checked on the host), over tiles of ROW_TILE
+// counts in two launches: the sum of every tile, then every tile scanned on
+// top of the sum of the tiles before it (integer sums: the result equals a
+// sequential scan).
+constexpr int ROW_TILE = 4096;
+int row_tiles(int64_t rows) { return (int)((rows + ROW_TILE - 1) / ROW_TILE); }
+
+__device__ __forceinline__ int block_sum_1024(int v, int* wsum) {   // 1024 threads; wsum[16]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) wsum[w] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < 16; ++i) t += wsum[i];
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(1024) void row_tile_sum_kernel(const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ tsum, const SeqList seqs, int hq,
+                                                            int hkv, int ntile_max) {
   __shared__ int wsum[16];
-  __shared__ int s_carry;
+  const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
+  const int64_t rows = (int64_t)hq * sp.nb, i0 = (int64_t)blockIdx.x * ROW_TILE + 4 * threadIdx.x;
+  if ((int64_t)blockIdx.x * ROW_TILE >= rows) return;
+  counts += sp.rows;
+  int own = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) own += i0 + e < rows ? counts[i0 + e] : 0;
+  const int t = block_sum_1024(own, wsum);
+  if (threadIdx.x == 0) tsum[(int64_t)blockIdx.y * ntile_max + blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ tsum,
+                                                         int32_t* __restrict__ row_ptr, const SeqList seqs, int hq,
+                                                         int hkv, int ntile_max) {
+  __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const SeqPos sp = seq_pos(seqs, blockIdx.x, hq, hkv);
-  const int64_t rows = (int64_t)hq * sp.nb;
+  const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
+  const int64_t rows = (int64_t)hq * sp.nb, base = (int64_t)blockIdx.x * ROW_TILE;
+  if (base >= rows) return;
   counts += sp.rows;
   row_ptr += sp.rp;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int64_t base = 0; base < rows; base += 4096) {
-    const int64_t i0 = base + 4 * tid;
-    int v[4];
+  // sum of the tiles before this one
+  int pre = 0;
+  for (int i = tid; i < (int)blockIdx.x; i += 1024) pre += tsum[(int64_t)blockIdx.y * ntile_max + i];
+  const int carry = block_sum_1024(pre, wsum);
+  const int64_t i0 = base + 4 * tid;
+  int v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = i0 + e < rows ? counts[i0 + e] : 0;
-    const int own = v[0] + v[1] + v[2] + v[3];
-    int incl = own;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    int before = s_carry;
-    for (int i = 0; i < w; ++i) before += wsum[i];
-    int run = before + incl - own;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e < rows) row_ptr[i0 + e] = run;
-      run += v[e];
-    }
-    __syncthreads();
-    if (tid == 1023) s_carry = run;
-    __syncthreads();
+  for (int e = 0; e < 4; ++e) v[e] = i0 + e < rows ? counts[i0 + e] : 0;
+  const int own = v[0] + v[1] + v[2] + v[3];
+  int incl = own;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  if (tid == 0) row_ptr[rows] = s_carry;
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = carry;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  int run = before + incl - own;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (i0 + e < rows) row_ptr[i0 + e] = run;
+    run += v[e];
+  }
+  if (tid == 1023 && base + ROW_TILE >= rows) row_ptr[rows] = run;   // the sequence's total
 }
 
 __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
@@ -1162,7 +1190,9 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);
   list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
                                                b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
-  scan_rows_kernel<<<seqs.nseq, 1024, 0, s>>>(b.counts, b.row_ptr, seqs, hq, hkv);
+  const int ntile = row_tiles((int64_t)hq * nb_max);
+  row_tile_sum_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, seqs, hq, hkv, ntile);
+  scan_rows_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, b.row_ptr, seqs, hq, hkv, ntile);
   list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
                                               b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
   if (b.sv_out || b.nv_out || b.ss_out || b.ns_out)
