@@ -805,27 +805,52 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
   // entries) and commits a run with one pair of LDS atomics
   uint32_t run_b = 0xffffffffu, run_c = 0;
   unsigned long long run_m = 0;
-  // four strided entries are loaded before any is used (memory-level
-  // parallelism); they are then taken in the same order as one at a time
+  auto take = [&](uint32_t x) {
+    if (PASS > 0 && (x >> hi) != (prefix >> hi)) return;
+    const uint32_t bk = (x >> shift) & mask;
+    if (bk != run_b) {
+      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+      run_b = bk;
+      run_c = 0;
+      run_m = 0;
+    }
+    ++run_c;
+    run_m += fx_mass(x);
+  };
   constexpr int U = 4;
-  for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
-    uint32_t xs[U];
+  if (((uintptr_t)bits & 15) == 0) {
+    // 16-byte loads of four consecutive entries, four loads in flight per
+    // thread; a ragged end of the slice is read entry by entry
+    for (int64_t e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
+      uint4 xs[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? bits[e0 + 256 * u] : 0u;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t x = xs[u];
-      if (e0 + 256 * u >= b) break;
-      if (PASS > 0 && (x >> hi) != (prefix >> hi)) continue;
-      const uint32_t bk = (x >> shift) & mask;
-      if (bk != run_b) {
-        if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
-        run_b = bk;
-        run_c = 0;
-        run_m = 0;
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 1024 * u;
+        if (e + 4 <= b) xs[u] = *(const uint4*)(bits + e);
+        else xs[u] = make_uint4(e < b ? bits[e] : 0u, e + 1 < b ? bits[e + 1] : 0u, e + 2 < b ? bits[e + 2] : 0u, 0u);
       }
-      ++run_c;
-      run_m += fx_mass(x);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 1024 * u;
+        if (e >= b) break;
+        take(xs[u].x);
+        if (e + 1 < b) take(xs[u].y);
+        if (e + 2 < b) take(xs[u].z);
+        if (e + 3 < b) take(xs[u].w);
+      }
+    }
+  } else {
+    // four strided entries are loaded before any is used (memory-level
+    // parallelism); they are then taken in the same order as one at a time
+    for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
+      uint32_t xs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? bits[e0 + 256 * u] : 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (e0 + 256 * u >= b) break;
+        take(xs[u]);
+      }
     }
   }
   if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
