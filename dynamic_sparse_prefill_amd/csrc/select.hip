@@ -996,16 +996,16 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
     const bool split = c.take < c.eq_cnt;
     int base = 0;
     long long eqb = split ? eqrow[row] : 0;
-    // four 64-entry pieces are loaded before any is used, then taken in order
-    for (int k00 = 0; k00 <= qb; k00 += 256) {
-      uint32_t xs[4];
+    // eight 64-entry pieces are loaded before any is used, then taken in order
+    for (int k00 = 0; k00 <= qb; k00 += 512) {
+      uint32_t xs[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int k = k00 + 64 * u + lane;
         xs[u] = k <= qb ? bits[k] : 0u;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int k0 = k00 + 64 * u;
         if (k0 > qb) break;
         const int k = k0 + lane;
