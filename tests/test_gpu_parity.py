@@ -496,3 +496,40 @@ def test_varlen_fp32_and_gqa7():
             assert torch.equal(sel.col_idx[col0:col0 + m], si.col_idx[:m])
             rp0 += hq * nb + 1
             col0 += hq * nb * (nb + 1) // 2
+
+
+def test_varlen_multi_tile_row_scan():
+    """A packed batch whose sequences need different numbers of 4096-row tiles
+    in the row-pointer scan (hq * N_b = 4608, 160 and 2560 rows) and different
+    numbers of pooled-logit row groups: selection outputs, lists and outputs
+    bitwise equal to single calls."""
+    hq, hkv, lens = 16, 4, [36864, 1280, 20480]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    parts = []
+    for i, n in enumerate(lens):
+        cfg = synth.custom_config(f"vl-tiles-{i}", n, hq, hkv, seed=90 + i, conc_frac=0.5)
+        spec = synth.make_spec(cfg)
+        parts.append((spec,) + synth.generate(spec))
+    spec0 = parts[0][0]
+    q = P.to_device(spec0, np.concatenate([p[1] for p in parts], axis=1))
+    k = P.to_device(spec0, np.concatenate([p[2] for p in parts], axis=1))
+    v = P.to_device(spec0, np.concatenate([p[3] for p in parts], axis=1))
+    params = P.params_of(spec0.cfg)
+    o, sel = dsp.crisp_prefill_varlen(q, k, v, cu, params)
+    torch.cuda.synchronize()
+    assert int((sel.route == 0).sum()) > 0 and int((sel.route == 1).sum()) > 0   # both paths exercised
+    rows0, rp0, col0 = 0, 0, 0
+    for i, n in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        nb = n // 128
+        oi, si = dsp.crisp_prefill(q[:, a:b].contiguous(), k[:, a:b].contiguous(), v[:, a:b].contiguous(), params)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, a:b], oi), f"sequence {i}: output differs"
+        assert torch.equal(sel.route[i * hq:(i + 1) * hq], si.route)
+        assert torch.equal(sel.row_ptr[rp0:rp0 + hq * nb + 1], si.row_ptr), f"sequence {i}: row pointers differ"
+        m = int(si.row_ptr[-1])
+        assert torch.equal(sel.col_idx[col0:col0 + m], si.col_idx[:m])
+        assert torch.equal(sel.pv[rows0:rows0 + hq * nb], si.pv)
+        rows0 += hq * nb
+        rp0 += hq * nb + 1
+        col0 += hq * nb * (nb + 1) // 2
