@@ -30,6 +30,9 @@
 namespace crisp {
 
 constexpr int PCH = 16;       // key blocks per score work-group
+// query heads of a KV group per score work-group: they share each K tile the
+// group loads (bf16; the fp32 path's query fragments are twice as large)
+template <typename T> constexpr int proxy_heads() { return sizeof(T) == 2 ? 2 : 1; }
 constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 
 int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
@@ -99,21 +102,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   __shared__ __attribute__((aligned(16))) float red[2][4][HD];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the t-vs-w branches are scalar
-  const int G = hq / hkv;
-  const int chunk = blockIdx.x / hq, rem = blockIdx.x % hq;
-  const int kvh = rem % hkv, hig = rem / hkv, h = kvh * G + hig;
-  const bool kbar_wg = hig == 0;   // block means of K, once per KV head
+  constexpr int HPW = proxy_heads<T>();
+  const int G = hq / hkv, npg = (G + HPW - 1) / HPW;   // head groups per KV head
+  const int chunk = blockIdx.x / (hkv * npg), rem = blockIdx.x % (hkv * npg);
+  const int kvh = rem % hkv, hp = rem / hkv;
+  const int h0 = kvh * G + HPW * hp, nh = min(HPW, G - HPW * hp);   // heads h0 .. h0 + nh - 1
+  const bool kbar_wg = hp == 0;   // block means of K, once per KV head
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
   const int64_t n = (int64_t)nb * BLK;
   if (chunk * PCH >= nb || seq_dense(nb, dense_below_n)) return;
   Q += sp.tok * sq_n;
   K += sp.tok * sk_n;
-  tstat += (sp.rows + (int64_t)h * nb) * BLK;
+  tstat += (sp.rows + (int64_t)h0 * nb) * BLK;   // head h0 + hh at tstat + hh * nb * BLK
   kbar += sp.kvrows * HD;
   const int qrow = 32 * w + l32;
-  typename Tile<T>::QFrag qf;
-  Tile<T>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
+  typename Tile<T>::QFrag qf[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j)
+    if (j < nh) Tile<T>::load_q(qf[j], Q + (int64_t)(h0 + j) * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const int kb0 = chunk * PCH, kb1 = min(nb, kb0 + PCH);
   const T* Kh = K + (int64_t)kvh * sk_h;
   typename Tile<bf16>::KStage stg;
@@ -148,58 +155,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][0][d] + red[0][1][d]) * (1.f / BLK);
       }
     }
-    f32x16 s[4];
-    Tile<T>::st(s, cur, qf, l32, g);
-    const bool last = (kb == nb - 1);
-    if (last) {
-      int lim = qrow;
-      asm volatile("" : "+v"(lim));   // compares stay in this once-per-row branch (no hoisted SGPR masks)
+    // every head of the group against the same K tile
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      if (hh >= nh) break;
+      f32x16 s[4];
+      Tile<T>::st(s, cur, qf[hh], l32, g);
+      const bool last = (kb == nb - 1);
+      if (last) {
+        int lim = qrow;
+        asm volatile("" : "+v"(lim));   // compares stay in this once-per-row branch (no hoisted SGPR masks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * t + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * t + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = pair_max(mx);   // every row keeps at least its diagonal key: finite
+      const float mb = mx * sl2;
+      const int64_t j0 = (int64_t)kb * BLK;
+      const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
+      float lo = 0.f, up = 0.f, an = 0.f;
+      // key c = 32t + .. against this wave's rows 32w .. 32w+31: t < w all lower,
+      // t > w all upper, t = w split per score; interior tiles take the short
+      // path, the last tile and the anchor tiles the general one
+      if (!last && !touches_anchor) {
+        interior_sums(s, sl2, mb, w, l32, g, lo, up);
+      } else {
+        int lim = qrow;
+        asm volatile("" : "+v"(lim));   // as above: the per-score compares stay in this branch
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+          if (t > w && last) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = pair_max(mx);   // every row keeps at least its diagonal key: finite
-    const float mb = mx * sl2;
-    const int64_t j0 = (int64_t)kb * BLK;
-    const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
-    float lo = 0.f, up = 0.f, an = 0.f;
-    // key c = 32t + .. against this wave's rows 32w .. 32w+31: t < w all lower,
-    // t > w all upper, t = w split per score; interior tiles take the short
-    // path, the last tile and the anchor tiles the general one
-    if (!last && !touches_anchor) {
-      interior_sums(s, sl2, mb, w, l32, g, lo, up);
-    } else {
-      int lim = qrow;
-      asm volatile("" : "+v"(lim));   // as above: the per-score compares stay in this branch
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t > w && last) continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = 32 * t + mfma32_row(i, g);
-          const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
-          bool lower = t < w;
-          if (t == w) lower = c <= lim;
-          if (lower) lo += p;
-          else if (!last) up += p;
-          if (touches_anchor && (lower || !last)) {
-            const int64_t j = j0 + c;
-            if (j < w_sink || j >= n - w_local) an += p;
+          for (int i = 0; i < 16; ++i) {
+            const int c = 32 * t + mfma32_row(i, g);
+            const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
+            bool lower = t < w;
+            if (t == w) lower = c <= lim;
+            if (lower) lo += p;
+            else if (!last) up += p;
+            if (touches_anchor && (lower || !last)) {
+              const int64_t j = j0 + c;
+              if (j < w_sink || j >= n - w_local) an += p;
+            }
           }
         }
       }
+      lo = pair_sum(lo);
+      up = pair_sum(up);
+      an = pair_sum(an);
+      if (g == 0) tstat[((int64_t)hh * nb + kb) * BLK + qrow] = make_float4(mx, lo, up, an);
     }
-    lo = pair_sum(lo);
-    up = pair_sum(up);
-    an = pair_sum(an);
-    if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
     if constexpr (PIPE) {
       // the other buffer and the other partials were last read before the
       // previous barrier
@@ -304,7 +316,10 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
                         void* rowstat, void* tiles, float* kbar, hipStream_t s) {
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int nseq = seqs.nseq;
-  const dim3 grid((unsigned)(((nb_max + PCH - 1) / PCH) * hq), (unsigned)nseq);
+  const int G = hq / hkv;
+  const int groups = hkv * ((G + (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()) - 1) /
+                            (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()));
+  const dim3 grid((unsigned)(((nb_max + PCH - 1) / PCH) * groups), (unsigned)nseq);
   if (fp32) {
     proxy_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
                                                    hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
