@@ -576,18 +576,6 @@ hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv
   return hipGetLastError();
 }
 
-static int cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
                             const int32_t* row_ptr, const int32_t* col_idx, int* queue, const SeqTable& seqs,
                             int nb_total, int hq, int hkv, const Strides& st, hipStream_t s) {
@@ -605,7 +593,7 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
     }
   } else {
     const int64_t items = (int64_t)seqs.unit_off[seqs.nseq] * (hq / hkv);
-    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, cu_count())));
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, device_cu_count())));
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
     k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, seqs,
                            nb_total, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
