@@ -22,6 +22,8 @@
 // used by Pooled Estimation.  Grid: blockIdx -> (key chunk, head-in-group,
 // KV head) so the G query heads sharing a K chunk run on one XCD and share
 // its L2.
+#include <algorithm>
+
 #include "common.h"
 #include "lanes.h"
 #include "launch.h"
@@ -29,7 +31,7 @@
 
 namespace crisp {
 
-constexpr int PCH = 16;       // key blocks per score work-group
+constexpr int PCH = 16;       // most key blocks per score work-group (fewer when the grid would be small)
 // query heads of a KV group per score work-group: they share each K tile the
 // group loads (bf16; the fp32 path's query fragments are twice as large)
 template <typename T> constexpr int proxy_heads() { return sizeof(T) == 2 ? 2 : 1; }
@@ -83,7 +85,7 @@ __device__ __forceinline__ void kbar_partials(float (*dst)[HD], const Tile<bf16>
   }
 }
 
-// Scores of the last query block against PCH key blocks; per (tile, row):
+// Scores of the last query block against kpc <= PCH key blocks; per (tile, row):
 // tile max m of the row and the sums of exp(s - m) over the lower part (key
 // column <= row: slash bin N_b-1-kb), the upper part (bin N_b-2-kb) and the
 // anchor windows.
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                                                           float4* __restrict__ tstat, float* __restrict__ kbar,
                                                           const SeqList seqs, int hq, int hkv, int64_t sq_h,
                                                           int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
-                                                          int w_local, int dense_below_n, float sl2) {
+                                                          int w_local, int dense_below_n, float sl2, int kpc) {
   // bf16: two K tiles (the next one is written while the current one is read);
   // fp32 keeps one (its staging would not fit in registers)
   constexpr bool PIPE = sizeof(T) == 2;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
   const int64_t n = (int64_t)nb * BLK;
-  if (chunk * PCH >= nb || seq_dense(nb, dense_below_n)) return;
+  if (chunk * kpc >= nb || seq_dense(nb, dense_below_n)) return;
   Q += sp.tok * sq_n;
   K += sp.tok * sk_n;
   tstat += (sp.rows + (int64_t)h0 * nb) * BLK;   // head h0 + hh at tstat + hh * nb * BLK
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
   for (int j = 0; j < HPW; ++j)
     if (j < nh) Tile<T>::load_q(qf[j], Q + (int64_t)(h0 + j) * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
-  const int kb0 = chunk * PCH, kb1 = min(nb, kb0 + PCH);
+  const int kb0 = chunk * kpc, kb1 = min(nb, kb0 + kpc);
   const T* Kh = K + (int64_t)kvh * sk_h;
   typename Tile<bf16>::KStage stg;
   if constexpr (PIPE) {
@@ -319,15 +321,21 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const int G = hq / hkv;
   const int groups = hkv * ((G + (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()) - 1) /
                             (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()));
-  const dim3 grid((unsigned)(((nb_max + PCH - 1) / PCH) * groups), (unsigned)nseq);
+  // key blocks per work-group: PCH, or fewer so that about two work-groups per
+  // CU exist (short sequences would otherwise run a few long serial chains)
+  const int64_t want = 2 * (int64_t)device_cu_count();
+  const int64_t per_chunk = (int64_t)groups * nseq;
+  const int64_t chunks = (want + per_chunk - 1) / per_chunk;
+  const int kpc = (int)std::max<int64_t>(1, std::min<int64_t>(PCH, (nb_max + chunks - 1) / chunks));
+  const dim3 grid((unsigned)(((nb_max + kpc - 1) / kpc) * groups), (unsigned)nseq);
   if (fp32) {
     proxy_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
                                                    hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
-                                                   dense_below_n, sl2);
+                                                   dense_below_n, sl2, kpc);
   } else {
     proxy_tiles_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar, seqs, hq,
                                                   hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
-                                                  dense_below_n, sl2);
+                                                  dense_below_n, sl2, kpc);
   }
   const int nchunk = proxy_chunks(nb_max);
   const unsigned vheads = (unsigned)(nseq * hq);
