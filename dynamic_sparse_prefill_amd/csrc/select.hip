@@ -561,16 +561,17 @@ constexpr int KT_PITCH = 132; // LDS pitch (floats) of a key-block-mean row: con
 // during the MFMAs) and shared by the work-group's waves.  Each tile is turned
 // row-major through LDS and stored with whole 128-byte row segments; the
 // segment's row max and sum of exp(L - max) go to `part` for the softmax.
-// The item's row group rg counts from the top of the sequence's triangle.
+// One item: row group rg_from_end counted from the bottom of the sequence's
+// triangle (0 = the longest rows), segment cs, virtual head vh.
 __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], float (&tileT)[PE_RB][32][33],
                                                const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                float* __restrict__ P, float2* __restrict__ part, const SeqList& seqs,
-                                               int hq, int hkv, int nseg, float scale, int vh, int rg_top, int cs) {
+                                               int hq, int hkv, int nseg, float scale, int vh, int rg_from_end, int cs) {
   const int h = vh % hq;
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
   const int nb = sp.nb;
   const int nrb = (nb + 31) / 32, nrg = (nrb + PE_RB - 1) / PE_RB;
-  const int rg = nrg - 1 - rg_top;
+  const int rg = nrg - 1 - rg_from_end;
   if (rg < 0) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int rb = rg * PE_RB + w;
@@ -620,10 +621,10 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
     if (ct + 1 < ct1) kfetch(ct + 1);
     if (ct < ntile) {
       // two independent chains (d slices 4i..4i+1 and 4i+2..4i+3) keep the
-      // matrix unit fed from one wave; summed at the end
-      // matrix operands read one step ahead of the four MFMAs that use them
-      // (the order is pinned: left to itself the compiler waits on each read
-      // just before its use)
+      // matrix unit fed from one wave, summed at the end; the operands are
+      // read one step ahead of the four MFMAs that use them (the order is
+      // pinned: left to itself the compiler waits on each read just before
+      // its use)
       f32x16 acc = {}, acc2 = {};
       const float* ka = &kt[buf][l32 * KT_PITCH + 64 * g];
       __builtin_amdgcn_sched_barrier(0);
