@@ -19,9 +19,9 @@
 // rescales the stored sums by exp(m - M) / L and adds them over the rows.
 // Every reduction has a fixed order (no float atomics), so the scores are
 // bit-reproducible.  The score pass also writes the block means of K (K-bar)
-// used by Pooled Estimation.  Grid: blockIdx -> (key chunk, head-in-group,
-// KV head) so the G query heads sharing a K chunk run on one XCD and share
-// its L2.
+// used by Pooled Estimation.  Grid: blockIdx -> (key chunk, group of query
+// heads of a KV group, KV head) so the work-groups sharing a K chunk run on
+// one XCD and share its L2; the heads of a group share each K tile in LDS.
 #include <algorithm>
 
 #include "common.h"
