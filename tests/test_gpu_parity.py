@@ -137,7 +137,7 @@ def test_strided_layout_matches_contiguous():
 
 # ------------------------------------------------------------------ small mixed layers: selection in full
 
-@pytest.mark.parametrize("n,hq,hkv,seed", [(8192, 8, 2, 21), (1664, 7, 1, 22), (384, 2, 1, 23)])
+@pytest.mark.parametrize("n,hq,hkv,seed", [(8192, 8, 2, 21), (1664, 7, 1, 22), (384, 2, 1, 23), (2048, 4, 4, 24)])
 def test_small_layer_selection_and_output(n, hq, hkv, seed):
     cfg = synth.custom_config("small", n, hq, hkv, seed=seed, conc_frac=0.5)
     spec = synth.make_spec(cfg)
