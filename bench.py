@@ -293,8 +293,8 @@ def measured_peaks(torch):
                    "second of two ~0.4 s launches; HBM: 2 GiB device copy, read + write bytes"}
 
 
-def run_layer(cfg_id, steps, warmup, torch, dsp, synth, with_dense=True, compare=False):
-    spec = synth.make_spec(synth.CONFIGS[cfg_id])
+def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=False):
+    spec = synth.make_spec(layer)
     cfg = spec.cfg
     t = time.time()
     Q, K, V = synth.generate(spec, threads=16)
@@ -408,7 +408,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes (MFMA loop, copy)")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--workload", type=int, default=4, help="layer id: 1 llama-32k, 2 llama-128k, 3 qwen-128k, 4 llama-512k")
+    ap.add_argument("--workload", default="llama3.1-8b-512k",
+                    choices=["llama3.1-8b-32k", "llama3.1-8b-128k", "qwen2.5-7b-128k", "llama3.1-8b-512k"],
+                    help="the layer timed")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline (counter-collection runs)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the decision-rule comparison (median floor, universal config, FlexPrefill)")
@@ -431,7 +433,7 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, torch)
-    main_res, spec, route = run_layer(args.workload, args.steps, args.warmup, torch, dsp, synth,
+    main_res, spec, route = run_layer(synth.WORKLOADS[args.workload], args.steps, args.warmup, torch, dsp, synth,
                                       with_dense=not args.no_dense, compare=not args.no_compare)
     log("[bench]", json.dumps(main_res))
     extra = {}
@@ -440,10 +442,10 @@ def main():
     if not args.no_varlen:
         extra["varlen"] = varlen_batches(dsp, torch, synth)
     if not args.no_extra:
-        for cid in (2, 3):
-            if cid == args.workload:
+        for name in ("llama3.1-8b-128k", "qwen2.5-7b-128k"):
+            if name == args.workload:
                 continue
-            r, _, _ = run_layer(cid, max(2, args.steps), 1, torch, dsp, synth)
+            r, _, _ = run_layer(synth.WORKLOADS[name], max(2, args.steps), 1, torch, dsp, synth)
             extra[r["workload"]] = {k: r[k] for k in ("ms", "dense_ms", "speedup", "select_ms", "sparse_attn_ms",
                                                       "density", "vs_heads", "pe_heads", "sparse_tflops",
                                                       "dense_tflops", "selection_roofline")}
@@ -486,7 +488,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "frac_of_measured": round(ach / peaks["mfma_bf16_tflops"], 4) if peaks else None,
-                     "traffic": profiled_traffic() if args.workload == 4 else None,
+                     "traffic": profiled_traffic() if args.workload == "llama3.1-8b-512k" else None,
                      "kernel": "fa_bf16_kernel<false> (sparse attention; event time includes the V re-layout)",
                      "flops_per_launch": main_res["tiles"] * TILE_FLOPS},
         "dense_roofline": ({"achieved": round(main_res["dense_tflops"], 2),

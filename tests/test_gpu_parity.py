@@ -42,7 +42,7 @@ def _lists_fn(sel, nb):
 # ------------------------------------------------------------------ tiny fp32 layer, everything in full
 
 def test_tiny_fp32_layer_full():
-    spec = synth.make_spec(synth.CONFIGS[0])
+    spec = synth.make_spec(synth.TINY_FP32_4K)
     cfg = spec.cfg
     Q, K, V = synth.generate(spec)
     p = P.params_of(cfg)
@@ -276,8 +276,8 @@ def test_output_is_causal():
 
 # ------------------------------------------------------------------ the Llama / Qwen layers
 
-def _big_layer(cid, heads_fid, nblk, seed_blocks):
-    spec = synth.make_spec(synth.CONFIGS[cid])
+def _big_layer(layer, heads_fid, nblk, seed_blocks):
+    spec = synth.make_spec(layer)
     cfg = spec.cfg
     Q, K, V = P.load_layer(spec)
     p = P.params_of(cfg)
@@ -304,22 +304,22 @@ def _big_layer(cid, heads_fid, nblk, seed_blocks):
 
 
 def test_llama_32k_layer():
-    _big_layer(1, 3, 8, 1)
+    _big_layer(synth.LLAMA_32K, 3, 8, 1)
 
 
 @pytest.mark.timeout(900)
 def test_llama_128k_layer():
-    _big_layer(2, 2, 6, 2)
+    _big_layer(synth.LLAMA_128K, 2, 6, 2)
 
 
 @pytest.mark.timeout(900)
 def test_qwen_128k_layer():
-    _big_layer(3, 2, 6, 3)
+    _big_layer(synth.QWEN_128K, 2, 6, 3)
 
 
 @pytest.mark.timeout(1200)
 def test_llama_512k_layer():
-    _big_layer(4, 1, 4, 4)
+    _big_layer(synth.LLAMA_512K, 1, 4, 4)
 
 
 # ------------------------------------------------------------------ variants: JSD router, median floor, coverage budget
@@ -384,7 +384,7 @@ def test_variant_min_blocks_and_gamma_sweep():
 def test_flexprefill_configuration_llama_128k():
     """FlexPrefill's pair of rules (JSD router, coverage budget at gamma 0.95)
     on the Llama 128k layer: decisions in full, sampled outputs."""
-    spec = synth.make_spec(synth.CONFIGS[2])
+    spec = synth.make_spec(synth.LLAMA_128K)
     cfg = spec.cfg
     Q, K, V = P.load_layer(spec)
     q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)

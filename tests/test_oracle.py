@@ -309,7 +309,7 @@ def test_select_head_on_tiny_generated_layer():
     """Tiny fp32 case: head 0 (sink + recency + 3 needles) routes to VS and keeps
     its needle blocks; head 1 (diffuse) routes to PE."""
     from workloads import synth
-    spec = synth.make_spec(synth.CONFIGS[0])
+    spec = synth.make_spec(synth.TINY_FP32_4K)
     cfg = spec.cfg
     Q, K, V = synth.generate(spec)
     r0 = O.select_head(Q[0].astype(np.float64), K[0].astype(np.float64), 128, 128, 128, cfg.tau, cfg.alpha, cfg.gamma)
@@ -450,7 +450,7 @@ def test_jsd_router_threshold_and_variants_on_tiny_layer():
     """JSD routing is VS iff JSD >= tau, so the VS set shrinks as tau grows;
     the variants produce valid lists (ascending, anchors present, causal)."""
     from workloads import synth
-    spec = synth.make_spec(synth.CONFIGS[0])
+    spec = synth.make_spec(synth.TINY_FP32_4K)
     cfg = spec.cfg
     Q, K, V = synth.generate(spec)
     js = []

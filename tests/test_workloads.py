@@ -27,13 +27,13 @@ def test_generation_is_deterministic_and_row_ranges_regenerate():
 
 
 def test_head_mix_and_planting():
-    spec = synth.make_spec(synth.CONFIGS[1])
+    spec = synth.make_spec(synth.LLAMA_32K)
     assert spec.concentrated.sum() == 19
-    spec3 = synth.make_spec(synth.CONFIGS[3])
+    spec3 = synth.make_spec(synth.QWEN_128K)
     assert spec3.concentrated.sum() == round(0.45 * 28)
     for g in range(8):
         assert 2 <= len(spec.needle_blocks[g]) <= 8
         assert all(1 <= b <= 256 - 2 for b in spec.needle_blocks[g])
-    lit = synth.make_spec(synth.CONFIGS[1], compensate=False)
+    lit = synth.make_spec(synth.LLAMA_32K, compensate=False)
     assert np.all(lit.c < spec.c) and np.all(lit.rho < spec.rho)
     assert np.allclose(spec.c - lit.c, np.log(8) * np.sqrt(128) / 4, atol=1e-5)

@@ -81,16 +81,17 @@ class LayerConfig:
         return self.n // BLOCK
 
 
-CONFIGS = {
-    0: LayerConfig("tiny-fp32-4k", 4096, 2, 2, "fp32", seed=0, tiny=True,
-                   sink=(6.0, 6.0), needles=(3, 3)),
-    1: LayerConfig("llama3.1-8b-32k", 32768, 32, 8, "bf16", seed=1),
-    2: LayerConfig("llama3.1-8b-128k", 131072, 32, 8, "bf16", seed=2),
-    3: LayerConfig("qwen2.5-7b-128k", 131072, 28, 4, "bf16", seed=3,
-                   conc_frac=0.45, sink=(3.0, 6.0), recency=1.5),
-    4: LayerConfig("llama3.1-8b-512k", 524288, 32, 8, "bf16", seed=4,
-                   needles=(2, 16)),
-}
+TINY_FP32_4K = LayerConfig("tiny-fp32-4k", 4096, 2, 2, "fp32", seed=0, tiny=True,
+                           sink=(6.0, 6.0), needles=(3, 3))
+LLAMA_32K = LayerConfig("llama3.1-8b-32k", 32768, 32, 8, "bf16", seed=1)
+LLAMA_128K = LayerConfig("llama3.1-8b-128k", 131072, 32, 8, "bf16", seed=2)
+QWEN_128K = LayerConfig("qwen2.5-7b-128k", 131072, 28, 4, "bf16", seed=3,
+                        conc_frac=0.45, sink=(3.0, 6.0), recency=1.5)
+LLAMA_512K = LayerConfig("llama3.1-8b-512k", 524288, 32, 8, "bf16", seed=4,
+                         needles=(2, 16))
+
+# the named layers, by name
+WORKLOADS = {c.name: c for c in (TINY_FP32_4K, LLAMA_32K, LLAMA_128K, QWEN_128K, LLAMA_512K)}
 
 
 def custom_config(name, n, hq, hkv, dtype="bf16", seed=0, **kw) -> LayerConfig:
