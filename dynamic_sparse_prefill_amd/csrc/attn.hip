@@ -17,10 +17,16 @@
 //    re-laid out once per call as per-block transposed tiles [d][key] so that
 //    the tile copy to LDS is a plain coalesced 32 KB copy.
 //  * One work-group = one head x two adjacent query blocks (256 rows, 8
-//    waves).  K and V^T tiles go straight from global memory to LDS
-//    (global_load_lds, no staging registers), XOR-swizzled for conflict-free
-//    16-byte reads, double-buffered so the next block streams in during a
-//    whole iteration; one barrier per key block.
+//    waves).  K and V^T tiles go straight from global memory to LDS (buffer
+//    loads with the LDS bit, no staging registers), XOR-swizzled for
+//    conflict-free 16-byte reads, double-buffered so the next block streams
+//    in during a whole iteration; one barrier per key block.
+//  * Operand fragments are read from LDS one MFMA step ahead (the reads of
+//    step c + 1 are in flight while the MFMAs of step c run), and every MFMA
+//    waits only for its own fragment.  The compiler can count the LDS reads
+//    that precisely only while the copy in flight is a buffer (MUBUF) load:
+//    a global (FLAT) copy into LDS makes it wait for every outstanding LDS
+//    read at each use.
 //  * Scheduling: a persistent grid (one work-group per CU) pulls (pair, head)
 //    items from 8 per-XCD queues, two KV groups at a time, longest rows
 //    first, stealing from other queues at the end: every CU stays busy
@@ -75,7 +81,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // gfx9 s_waitcnt immediates: wait for vector-memory count <= N only.
 constexpr int WAIT_VM0 = 0x0F70;
-constexpr int WAIT_VM8 = 0x0F78;
 
 __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -93,8 +98,10 @@ __device__ __forceinline__ float pair_max(float x) {
 // A 128-row x 256-byte tile goes to LDS as 16-byte chunks, chunk c of row r at
 // physical chunk c ^ (r & 15): 16 lanes reading the same logical chunk of 16
 // consecutive rows hit 16 different bank groups.  With 8 waves, wave w copies
-// rows 16w..16w+15 with 4 direct global->LDS loads of 1 KB (4 rows) each; lane
-// L of load i fills row 16w + 4i + L/16, physical chunk L%16.
+// rows 16w..16w+15 with 4 buffer loads of 1 KB (4 rows) each that write LDS
+// directly; lane L of load i fills row 16w + 4i + L/16, physical chunk L%16.
+// The buffer resource is based at the tile and spans exactly its bytes, so an
+// offset outside the tile would read zeros rather than other memory.
 struct TileCopy {
   uint32_t off[4];
   __device__ void init(int wu, int lane, uint32_t row_bytes) {
@@ -105,65 +112,19 @@ struct TileCopy {
       off[i] = (uint32_t)r * row_bytes + ((uint32_t)(pc ^ (r & 15)) << 4);
     }
   }
-  __device__ void issue(const char* src, uint32_t lds, int wu) const {
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* dst, int wu) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // keep only the 32-bit offset live across the loop: the 64-bit address is
-      // formed right before the copy instead of being hoisted (register pressure)
-      uint32_t o = off[i];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds((const void*)(src + o), (lds_void*)(uintptr_t)(lds + (16 * wu + 4 * i) * 256),
-                                       16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (16 * wu + 4 * i) * 256), 16, off[i], 0, 0, 0);
   }
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+// buffer resource over `bytes` bytes at p (raw: no stride, no swizzle)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, bytes, 0x00020000);
 }
 
-// Four 16-byte LDS reads at addr + OFF + {0, 8, 16, 24} KB (rows 0, 32, 64, 96
-// of a tile for this lane), completed inside the same asm block.  Written by
-// hand: while a global->LDS copy is in flight the compiler can only follow its
-// own LDS reads with a full lgkmcnt(0) wait, so grouping the reads of a step
-// under one wait is done here explicitly.  The outputs are early-clobber: a read's
-// result may land while later reads of the block still need the address
-// registers, so no output may share a register with an address.
-template <int OFF>
-__device__ __forceinline__ void lds_read4(bf16x8 (&a)[4], uint32_t addr) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%5\n\t"
-      "ds_read_b128 %1, %4 offset:%6\n\t"
-      "ds_read_b128 %2, %4 offset:%7\n\t"
-      "ds_read_b128 %3, %4 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-      : "v"(addr), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
-      : "memory");
-}
-
-// Eight 16-byte LDS reads: rows 0/32/64/96 at a0 + OFF and at a1 + OFF, completed
-// inside the block.  Issued right behind eight queued MFMAs, whose execution
-// (~256 cycles) covers the LDS latency.
-template <int OFF>
-__device__ __forceinline__ void lds_read8(bf16x8 (&a)[4], bf16x8 (&b)[4], uint32_t a0, uint32_t a1) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%10\n\t"
-      "ds_read_b128 %1, %8 offset:%11\n\t"
-      "ds_read_b128 %2, %8 offset:%12\n\t"
-      "ds_read_b128 %3, %8 offset:%13\n\t"
-      "ds_read_b128 %4, %9 offset:%10\n\t"
-      "ds_read_b128 %5, %9 offset:%11\n\t"
-      "ds_read_b128 %6, %9 offset:%12\n\t"
-      "ds_read_b128 %7, %9 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 8192), "i"(OFF + 16384), "i"(OFF + 24576)
-      : "memory");
-}
-
-constexpr int TILE_BYTES = BLK * 256;        // one K or V^T tile in LDS
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V^T
+constexpr int TILE_BYTES = BLK * 256;  // one K or V^T tile in LDS
 
 // Work queues.  The kernel is persistent (one work-group per CU).  A unit of
 // work is one (query-block pair, KV head) with its G query heads, whose items
@@ -263,7 +224,7 @@ struct PairCursor {
 // iteration, with one barrier per key block.
 template <bool DENSE>
 __device__ __forceinline__ void fa_bf16_item(
-    char* smem, int pair, int kvh, int h,
+    char* sK0, char* sV0, char* sK1, char* sV1, int pair, int kvh, int h,
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int hq, int hkv,
     int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int64_t so_h, int64_t so_n, int64_t vt_h, float sl2) {
@@ -304,66 +265,72 @@ __device__ __forceinline__ void fa_bf16_item(
   const int qrow = 32 * wq + l32;
   bf16* orow = O + (int64_t)h * so_h + (int64_t)(qmine * BLK + qrow) * so_n;
 
-  const uint32_t lbase = lds_addr(smem);
   const uint32_t krow = (uint32_t)(sk_n * 2);
   const char* Kh = (const char*)(K + (int64_t)kvh * sk_h);
   const char* Vh = (const char*)(Vt + (int64_t)kvh * vt_h);
   TileCopy kc, vc;
   kc.init(w, lane, krow);
   vc.init(w, lane, 256);
-  auto issue = [&](int kb, int stage) {
-    const uint32_t sb = lbase + stage * STAGE_BYTES;
-    kc.issue(Kh + (int64_t)kb * BLK * krow, sb, w);
-    vc.issue(Vh + (int64_t)kb * (BLK * HD * 2), sb + TILE_BYTES, w);
+  const int kspan = (int)((BLK - 1) * krow + 256);
+  auto issue = [&](int kb, char* dK, char* dV) {
+    kc.issue(tile_rsrc(Kh + (int64_t)kb * BLK * krow, kspan), dK, w);
+    vc.issue(tile_rsrc(Vh + (int64_t)kb * (BLK * HD * 2), BLK * HD * 2), dV, w);
   };
 
   bool a0, b0;
   int kb = next_block(a0, b0);
-  if (kb >= 0) issue(kb, 0);
+  if (kb >= 0) issue(kb, sK0, sV0);
   bool a1 = false, b1 = false;
   int kb1 = kb >= 0 ? next_block(a1, b1) : -1;
 
   Tile<bf16>::QFrag qf;
   if (rows_ok) Tile<bf16>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)(qmine * BLK + qrow) * sq_n, g);
-  // LDS address of logical chunk 2c + g of this lane's row in the K tile of stage 0
   uint32_t kx[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) kx[c] = lbase + l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
+  for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
 
   f32x16 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
   float m = -1e30f, l = 0.f;
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-  int stage = 0;
 
-  while (kb >= 0) {
+  // One key block with its tiles in (cK, cV) while the next block's are copied
+  // into (nK, nV).  The stages are separate LDS arrays named at compile time
+  // (the loop below alternates two inlined copies of the step), so the
+  // compiler can tell the reads of one stage from the copy into the other.
+  auto step = [&](const char* cK, const char* cV, char* nK, char* nV) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);       // this wave's share of the tiles of kb has landed
     block_barrier();                            // all of them have; every wave left the other stage
     // the list lookup comes before the copy is issued: a window refill then has
     // nothing in flight to wait for (all loads completed at the wait above)
     bool a2 = false, b2 = false;
     const int kb2 = kb1 >= 0 ? next_block(a2, b2) : -1;
-    if (kb1 >= 0) issue(kb1, stage ^ 1);
+    if (kb1 >= 0) issue(kb1, nK, nV);
     const bool active = half ? b0 : a0;
     if (active) {
-      const uint32_t so = stage * STAGE_BYTES;
       f32x16 s[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = f32x16{};
-      bf16x8 fa[4], fb[4];
-      lds_read8<0>(fa, fb, kx[0] + so, kx[1] + so);
+      // Operand fragments are double-buffered in source order: the reads of
+      // step c + 1 are issued before the MFMAs of step c (the scheduling
+      // barriers keep that order), so each MFMA waits only for a read issued
+      // four MFMAs earlier.  The last step reads the first V^T fragments.
+      bf16x8 fk[2][4], fv[2][4];
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) {
+      for (int t = 0; t < 4; ++t) fk[0][t] = *(const bf16x8*)(cK + kx[0] + 8192 * t);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fa[t], qf.v[c], s[t]);
+      for (int c = 0; c < 8; ++c) {
+        if (c + 1 < 8) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fb[t], qf.v[c + 1], s[t]);
+          for (int t = 0; t < 4; ++t) fk[(c + 1) & 1][t] = *(const bf16x8*)(cK + kx[c + 1] + 8192 * t);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) fv[0][u] = *(const bf16x8*)(cV + kx[0] + 8192 * u);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 < 8)
-          lds_read8<0>(fa, fb, kx[c + 2] + so, kx[c + 3] + so);
-        else  // first V^T fragments, behind the tail of the score MFMAs
-          lds_read8<TILE_BYTES>(fa, fb, kx[0] + so, kx[1] + so);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = mfma_bf16(fk[c & 1][t], qf.v[c], s[t]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kb == qmine) {  // diagonal tile: keys after the query are masked
@@ -396,7 +363,7 @@ __device__ __forceinline__ void fa_bf16_item(
       const float mb = m * sl2;
       // P in bf16, already in the B-operand order of the O^T MFMAs; the row sum
       // is taken over the same rounded values (v_dot2 with (1, 1)).  P for key
-      // chunks mm+2, mm+3 is formed while the MFMAs of chunks mm, mm+1 run.
+      // chunk mm + 2 is formed while the MFMAs of chunk mm run.
       bf16x8 pb[8];
       auto form_p = [&](int mm) {
 #pragma unroll
@@ -412,24 +379,25 @@ __device__ __forceinline__ void fa_bf16_item(
       form_p(0);
       form_p(1);
 #pragma unroll
-      for (int mm = 0; mm < 8; mm += 2) {
+      for (int mm = 0; mm < 8; ++mm) {
+        if (mm + 1 < 8) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fa[u], pb[mm], acc[u]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fb[u], pb[mm + 1], acc[u]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (mm + 2 < 8) {
-          form_p(mm + 2);
-          form_p(mm + 3);
-          __builtin_amdgcn_sched_barrier(0);
-          lds_read8<TILE_BYTES>(fa, fb, kx[mm + 2] + so, kx[mm + 3] + so);
+          for (int u = 0; u < 4; ++u) fv[(mm + 1) & 1][u] = *(const bf16x8*)(cV + kx[mm + 1] + 8192 * u);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_bf16(fv[mm & 1][u], pb[mm], acc[u]);
+        if (mm + 2 < 8) form_p(mm + 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     kb = kb1; a0 = a1; b0 = b1;
     kb1 = kb2; a1 = a2; b1 = b2;
-    stage ^= 1;
+  };
+  while (kb >= 0) {
+    step(sK0, sV0, sK1, sV1);
+    if (kb < 0) break;
+    step(sK1, sV1, sK0, sV0);
   }
   if (!rows_ok) return;
   l += __shfl_xor(l, 32, 64);
@@ -453,7 +421,11 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue,
     const SeqTable sq, int nb_total, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n,
     int64_t so_h, int64_t so_n, float sl2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  // two stages of (K, V^T) tiles, each stage tile its own array
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
   __shared__ int s_item;
   const int home = blockIdx.x % NQUEUE;
   const int64_t vt_h = (int64_t)nb_total * (BLK * HD);
@@ -467,7 +439,7 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
       int seq, pair, kvh, h;
       if (!queue_item(x, s_item, sq, hq, hkv, seq, pair, kvh, h)) break;
       const int64_t t0 = sq.tok[seq];
-      fa_bf16_item<DENSE>(smem, pair, kvh, h, Q + t0 * sq_n, K + t0 * sk_n, Vt + t0 * HD, O + t0 * so_n,
+      fa_bf16_item<DENSE>(sK0, sV0, sK1, sV1, pair, kvh, h, Q + t0 * sq_n, K + t0 * sk_n, Vt + t0 * HD, O + t0 * so_n,
                           row_ptr + sq.rp[seq], col_idx + sq.col[seq], sq.nb[seq], hq, hkv, sq_h, sq_n, sk_h,
                           sk_n, so_h, so_n, vt_h, sl2);
     }

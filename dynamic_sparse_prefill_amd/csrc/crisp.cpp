@@ -30,6 +30,9 @@ constexpr int HD = 128;    // head dim d
 namespace {
 
 constexpr int64_t MAX_NB = 32768;
+// largest token stride (elements): a 128-row K tile then spans under 2^31 bytes, the range of
+// the attention kernel's buffer resources and tile offsets
+constexpr int64_t MAX_TOKEN_STRIDE = int64_t(1) << 22;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -46,6 +49,9 @@ int check_shape(const crisp_shape* s) {
   for (int64_t x : st)
     if (x < 0 || x % 8) return CRISP_E_ARG;
   if (s->sq_n < HD || s->sk_n < HD || s->sv_n < HD || s->so_n < HD) return CRISP_E_ARG;
+  if (s->sq_n > MAX_TOKEN_STRIDE || s->sk_n > MAX_TOKEN_STRIDE || s->sv_n > MAX_TOKEN_STRIDE ||
+      s->so_n > MAX_TOKEN_STRIDE)
+    return CRISP_E_UNSUPPORTED;
   // worst-case list size must fit int32 row pointers
   const int64_t nb = s->n / BLK;
   if ((int64_t)s->hq * nb * (nb + 1) / 2 > 0x7fffffffLL) return CRISP_E_UNSUPPORTED;

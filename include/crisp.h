@@ -31,8 +31,9 @@
  *     pointers must be 16-byte aligned.  Q and O have hq heads, K and V have
  *     hkv heads; query head h reads KV head h / (hq / hkv).
  *   - Supported: d == 128, block == 128, n a positive multiple of 128 with
- *     n / 128 <= 32768, hq a multiple of hkv.  dtype bf16 (compute: bf16
- *     MFMA, fp32 softmax and accumulation) or fp32 (fp32 MFMA throughout).
+ *     n / 128 <= 32768, token strides <= 2^22 elements, hq a multiple of
+ *     hkv.  dtype bf16 (compute: bf16 MFMA, fp32 softmax and accumulation) or
+ *     fp32 (fp32 MFMA throughout).
  *   - Calls on different streams may overlap as long as their output and
  *     workspace buffers are distinct.
  */

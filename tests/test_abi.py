@@ -55,6 +55,9 @@ def test_workspace_and_capacity_queries():
     # invalid shapes and parameters report zero
     assert dsp.select_workspace_bytes(_shape(d=64), p) == 0
     assert dsp.col_capacity(_shape(n=1000)) == 0
+    huge = _shape()
+    huge.sk_n = (1 << 22) + 8                         # token stride beyond the supported range
+    assert dsp.select_workspace_bytes(huge, p) == 0
     bad = dsp.CrispParams(gamma=0.0)
     assert dsp.workspace_bytes(s, bad) == 0
 
