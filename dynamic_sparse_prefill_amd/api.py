@@ -7,7 +7,7 @@ call fails, an exception is raised.
 
 Tensor layout: q, o [hq, n, 128]; k, v [hkv, n, 128]; dtype torch.bfloat16 or
 torch.float32; the last axis contiguous; any head / token strides that are
-multiples of 8 elements.
+multiples of 8 elements, token strides at most 2^22 elements.
 """
 from __future__ import annotations
 
