@@ -174,7 +174,8 @@ def compare_rules(cfg, q, k, v, dsp, torch, steps, dense_ms):
 
 def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=3):
     """CRISP vs dense ms per layer on Llama-shaped layers of growing length (4k-64k):
-    where sparse prefill starts to pay (the length gate)."""
+    where sparse prefill starts to pay (the length gate).  CRISP is timed as
+    enqueued call by call and as one HIP graph replay of the same prefill."""
     res = {}
     for n in ns:
         cfg = synth.custom_config(f"llama-shape-{n // 1024}k", n, 32, 8, seed=7, conc_frac=0.6)
@@ -186,14 +187,21 @@ def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=
         o = torch.empty_like(q)
         sel = dsp.new_selection(q, k, diagnostics=False)
         ws = torch.empty(dsp.workspace_bytes(dsp.make_shape(q, k, v, o), p), dtype=torch.uint8, device="cuda")
-        ms = timed(lambda: dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws), steps, 2, torch)
+        reps = max(steps, 20) if n <= 16384 else steps          # short layers: enough calls to time
+        ms = timed(lambda: dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws), reps, 2, torch)
+        # the same prefill captured once in a HIP graph and replayed (no per-kernel launch cost)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dsp.crisp_prefill(q, k, v, p, sel=sel, o=o, ws=ws)
+        gms = timed(graph.replay, reps, 2, torch)
         aws = ws[dsp.select_workspace_bytes(dsp.make_shape(q, k, v, o), p):]
-        dms = timed(lambda: dsp.crisp_dense_attn(q, k, v, o=o, ws=aws), steps, 2, torch)
+        dms = timed(lambda: dsp.crisp_dense_attn(q, k, v, o=o, ws=aws), reps, 2, torch)
         nb = n // 128
-        res[n] = {"crisp_ms": round(ms, 3), "dense_ms": round(dms, 3), "speedup": round(dms / ms, 3),
+        res[n] = {"crisp_ms": round(ms, 3), "crisp_graph_ms": round(gms, 3), "dense_ms": round(dms, 3),
+                  "speedup": round(dms / ms, 3), "speedup_graph": round(dms / gms, 3),
                   "density": round(int(sel.row_ptr[-1].item()) / (32 * nb * (nb + 1) // 2), 4)}
         log(f"[bench] length {n}: {res[n]}")
-        del q, k, v, o, sel, ws, aws
+        del graph, q, k, v, o, sel, ws, aws
         torch.cuda.empty_cache()
     return res
 
