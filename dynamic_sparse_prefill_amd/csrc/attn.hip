@@ -137,10 +137,14 @@ constexpr int TILE_BYTES = BLK * 256;  // one K or V^T tile in LDS
 // depends on the placement; every item is taken exactly once.
 
 // t-th item of queue x -> (sequence, pair, kvh, h); false once the queue is
-// exhausted.  Units are numbered sequence after sequence; within a sequence,
-// KV groups go two at a time (2j, 2j+1 alternating unit by unit, longest rows
-// first; a last odd group alone), so all queues stream the K/V of the same
-// two groups at any moment: a working set that stays in the last-level cache.
+// exhausted.  Units are numbered sequence after sequence.  Within a sequence
+// whose K and V are larger than the last-level cache, KV groups go two at a
+// time (2j, 2j+1 alternating unit by unit, longest rows first; a last odd
+// group alone), so all queues stream the K/V of the same two groups at any
+// moment: a working set that stays in that cache.  When K and V fit in it
+// (sq.pair_major), units go pair by pair over all KV groups, longest rows
+// first: plain longest-first packing, which evens out the end of a short
+// launch (8k-64k tokens: 5-12% faster; at 512k it costs 8%).
 __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int hkv, int& seq, int& pair, int& kvh,
                                   int& h) {
   const int G = hq / hkv;
@@ -150,8 +154,14 @@ __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int 
   while (u >= sq.unit_off[i + 1]) ++i;
   const int v = u - sq.unit_off[i];
   const int np = (sq.nb[i] + 1) >> 1;
-  const int gp = v / (2 * np), r = v % (2 * np);
   seq = i;
+  if (sq.pair_major) {
+    kvh = v % hkv;
+    pair = np - 1 - v / hkv;
+    h = kvh * G + t % G;
+    return true;
+  }
+  const int gp = v / (2 * np), r = v % (2 * np);
   if (2 * gp + 1 < hkv) {
     kvh = 2 * gp + (r & 1);
     pair = np - 1 - (r >> 1);
@@ -566,8 +576,14 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
   } else {
     const int64_t items = (int64_t)seqs.unit_off[seqs.nseq] * (hq / hkv);
     const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, device_cu_count())));
+    // unit order: longest-first packing when every sequence's K and V fit in
+    // the 256 MB last-level cache, two KV groups at a time otherwise
+    SeqTable t = seqs;
+    int64_t nb_max = 0;
+    for (int i = 0; i < t.nseq; ++i) nb_max = std::max<int64_t>(nb_max, t.nb[i]);
+    t.pair_major = 2 * (int64_t)hkv * nb_max * BLK * HD * 2 <= (int64_t(256) << 20);
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
-    k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, seqs,
+    k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, t,
                            nb_total, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
   }
   return hipGetLastError();

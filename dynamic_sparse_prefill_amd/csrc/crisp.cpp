@@ -234,6 +234,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
 SeqTable single_sequence(int nb, int hkv) {
   SeqTable t;
   t.nseq = 1;
+  t.pair_major = 0;
   t.unit_off[0] = 0;
   t.unit_off[1] = ((nb + 1) / 2) * hkv;
   t.nb[0] = nb;
@@ -401,6 +402,7 @@ int crisp_prefill_varlen(const crisp_shape* shape, int32_t nseq, const int64_t* 
   if (st) return st;
   SeqTable seqs;
   seqs.nseq = nseq;
+  seqs.pair_major = 0;
   seqs.unit_off[0] = 0;
   for (int i = 0; i < nseq; ++i) {
     const int64_t nb = P.len[i] / BLK;

@@ -29,6 +29,7 @@ struct SeqTable {
   int64_t tok[MAX_SEQ];
   int64_t rp[MAX_SEQ];
   int64_t col[MAX_SEQ];
+  int pair_major;              // set by the attention launcher: unit order (see queue_item in attn.hip)
 };
 
 // Sequences of a selection batch (a single prefill is one sequence), by
