@@ -21,12 +21,17 @@ pages it follows:
                kept iff its mass exceeds alpha * mu; both directions (vertical
                = column means, slash = diagonal means) are thresholded
                separately and unioned.
-* [rcap.io summary, per-head pseudo-code] the explicit formulas:
-               A_hat = softmax(Q_lastblock K^T / sqrt(d));
-               C_struct = A_hat[:, sink + recency].sum() / b;
-               p = block_pool(colmean), block_pool(diagmean);
-               mu = max(1 - p[0] - p[-1], 0) / (N_blocks - 2);
-               S = {j : p_j > alpha mu};  PE: gamma_cumsum(pool(Q), pool(K), 0.95).
+* [rcap.io CRISP summary, per-head pseudo-code] where the paper's display
+               equations were lost, this summary supplies them: the proxy map is
+               the scaled, softmaxed product of the last query block with every
+               key; the structural mass is that map's total on the sink and
+               recency columns, averaged over the proxy rows; the vertical and
+               slash scores are its column and diagonal averages summed per
+               block; the floor is the mass left outside the two end blocks
+               (never negative) spread over the remaining N_b - 2 blocks; a
+               block survives when its score is above alpha times that floor;
+               Pooled-Estimation heads use the cumulative-mass cut on block
+               means of Q and K at gamma = 0.95.
 
 Readings where the pages are silent (each is repeated in the design notes):
 causal mask inside the proxy; C_struct over the union of the two windows;

@@ -252,6 +252,58 @@ def test_pe_cut_ties_go_to_lower_flat_index():
     assert info2["kstar"] == 8 and m2[2, 1] and not m2[3, 1] and not m2[3, 2]
 
 
+def test_pe_cut_stops_at_first_prefix_reaching_target_exactly():
+    """Dyadic masses make every prefix sum exact: sorted (value, flat index)
+    1 (0,0); .5 (1,0) (1,1) (2,0) (3,3); .25 (2,1) (2,2) (3,1); .125 (3,0) (3,2)
+    give prefix sums 1, 1.5, 2, 2.5, 3, 3.25, 3.5, 3.75, 3.875, 4 (T = 4).
+    With gamma = 7/8, gamma*T = 3.5 equals the seventh prefix, and the pages
+    stop accumulating once the mass reaches gamma [CRISP §2, PE path], so seven
+    entries are kept and (3,1), the eighth, is not."""
+    P = np.array([[1.0, 0, 0, 0],
+                  [0.5, 0.5, 0, 0],
+                  [0.5, 0.25, 0.25, 0],
+                  [0.125, 0.25, 0.125, 0.5]])
+    m, info = O.pe_cut(P, 0.875)
+    assert info["kstar"] == 7 and info["prefix"] == 3.5 == info["target"]
+    want = np.array([[1, 0, 0, 0],
+                     [1, 1, 0, 0],
+                     [1, 1, 1, 0],
+                     [1, 0, 0, 1]], bool)                   # (3,0) is an anchor, (3,1) stays out
+    assert np.array_equal(m, want)
+    # a hair above 7/8 needs the eighth entry
+    m8, info8 = O.pe_cut(P, float(np.nextafter(0.875, 1.0)))
+    assert info8["kstar"] == 8 and m8[3, 1]
+    # the same through the decision function, which takes gamma as the float32 parameter
+    _, _, _, lists, info2 = O.decide_from_scores(0, np.float32(0), None, None, P.astype(np.float32), 4, 0.3, 1.0,
+                                                 0.875)
+    assert info2["kstar"] == 7 and [l.tolist() for l in lists] == [[0], [0, 1], [0, 1, 2], [0, 3]]
+
+
+def test_coverage_cut_stops_at_first_prefix_reaching_target_exactly():
+    """Scores .5 .25 .125 .125 (dyadic, exact sums): gamma = .75 is reached
+    exactly by the first two blocks, so the budget is {0, 1} plus the anchor 3
+    [CRISP §2, accumulated until the mass reaches gamma]."""
+    p = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    keep, info = O.coverage_cut(p, 0.75)
+    assert info["kstar"] == 2 and sorted(keep.tolist()) == [0, 1]
+    sel, _ = O.vs_select_coverage(p, 0.75)
+    assert sel.tolist() == [0, 1, 3]
+    keep, info = O.coverage_cut(p, float(np.nextafter(0.75, 1.0)))
+    assert info["kstar"] == 3
+
+
+def test_jsd_router_at_equality():
+    """The router sends a head to Vertical-Slash when JSD >= tau [CRISP §2]:
+    identical distributions have JSD exactly 0, which meets tau = 0; a JSD equal
+    to the float32 tau meets it, the next double below does not."""
+    a = np.array([0.25, 0.25, 0.5])
+    assert O.jsd(a, a) == 0.0 and O.route_jsd(O.jsd(a, a), 0.0)
+    assert O.route_jsd(0.25, 0.25)
+    assert not O.route_jsd(float(np.nextafter(0.25, 0.0)), 0.25)
+    # tau is the float32 parameter: float32(0.1) is above 0.1, so JSD = 0.1 stays Pooled-Estimation
+    assert not O.route_jsd(0.1, 0.1) and O.route_jsd(float(np.float32(0.1)), 0.1)
+
+
 # ------------------------------------------------------------------ attention
 
 def _sdpa(q, k, v):
@@ -444,6 +496,35 @@ def test_pooled_estimate_closed_forms():
     k2 = k.copy()
     k2[2 * blk:3 * blk] += 200.0 * q.mean(axis=0) / np.linalg.norm(q.mean(axis=0))
     assert O.pooled_estimate(q, k2, blk)[2] > 1 - 1e-12
+    # a logit gap far beyond exp's range still gives the exact one-hot limit (the
+    # softmax is evaluated relative to its largest logit)
+    k3 = k.copy()
+    k3[4 * blk:5 * blk] += 1e5 * q.mean(axis=0) / np.linalg.norm(q.mean(axis=0))
+    want = np.zeros(nb); want[4] = 1.0
+    assert np.array_equal(O.pooled_estimate(q, k3, blk), want)
+
+
+def test_pooled_estimate_block_constant_keys_library_softmax():
+    """Keys constant within each block pool to those constants, and query rows
+    c + e_r with sum_r e_r = 0 pool to c, so a_bar is the softmax (scipy) of
+    K_const . c / sqrt(d) over the blocks [CRISP §2: softmax after pooling both
+    queries and keys, at the attention scale].  The rows differ from one
+    another, so pooling by a sum (b * c) or a dropped 1/sqrt(d) both move a_bar
+    far outside the tolerance."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(97)
+    blk, nb, d = 4, 7, 16
+    kc = rng.standard_normal((nb, d))
+    k = np.repeat(kc, blk, axis=0)
+    c = rng.standard_normal(d)
+    e = rng.standard_normal((blk, d)) * 2.0
+    e -= e.mean(axis=0)
+    q = c[None, :] + e
+    want = softmax(kc @ c / math.sqrt(d))
+    got = O.pooled_estimate(q, k, blk)
+    assert np.allclose(got, want, atol=1e-14)
+    assert np.abs(softmax(kc @ c) - want).max() > 1e-2           # the scale matters on this input
+    assert np.abs(softmax(kc @ (blk * c) / math.sqrt(d)) - want).max() > 1e-2   # and so does the mean
 
 
 def test_jsd_router_threshold_and_variants_on_tiny_layer():
