@@ -276,13 +276,36 @@ def test_output_is_causal():
 
 # ------------------------------------------------------------------ the Llama / Qwen layers
 
-def _big_layer(layer, heads_fid, nblk, seed_blocks):
-    spec = synth.make_spec(layer)
+# Full-size protocol: every decision of every head bit-exact, every head's
+# proxy scores against the oracle's float64 ones, and for every head the
+# output rows of query blocks 0, N_b - 1 and 14 seeded others.
+
+_LAYERS = {}
+
+
+def _layer_on_device(layer):
+    """Host arrays and device tensors of a named layer, generated once per session
+    (the 128k layers serve several tests)."""
+    if layer.name not in _LAYERS:
+        _LAYERS.clear()
+        torch.cuda.empty_cache()
+        spec = synth.make_spec(layer)
+        Q, K, V = P.load_layer(spec)
+        _LAYERS[layer.name] = (spec, Q, K, V, P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V))
+    return _LAYERS[layer.name]
+
+
+def _drop_layers():
+    _LAYERS.clear()
+    torch.cuda.empty_cache()
+
+
+def _big_layer(layer, seed_blocks, pe_fid=None):
+    spec, Q, K, V, q, k, v = _layer_on_device(layer)
     cfg = spec.cfg
-    Q, K, V = P.load_layer(spec)
     p = P.params_of(cfg)
-    q, k, v, o, sel = _run_layer(spec, Q, K, V, p)
-    del q, k, v
+    o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+    torch.cuda.synchronize()
     route = sel.route.cpu().numpy()
     P.log(f"[{cfg.name}] routes VS={int((route == 1).sum())} PE={int((route == 0).sum())}")
     # diffuse heads route to PE; each KV group's lead concentrated head (its keys carry the
@@ -291,35 +314,145 @@ def _big_layer(layer, heads_fid, nblk, seed_blocks):
     assert np.all(route[~spec.concentrated] == 0), route
     assert np.all(route[spec.lead[spec.lead >= 0]] == 1), route
     P.log(f"[{cfg.name}] C_struct", np.round(sel.c_struct.cpu().numpy(), 3).tolist())
-    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p, name=cfg.name)
     P.log(f"[{cfg.name}] decisions", rep)
-    assert rep["heads_checked"] + rep["pe_exempt"] == cfg.hq
-    vs = [h for h in range(cfg.hq) if route[h] == 1][:heads_fid]
-    pe = [h for h in range(cfg.hq) if route[h] == 0][:heads_fid]
-    P.log(f"[{cfg.name}] score err", P.check_score_fidelity(spec, Q, K, sel, vs + pe))
-    P.log(f"[{cfg.name}] PE prob err", P.check_pe_fidelity(spec, Q, K, sel, pe[:1]))
-    blocks = synth.sample_blocks(cfg.nb, nblk, seed_blocks)
-    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), vs[:2] + pe[:2], blocks)
-    P.log(f"[{cfg.name}] attention (sampled {len(blocks)} blocks x 4 heads) max {mx:.2e} mean {mean:.2e}")
+    # no head of a named layer needs the fixed-point exemption: every list is compared
+    assert rep["pe_exempt"] == 0 and rep["vs_exempt"] == 0 and rep["heads_checked"] == cfg.hq, rep
+    P.log(f"[{cfg.name}] score err (every head)", P.check_score_fidelity(spec, Q, K, sel, range(cfg.hq)))
+    pe = [h for h in range(cfg.hq) if route[h] == 0]
+    P.log(f"[{cfg.name}] PE prob err", P.check_pe_fidelity(spec, Q, K, sel, pe[:pe_fid]))
+    blocks = synth.sample_blocks(cfg.nb, 14, seed_blocks)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(cfg.hq), blocks)
+    P.log(f"[{cfg.name}] attention (every head x {len(blocks)} blocks) max {mx:.2e} mean {mean:.2e}")
+    return sel
 
 
 def test_llama_32k_layer():
-    _big_layer(synth.LLAMA_32K, 3, 8, 1)
+    _big_layer(synth.LLAMA_32K, 1)
 
 
 @pytest.mark.timeout(900)
 def test_llama_128k_layer():
-    _big_layer(synth.LLAMA_128K, 2, 6, 2)
+    _big_layer(synth.LLAMA_128K, 2)
+
+
+@pytest.mark.timeout(900)
+def test_llama_128k_alpha_tau_sweep():
+    """The 128k Llama layer under the sweep alpha in {0.5, 1, 2} x tau in
+    {0.2, 0.3, 0.5}: every decision of every head bit-exact for the nine pairs;
+    for each alpha at tau = 0.3 the output rows of every Vertical-Slash head
+    (the heads alpha acts on) on 16 query blocks."""
+    spec, Q, K, V, q, k, v = _layer_on_device(synth.LLAMA_128K)
+    cfg = spec.cfg
+    sizes = {}
+    for tau in (0.2, 0.3, 0.5):
+        for alpha in (0.5, 1.0, 2.0):
+            p = P.params_of(cfg, tau=tau, alpha=alpha)
+            sel = dsp.crisp_select(q, k, p, pe_prob=True)
+            torch.cuda.synchronize()
+            rep = P.check_decisions(sel, cfg.hq, cfg.nb, p, name=f"{cfg.name} sweep")
+            assert rep["pe_exempt"] == 0 and rep["heads_checked"] == cfg.hq, rep
+            vs = sel.route.cpu().numpy() == 1
+            sizes[(tau, alpha)] = (int(vs.sum()), float(sel.nv.cpu().numpy()[vs].mean()) if vs.any() else 0.0)
+    P.log(f"[{cfg.name} sweep] (VS heads, mean |S_v|) per (tau, alpha)", sizes)
+    for tau in (0.2, 0.3, 0.5):                   # the budget shrinks as alpha grows
+        assert sizes[(tau, 0.5)][1] >= sizes[(tau, 1.0)][1] >= sizes[(tau, 2.0)][1]
+    for alpha in (0.5, 2.0):                      # alpha = 1 is the layer test above
+        p = P.params_of(cfg, alpha=alpha)
+        o, sel = dsp.crisp_prefill(q, k, v, p)
+        torch.cuda.synchronize()
+        route = sel.route.cpu().numpy()
+        heads = [h for h in range(cfg.hq) if route[h] == 1]
+        blocks = synth.sample_blocks(cfg.nb, 14, 20 + int(alpha * 2))
+        mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), heads, blocks)
+        P.log(f"[{cfg.name} alpha={alpha}] attention ({len(heads)} VS heads x {len(blocks)} blocks) "
+              f"max {mx:.2e} mean {mean:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_dense_attention_llama_128k():
+    """Dense attention at 128k, where K and V (512 MB) exceed the last-level
+    cache and the persistent kernel orders its work two KV groups at a time:
+    one query head of every KV group (a different member of each group) on 16
+    query blocks against the oracle's causal attention."""
+    spec, Q, K, V, q, k, v = _layer_on_device(synth.LLAMA_128K)
+    cfg = spec.cfg
+    o = dsp.crisp_dense_attn(q, k, v)
+    torch.cuda.synchronize()
+    G = cfg.hq // cfg.hkv
+    heads = [g * G + g % G for g in range(cfg.hkv)]
+    blocks = synth.sample_blocks(cfg.nb, 14, 6)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: range(qb + 1), heads, blocks)
+    P.log(f"[{cfg.name} dense] attention ({len(heads)} heads x {len(blocks)} blocks) max {mx:.2e} mean {mean:.2e}")
+    _drop_layers()
 
 
 @pytest.mark.timeout(900)
 def test_qwen_128k_layer():
-    _big_layer(synth.QWEN_128K, 2, 6, 3)
+    _big_layer(synth.QWEN_128K, 3)
+    _drop_layers()
 
 
 @pytest.mark.timeout(1200)
 def test_llama_512k_layer():
-    _big_layer(synth.LLAMA_512K, 1, 4, 4)
+    _big_layer(synth.LLAMA_512K, 4, pe_fid=4)
+    _drop_layers()
+
+
+@pytest.mark.timeout(900)
+def test_odd_kv_count_beyond_cache():
+    """Three KV groups at 196,608 tokens: K and V take 302 MB, more than the
+    256 MB last-level cache, so the attention work is ordered two groups at a
+    time and the third group runs alone.  Sparse and dense outputs of every
+    head on sampled blocks, every decision bit-exact."""
+    cfg = synth.custom_config("odd-kv-196k", 196608, 6, 3, seed=17, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = P.load_layer(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    p = P.params_of(cfg)
+    o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+    od = dsp.crisp_dense_attn(q, k, v)
+    torch.cuda.synchronize()
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p, name=cfg.name)
+    assert rep["heads_checked"] + rep["pe_exempt"] == cfg.hq, rep
+    route = sel.route.cpu().numpy()
+    assert (route == 1).any() and (route == 0).any(), route
+    blocks = synth.sample_blocks(cfg.nb, 14, 8)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(cfg.hq), blocks)
+    P.log(f"[{cfg.name}] sparse attention max {mx:.2e} mean {mean:.2e}")
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, od, lambda h, qb: range(qb + 1), range(cfg.hq), blocks[::2])
+    P.log(f"[{cfg.name}] dense attention max {mx:.2e} mean {mean:.2e}")
+
+
+@pytest.mark.parametrize("sink,local", [(0, 0), (64, 200), (200, 64), (1, 1), (127, 129), (300, 1000),
+                                        (0, 4096), (4096, 0)])
+def test_anchor_windows(sink, local):
+    """Sink and recency windows that are not one block [CRISP §3.2: w_sink and
+    w_local are parameters]: windows inside a tile, across tile edges, empty,
+    and the whole sequence.  C_struct against the oracle's (same windows), every
+    decision bit-exact (route at the default tau and at tau = 0), full outputs."""
+    cfg = synth.custom_config("anchors", 4096, 4, 2, seed=71, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    for tau in (cfg.tau, 0.0):
+        p = P.params_of(cfg, sink=sink, local=local, tau=tau)
+        o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+        torch.cuda.synchronize()
+        err = P.check_score_fidelity(spec, Q, K, sel, range(cfg.hq), sink=sink, local=local)
+        rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+        assert rep["heads_checked"] + rep["pe_exempt"] == cfg.hq, rep
+        cs = sel.c_struct.cpu().numpy()
+        if sink == 0 and local == 0:
+            assert np.all(cs == 0)
+        if tau == 0.0:
+            assert np.all(sel.route.cpu().numpy() == 1)          # C_struct >= 0 always
+        P.log(f"[anchors {sink}/{local} tau={tau}] C_struct {np.round(cs, 4).tolist()} score err {err:.1e} "
+              f"routes {sel.route.cpu().tolist()}")
+        P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(cfg.hq), range(cfg.nb))
+    # windows covering everything: C_struct is the whole proxy mass
+    if sink >= cfg.n or local >= cfg.n:
+        assert np.all(np.abs(cs - 1.0) < 1e-5), cs
 
 
 # ------------------------------------------------------------------ variants: JSD router, median floor, coverage budget
@@ -384,10 +517,8 @@ def test_variant_min_blocks_and_gamma_sweep():
 def test_flexprefill_configuration_llama_128k():
     """FlexPrefill's pair of rules (JSD router, coverage budget at gamma 0.95)
     on the Llama 128k layer: decisions in full, sampled outputs."""
-    spec = synth.make_spec(synth.LLAMA_128K)
+    spec, Q, K, V, q, k, v = _layer_on_device(synth.LLAMA_128K)
     cfg = spec.cfg
-    Q, K, V = P.load_layer(spec)
-    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
     flags = dsp.FLAG_ROUTE_JSD | dsp.FLAG_VS_COVERAGE
     sel0 = dsp.crisp_select(q, k, P.params_of(cfg, tau=0.0, flags=flags))
     torch.cuda.synchronize()
@@ -397,8 +528,8 @@ def test_flexprefill_configuration_llama_128k():
     p = P.params_of(cfg, tau=float(np.median(js)), flags=flags)
     o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
     torch.cuda.synchronize()
-    del q, k, v
-    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p)
+    _drop_layers()
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p, name=f"{cfg.name} FlexPrefill")
     P.log("[flex 128k] decisions", rep, "routes", sel.route.cpu().tolist())
     assert rep["heads_checked"] + rep["pe_exempt"] + rep["vs_exempt"] + rep["route_ties"] == cfg.hq
     route = sel.route.cpu().numpy()
