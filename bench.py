@@ -41,8 +41,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 TILE_FLOPS = 4 * 128 * 128 * 128          # QK^T + PV for one 128 x 128 tile at d = 128
+# causal part of a diagonal tile: query row r sees keys 0..r, 129/256 of the tile's pairs
+DIAG_USEFUL = 129 / 256
 PEAK_BF16_TFLOPS = 2500.0                  # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3              # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+# VALU model of the chip (256 CUs at 2.4 GHz, 4 SIMDs of 16 lanes each): a
+# full-rate vector op costs one lane-cycle per lane, a transcendental (v_exp_f32)
+# four; 64 lane-cycles per clock per CU.
+CU, CLOCK_GHZ, LANE_CYCLES_PER_CLK = 256, 2.4, 64
 
 
 def log(*a):
@@ -108,6 +115,51 @@ def step_events(fn, reps, torch, flush=None):
         e.record()
         e.synchronize()
         out.append(s.elapsed_time(e))
+    return out
+
+
+def head_mix(spec, sel_route, c_struct):
+    """Route counts of a layer against how its heads were generated, and the
+    C_struct distribution (so a reader sees which heads the router sent where)."""
+    conc = np.asarray(spec.concentrated, bool)
+    edges = [0.0, 0.01, 0.05, 0.1, 0.2, 0.3, 0.5, 0.75, 1.0001]
+    hist, _ = np.histogram(np.asarray(c_struct, np.float64), bins=edges)
+    return {"vs": int((sel_route == 1).sum()), "pe": int((sel_route == 0).sum()),
+            "dense": int((sel_route == -1).sum()),
+            "concentrated": int(conc.sum()), "concentrated_to_vs": int(((sel_route == 1) & conc).sum()),
+            "diffuse_to_pe": int(((sel_route == 0) & ~conc).sum()),
+            "c_struct_hist": {f"[{a:g},{min(b, 1.0):g})": int(c) for a, b, c in zip(edges[:-1], edges[1:], hist)},
+            "c_struct_min_max": [round(float(np.min(c_struct)), 4), round(float(np.max(c_struct)), 4)]}
+
+
+def selection_stage_bounds(cfg, route, tiles):
+    """Lower bounds of the selection's stages from their algorithmic work.
+    proxy: K once (HBM), 2*128*n*d flops per query head (bf16 MFMA) and, per
+    score, one v_exp_f32 (4 lane-cycles) plus three full-rate ops (scale and
+    shift, sum, max): the VALU bound is the largest of the three.  Pooled
+    estimation: Q of the PE heads once (pooling), pooled logits on fp32 MFMA
+    (2 * d flops per causal block pair), the pooled matrix written once and read
+    by the cut.  Lists: 4 bytes per entry written."""
+    nb = cfg.n // 128
+    h_pe = int((route == 0).sum())
+    tri = nb * (nb + 1) // 2
+    scores = cfg.hq * 128 * cfg.n
+    proxy = {"hbm_ms": cfg.hkv * cfg.n * 128 * 2 / (PEAK_HBM_GBS * 1e9) * 1e3,
+             "mfma_ms": 2 * 128 * cfg.n * 128 * cfg.hq / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
+             "valu_ms": scores * (4 + 3) / (CU * LANE_CYCLES_PER_CLK * CLOCK_GHZ * 1e9) * 1e3}
+    pool = {"hbm_ms": h_pe * cfg.n * 128 * 2 / (PEAK_HBM_GBS * 1e9) * 1e3}
+    logits = {"mfma_fp32_ms": h_pe * tri * 2 * 128 / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e3,
+              "hbm_ms": h_pe * tri * 4 / (PEAK_HBM_GBS * 1e9) * 1e3}
+    cut = {"hbm_ms": 2 * h_pe * tri * 4 / (PEAK_HBM_GBS * 1e9) * 1e3}
+    lists = {"hbm_ms": 4 * tiles / (PEAK_HBM_GBS * 1e9) * 1e3}
+    out = {}
+    for name, b in (("proxy_scores", proxy), ("pool_q", pool), ("pooled_logits", logits), ("pooled_cut", cut),
+                    ("lists", lists)):
+        bound = max(b, key=b.get)
+        out[name] = {k: round(v, 4) for k, v in b.items()}
+        out[name]["bound"] = bound.replace("_ms", "")
+    out["sum_of_bounds_ms"] = round(sum(max(v for k, v in b.items() if k.endswith("_ms"))
+                                        for b in (proxy, pool, logits, cut, lists)), 4)
     return out
 
 
@@ -301,8 +353,8 @@ def measured_peaks(torch):
                    "second of two ~0.4 s launches; HBM: 2 GiB device copy, read + write bytes"}
 
 
-def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=False):
-    spec = synth.make_spec(layer)
+def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=False, compensate=True):
+    spec = synth.make_spec(layer, compensate=compensate)
     cfg = spec.cfg
     t = time.time()
     Q, K, V = synth.generate(spec, threads=16)
@@ -325,6 +377,7 @@ def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=
     cold = step_events(step, max(1, steps), torch, flush=flush)
     del flush
     route = sel.route.cpu().numpy()
+    cstruct = sel.c_struct.cpu().numpy()
     tiles = int(sel.row_ptr[-1].item())
     nb = cfg.nb
     dense_tiles = cfg.hq * nb * (nb + 1) // 2
@@ -337,6 +390,11 @@ def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=
                step_ms={"warm_median": float(np.median(warm)), "warm_min": float(np.min(warm)),
                         "l2_flushed_median": float(np.median(cold)), "l2_flushed_min": float(np.min(cold))})
     out["selection_roofline"] = selection_roofline(cfg, route, tiles, sel_ms)
+    out["selection_roofline"]["stage_bounds"] = selection_stage_bounds(cfg, route, tiles)
+    out["heads"] = head_mix(spec, route, cstruct)
+    # every list holds its diagonal block: hq * nb diagonal tiles, each 129/256 useful
+    diag = cfg.hq * nb
+    out["useful_flops"] = ((tiles - diag) + diag * DIAG_USEFUL) * TILE_FLOPS
     if with_dense:
         od = torch.empty_like(q)
         dws = attn_ws
@@ -346,6 +404,7 @@ def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=
         out["speedup"] = out["dense_ms"] / ms
         out["dense_tflops"] = dense_tiles * TILE_FLOPS / (out["dense_kernel_ms"] * 1e-3) / 1e12
     out["sparse_tflops"] = tiles * TILE_FLOPS / (attn_ms * 1e-3) / 1e12
+    out["useful_tflops"] = out["useful_flops"] / (attn_ms * 1e-3) / 1e12
     if compare:
         del sel, o, ws
         torch.cuda.empty_cache()
@@ -455,9 +514,16 @@ def main():
                 continue
             r, _, _ = run_layer(synth.WORKLOADS[name], max(2, args.steps), 1, torch, dsp, synth)
             extra[r["workload"]] = {k: r[k] for k in ("ms", "dense_ms", "speedup", "select_ms", "sparse_attn_ms",
-                                                      "density", "vs_heads", "pe_heads", "sparse_tflops",
+                                                      "density", "heads", "sparse_tflops", "useful_tflops",
                                                       "dense_tflops", "selection_roofline")}
             log("[bench]", json.dumps(r))
+        # the 32k Llama layer with the literal generator constants (no length
+        # compensation): the anchor share of concentrated heads falls with n,
+        # so more of them route to Pooled Estimation
+        r, _, _ = run_layer(synth.LLAMA_32K, max(3, args.steps), 1, torch, dsp, synth, compensate=False)
+        extra["llama3.1-8b-32k-literal-constants"] = {k: r[k] for k in ("ms", "dense_ms", "speedup", "select_ms",
+                                                                        "sparse_attn_ms", "density", "heads")}
+        log("[bench]", json.dumps(r))
     peaks = None if args.no_peaks else measured_peaks(torch)
     if peaks:
         log("[bench] measured peaks", json.dumps(peaks))
@@ -492,9 +558,12 @@ def main():
             if peaks else {})),
         "rules": main_res.get("rules"),
         "density": round(main_res["density"], 4),
-        "heads": {"vs": main_res["vs_heads"], "pe": main_res["pe_heads"]},
+        "heads": main_res["heads"],
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "useful_achieved": round(main_res["useful_tflops"], 2),
+                     "useful_frac": round(main_res["useful_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "useful_flops_per_launch": int(main_res["useful_flops"]),
                      "frac_of_measured": round(ach / peaks["mfma_bf16_tflops"], 4) if peaks else None,
                      "traffic": profiled_traffic() if args.workload == "llama3.1-8b-512k" else None,
                      "kernel": "fa_bf16_kernel<false> (sparse attention; event time includes the V re-layout)",

@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "lanes.h"
 #include "launch.h"
 #include "tile.h"
 
@@ -86,13 +87,6 @@ __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// max of a lane's value and that of lane ^ 32 with one v_permlane32_swap (no
-// LDS round trip): both lanes of the pair get the result
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // A 128-row x 256-byte tile goes to LDS as 16-byte chunks, chunk c of row r at

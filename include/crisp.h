@@ -150,7 +150,11 @@ int crisp_sparse_attn(const crisp_shape *shape, const void *q, const void *k, co
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dense causal attention on the same tile engine: every key block 0..qb for
- * every row.  The speedup baseline and the dense path of the method. */
+ * every row, i.e. the problem statement's mask M_S with every causal block
+ * selected [CRISP §2], and the exact dense attention the paper's latency
+ * comparison measures speedups against [CRISP §5, attention-only latency].
+ * Also the path the method falls back to (route -1).  Reads q, k, v; writes
+ * o [hq, n, d].  Workspace and errors as for crisp_sparse_attn. */
 int crisp_dense_attn(const crisp_shape *shape, const void *q, const void *k, const void *v,
                      void *o, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
