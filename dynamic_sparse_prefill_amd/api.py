@@ -29,7 +29,7 @@ FLAG_ROUTE_JSD, FLAG_VS_MEDIAN, FLAG_VS_COVERAGE = 1, 2, 4
 EXPORTS = ("crisp_select_workspace_bytes", "crisp_attn_workspace_bytes", "crisp_workspace_bytes",
            "crisp_col_capacity", "crisp_select", "crisp_sparse_attn", "crisp_dense_attn",
            "crisp_prefill", "crisp_status_string", "crisp_varlen_col_capacity", "crisp_varlen_workspace_bytes",
-           "crisp_prefill_varlen")
+           "crisp_prefill_varlen", "crisp_noalloc_scratch_bytes", "crisp_prefill_noalloc")
 
 
 class CrispShape(C.Structure):
@@ -107,6 +107,10 @@ def lib() -> C.CDLL:
         L.crisp_varlen_workspace_bytes.restype = C.c_size_t
         L.crisp_prefill_varlen.argtypes = [sp, C.c_int32, i64p, vp, vp, vp, pp, selp, vp, vp, C.c_size_t, vp]
         L.crisp_prefill_varlen.restype = C.c_int
+        L.crisp_noalloc_scratch_bytes.argtypes = []
+        L.crisp_noalloc_scratch_bytes.restype = C.c_size_t
+        L.crisp_prefill_noalloc.argtypes = [sp, vp, vp, vp, pp, selp, vp, vp]
+        L.crisp_prefill_noalloc.restype = C.c_int
         _LIB = L
     return _LIB
 
@@ -293,6 +297,25 @@ def crisp_prefill(q, k, v, params: CrispParams | None = None, sel: Selection | N
                              C.byref(c_sel), o.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
     if st:
         raise CrispError(st, "crisp_prefill")
+    return o, sel
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the fixed scratch array behind crisp_prefill_noalloc."""
+    return int(lib().crisp_noalloc_scratch_bytes())
+
+
+def crisp_prefill_noalloc(q, k, v, params: CrispParams, sel: Selection, o: torch.Tensor):
+    """crisp_prefill with the library's fixed scratch as workspace: the caller
+    passes the outputs (sel from new_selection, o like q) and nothing is
+    allocated.  Raises CrispError with status CRISP_E_TOO_LARGE (-5) when the
+    problem needs more than noalloc_scratch_bytes()."""
+    shape = make_shape(q, k, v, o)
+    c_sel = sel.c()
+    st = lib().crisp_prefill_noalloc(C.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), C.byref(params.c()),
+                                     C.byref(c_sel), o.data_ptr(), _stream())
+    if st:
+        raise CrispError(st, "crisp_prefill_noalloc")
     return o, sel
 
 

@@ -6,9 +6,17 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 using namespace crisp;
+
+// Workspace of crisp_prefill_noalloc: a fixed device array, one copy per GPU,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it names a stand-in, not device memory): it looks up the
+// array's device address once per device and passes that.
+static __device__ __align__(256) char scratch[CRISP_NOALLOC_SCRATCH_BYTES];
 
 int crisp::device_cu_count() {
   static int cache[64] = {0};
@@ -256,6 +264,26 @@ int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, 
                                     s->hq, s->hkv, strides(s), stream));
 }
 
+// ---- allocation-free prefill
+
+std::mutex scratch_mu;
+void* scratch_dev[64];   // device address of `scratch` per device, looked up on first use
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CRISP_E_HIP;
+  if (dev < 0 || dev >= 64) return CRISP_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CRISP_E_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return CRISP_OK;
+}
+
 // ---- packed batches (varlen)
 
 struct VarlenPlan {
@@ -371,6 +399,27 @@ int crisp_prefill(const crisp_shape* shape, const void* q, const void* k, const 
   return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream);
 }
 
+size_t crisp_noalloc_scratch_bytes(void) { return CRISP_NOALLOC_SCRATCH_BYTES; }
+
+int crisp_prefill_noalloc(const crisp_shape* shape, const void* q, const void* k, const void* v,
+                          const crisp_params* params, crisp_selection* sel, void* o, hipStream_t stream) {
+  // every check before the first HIP call
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_params(shape, params))) return st;
+  const size_t sel_bytes = select_layout(shape).total;
+  if (sel_bytes + attn_ws(shape) > CRISP_NOALLOC_SCRATCH_BYTES) return CRISP_E_TOO_LARGE;
+  if (!v || !o) return CRISP_E_ARG;
+  if ((st = check_qkv(shape, q, k, v, o))) return st;
+  if (!sel || !sel->route || !sel->c_struct || !sel->row_ptr || !sel->col_idx) return CRISP_E_ARG;
+  if (sel->col_capacity < crisp_col_capacity(shape)) return CRISP_E_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  st = run_select(shape, q, k, params, sel, ws, stream);
+  if (st) return st;
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)ws + sel_bytes, stream);
+}
+
 int64_t crisp_varlen_col_capacity(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens) {
   VarlenPlan P;
   if (plan_varlen(shape, nseq, cu_seqlens, nullptr, &P)) return 0;
@@ -423,6 +472,7 @@ const char* crisp_status_string(int status) {
     case CRISP_E_UNSUPPORTED: return "unsupported shape or dtype";
     case CRISP_E_WORKSPACE: return "workspace or list capacity too small";
     case CRISP_E_HIP: return "kernel launch failed";
+    case CRISP_E_TOO_LARGE: return "problem needs more workspace than the allocation-free entry point's fixed scratch";
     default: return "unknown status";
   }
 }

@@ -53,7 +53,8 @@ typedef enum {
   CRISP_E_ARG = -1,          /* invalid argument: NULL pointer, bad shape, stride or parameter */
   CRISP_E_UNSUPPORTED = -2,  /* valid but not implemented: d != 128, block != 128, unknown dtype, n too long */
   CRISP_E_WORKSPACE = -3,    /* workspace or column capacity too small */
-  CRISP_E_HIP = -4           /* a kernel launch failed */
+  CRISP_E_HIP = -4,          /* a kernel launch failed */
+  CRISP_E_TOO_LARGE = -5     /* crisp_prefill_noalloc: the problem's workspace exceeds the fixed scratch */
 } crisp_status;
 
 typedef enum { CRISP_BF16 = 0, CRISP_FP32 = 1 } crisp_dtype;
@@ -163,6 +164,28 @@ int crisp_dense_attn(const crisp_shape *shape, const void *q, const void *k, con
 int crisp_prefill(const crisp_shape *shape, const void *q, const void *k, const void *v,
                   const crisp_params *params, crisp_selection *sel, void *o,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- allocation-free prefill -----------------------------------------------
+ * For callers that cannot allocate device memory at call time: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * crisp_prefill_noalloc computes exactly what crisp_prefill computes, with the
+ * same kernels, but takes no workspace argument: its workspace is a fixed
+ * device array of CRISP_NOALLOC_SCRATCH_BYTES inside the library (one copy per
+ * GPU, held until the process ends).  The caller still owns q, k, v, o and the
+ * selection buffers.  It allocates nothing and calls no allocating routine.
+ *   - A problem whose workspace (crisp_workspace_bytes) exceeds the scratch is
+ *     rejected with CRISP_E_TOO_LARGE before anything is enqueued (128 MiB holds
+ *     a Llama-shaped layer of 32 query / 8 KV heads up to about 40k tokens).
+ *   - The first call on a device looks up the array's device address on that
+ *     device (hipGetSymbolAddress); CRISP_E_HIP if that fails.
+ *   - Every call on one GPU uses the same array, so calls that overlap in time
+ *     on one GPU (two streams, two host threads) race and give wrong results;
+ *     calls on different GPUs do not interact.  No state is carried from one
+ *     call to the next: every counter is cleared by the call's own kernels. */
+#define CRISP_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+size_t crisp_noalloc_scratch_bytes(void);
+int crisp_prefill_noalloc(const crisp_shape *shape, const void *q, const void *k, const void *v,
+                          const crisp_params *params, crisp_selection *sel, void *o, hipStream_t stream);
 
 /* ---- packed batches (varlen) ------------------------------------------------
  * nseq sequences (1 <= nseq <= 64) packed along the token axis of q, k, v, o:

@@ -144,3 +144,26 @@ def test_varlen_queries_and_validation():
     small = api.CrispSelectionC(16, 16, 16, 16, 10)
     assert L.crisp_prefill_varlen(C.byref(s), 3, arr, 16, 16, 16, C.byref(p.c()), C.byref(small), 16, 256,
                                   1 << 40, None) == -3
+
+
+def test_noalloc_entry_point_rejects_before_any_launch():
+    """The allocation-free prefill checks everything on the host first: a
+    problem whose workspace exceeds the fixed scratch is CRISP_E_TOO_LARGE
+    (-5), missing outputs are CRISP_E_ARG, a short list buffer
+    CRISP_E_WORKSPACE; none of these touches the device."""
+    L = dsp.lib()
+    cap = dsp.noalloc_scratch_bytes()
+    assert cap == 128 << 20
+    p = dsp.CrispParams()
+    sel = api.CrispSelectionC(16, 16, 16, 16, 1 << 40)
+    small = _shape(n=4096, hq=4, hkv=2)
+    assert dsp.workspace_bytes(small, p) <= cap
+    big = _shape(n=65536, hq=32, hkv=8)
+    assert dsp.workspace_bytes(big, p) > cap
+    assert L.crisp_prefill_noalloc(C.byref(big), 16, 16, 16, C.byref(p.c()), C.byref(sel), 16, None) == -5
+    assert dsp.api.status_string(-5).startswith("problem needs more workspace")
+    assert L.crisp_prefill_noalloc(C.byref(small), 16, 16, 16, C.byref(p.c()), None, 16, None) == -1
+    assert L.crisp_prefill_noalloc(C.byref(small), 16, 16, 0, C.byref(p.c()), C.byref(sel), 16, None) == -1
+    short = api.CrispSelectionC(16, 16, 16, 16, 10)
+    assert L.crisp_prefill_noalloc(C.byref(small), 16, 16, 16, C.byref(p.c()), C.byref(short), 16, None) == -3
+    assert L.crisp_prefill_noalloc(C.byref(_shape(d=64)), 16, 16, 16, C.byref(p.c()), C.byref(sel), 16, None) == -2
