@@ -42,6 +42,15 @@
 namespace crisp {
 
 constexpr int NQUEUE = 8;  // work queues of the persistent attention kernel (one per XCD)
+// Sparse attention walks the item order twice, each pass with its own NQUEUE
+// counters: first it takes only the items whose lists cover more than a
+// quarter of their causal key blocks, then the rest (dense attention makes one
+// pass over all items).  Long items then start in waves of about equal length,
+// as in dense attention, and the work-groups of an XCD walk the same K / V
+// tiles of their KV group at about the same time, sharing them through L2;
+// with short items interleaved, long ones would start at scattered times and
+// walk unrelated tiles.  The short items fill the end of the launch.
+constexpr int NPHASE = 2;
 
 // ------------------------------------------------------------------ V re-layout
 
@@ -55,13 +64,13 @@ __host__ __device__ __forceinline__ int vt_pos(int e) {
 }
 
 // V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128]; bf16 rows use vt_pos order.
-// Also clears the attention kernel's work-queue counter (it runs right before).
+// Also clears the attention kernels' work-queue counters (they run right after).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, T* __restrict__ Vt,
                                                           int nb, int64_t sv_h, int64_t sv_n, int* queue) {
   __shared__ T tile[BLK][HD + 2];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  if (kb == 0 && g == 0 && tid < NQUEUE && queue) queue[tid] = 0;
+  if (kb == 0 && g == 0 && tid < NQUEUE * NPHASE && queue) queue[tid] = 0;
   const T* src = V + (int64_t)g * sv_h + (int64_t)kb * BLK * sv_n;
   for (int e = tid; e < BLK * HD; e += 256) {
     const int r = e / HD, d = e % HD;
@@ -418,7 +427,10 @@ __device__ __forceinline__ void fa_bf16_item(
 }
 
 // Persistent loop: one work-group per CU takes items from the queues until
-// all are empty.  `queue` holds NQUEUE counters, zero at launch.
+// all are empty.  `queue` holds NQUEUE counters per pass, zero at launch.
+// Dense: one pass over every item.  Sparse: pass 1 takes only the items whose
+// two lists hold more than a quarter of the pair's causal key blocks, pass 2
+// the others.
 template <bool DENSE>
 __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
@@ -433,19 +445,30 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
   __shared__ int s_item;
   const int home = blockIdx.x % NQUEUE;
   const int64_t vt_h = (int64_t)nb_total * (BLK * HD);
-  for (int k = 0; k < NQUEUE; ++k) {
-    const int x = (home + k) % NQUEUE;
-    while (true) {
-      __builtin_amdgcn_s_waitcnt(0);              // nothing of the last item is still in flight
-      __syncthreads();                            // every wave is done with the last item's LDS
-      if (threadIdx.x == 0) s_item = atomicAdd(queue + x, 1);
-      __syncthreads();
-      int seq, pair, kvh, h;
-      if (!queue_item(x, s_item, sq, hq, hkv, seq, pair, kvh, h)) break;
-      const int64_t t0 = sq.tok[seq];
-      fa_bf16_item<DENSE>(sK0, sV0, sK1, sV1, pair, kvh, h, Q + t0 * sq_n, K + t0 * sk_n, Vt + t0 * HD, O + t0 * so_n,
-                          row_ptr + sq.rp[seq], col_idx + sq.col[seq], sq.nb[seq], hq, hkv, sq_h, sq_n, sk_h,
-                          sk_n, so_h, so_n, vt_h, sl2);
+  for (int pass = 0; pass < (DENSE ? 1 : NPHASE); ++pass) {
+    int* qs = queue + NQUEUE * pass;
+    for (int k = 0; k < NQUEUE; ++k) {
+      const int x = (home + k) % NQUEUE;
+      while (true) {
+        __builtin_amdgcn_s_waitcnt(0);              // nothing of the last item is still in flight
+        __syncthreads();                            // every wave is done with the last item's LDS
+        if (threadIdx.x == 0) s_item = atomicAdd(qs + x, 1);
+        __syncthreads();
+        int seq, pair, kvh, h;
+        if (!queue_item(x, s_item, sq, hq, hkv, seq, pair, kvh, h)) break;
+        if (!DENSE) {                               // long items in pass 0, short ones in pass 1
+          const int nbs = sq.nb[seq], qlo = 2 * pair;
+          const int32_t* rp = row_ptr + sq.rp[seq] + (int64_t)h * nbs + qlo;
+          const bool two = qlo + 1 < nbs;
+          const int len = (two ? rp[2] : rp[1]) - rp[0];
+          const int causal = qlo + 1 + (two ? qlo + 2 : 0);
+          if ((4 * len > causal) != (pass == 0)) continue;
+        }
+        const int64_t t0 = sq.tok[seq];
+        fa_bf16_item<DENSE>(sK0, sV0, sK1, sV1, pair, kvh, h, Q + t0 * sq_n, K + t0 * sk_n, Vt + t0 * HD,
+                            O + t0 * so_n, row_ptr + sq.rp[seq], col_idx + sq.col[seq], sq.nb[seq], hq, hkv, sq_h,
+                            sq_n, sk_h, sk_n, so_h, so_n, vt_h, sl2);
+      }
     }
   }
 }
