@@ -224,10 +224,14 @@ def compare_rules(cfg, q, k, v, dsp, torch, steps, dense_ms):
     return out
 
 
+LENGTH_GATE = 8192   # dense_below_n at the crossover the length sweep measures on this GPU
+
+
 def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=3):
     """CRISP vs dense ms per layer on Llama-shaped layers of growing length (4k-64k):
     where sparse prefill starts to pay (the length gate).  CRISP is timed as
-    enqueued call by call and as one HIP graph replay of the same prefill."""
+    enqueued call by call, as one HIP graph replay of the same prefill, and with
+    the length gate at LENGTH_GATE tokens (shorter layers take the dense path)."""
     res = {}
     for n in ns:
         cfg = synth.custom_config(f"llama-shape-{n // 1024}k", n, 32, 8, seed=7, conc_frac=0.6)
@@ -249,9 +253,14 @@ def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=
         aws = ws[dsp.select_workspace_bytes(dsp.make_shape(q, k, v, o), p):]
         dms = timed(lambda: dsp.crisp_dense_attn(q, k, v, o=o, ws=aws), reps, 2, torch)
         nb = n // 128
+        density = int(sel.row_ptr[-1].item()) / (32 * nb * (nb + 1) // 2)
+        # with the length gate at the measured crossover: below it the prefill takes the dense path
+        pg = dsp.CrispParams(tau=cfg.tau, alpha=cfg.alpha, gamma=cfg.gamma, dense_below_n=LENGTH_GATE)
+        gated = timed(lambda: dsp.crisp_prefill(q, k, v, pg, sel=sel, o=o, ws=ws), reps, 2, torch) if n < LENGTH_GATE else ms
         res[n] = {"crisp_ms": round(ms, 3), "crisp_graph_ms": round(gms, 3), "dense_ms": round(dms, 3),
                   "speedup": round(dms / ms, 3), "speedup_graph": round(dms / gms, 3),
-                  "density": round(int(sel.row_ptr[-1].item()) / (32 * nb * (nb + 1) // 2), 4)}
+                  "crisp_gated_ms": round(gated, 3), "speedup_gated": round(dms / gated, 3),
+                  "density": round(density, 4)}
         log(f"[bench] length {n}: {res[n]}")
         del graph, q, k, v, o, sel, ws, aws
         torch.cuda.empty_cache()

@@ -42,15 +42,19 @@
 namespace crisp {
 
 constexpr int NQUEUE = 8;  // work queues of the persistent attention kernel (one per XCD)
-// Sparse attention walks the item order twice, each pass with its own NQUEUE
-// counters: first it takes only the items whose lists cover more than a
-// quarter of their causal key blocks, then the rest (dense attention makes one
-// pass over all items).  Long items then start in waves of about equal length,
-// as in dense attention, and the work-groups of an XCD walk the same K / V
-// tiles of their KV group at about the same time, sharing them through L2;
-// with short items interleaved, long ones would start at scattered times and
-// walk unrelated tiles.  The short items fill the end of the launch.
+// Sparse attention of long sequences walks the item order twice, each pass
+// with its own NQUEUE counters: first it takes only the items whose lists
+// cover more than a quarter of their causal key blocks, then the rest.  Long
+// items then start in waves of about equal length, as in dense attention, and
+// the work-groups of an XCD walk the same K / V tiles of their KV group at
+// about the same time, sharing them through L2; with short items interleaved,
+// long ones would start at scattered times and walk unrelated tiles.  The
+// short items fill the end of the launch.  The second walk costs every
+// work-group a pull from each queue; with a few items per CU (sequences under
+// TWO_PASS_NB blocks) that outweighs the locality, and sparse attention makes
+// one pass over all items, as dense attention always does.
 constexpr int NPHASE = 2;
+constexpr int TWO_PASS_NB = 256;
 
 // ------------------------------------------------------------------ V re-layout
 
@@ -428,15 +432,15 @@ __device__ __forceinline__ void fa_bf16_item(
 
 // Persistent loop: one work-group per CU takes items from the queues until
 // all are empty.  `queue` holds NQUEUE counters per pass, zero at launch.
-// Dense: one pass over every item.  Sparse: pass 1 takes only the items whose
-// two lists hold more than a quarter of the pair's causal key blocks, pass 2
-// the others.
+// passes == 1: one pass over every item.  passes == 2 (sparse only): the
+// first pass takes only the items whose two lists hold more than a quarter of
+// the pair's causal key blocks, the second the others.
 template <bool DENSE>
 __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt, bf16* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue,
     const SeqTable sq, int nb_total, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n,
-    int64_t so_h, int64_t so_n, float sl2) {
+    int64_t so_h, int64_t so_n, float sl2, int passes) {
   // two stages of (K, V^T) tiles, each stage tile its own array
   __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
   __shared__ int s_item;
   const int home = blockIdx.x % NQUEUE;
   const int64_t vt_h = (int64_t)nb_total * (BLK * HD);
-  for (int pass = 0; pass < (DENSE ? 1 : NPHASE); ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     int* qs = queue + NQUEUE * pass;
     for (int k = 0; k < NQUEUE; ++k) {
       const int x = (home + k) % NQUEUE;
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
         __syncthreads();
         int seq, pair, kvh, h;
         if (!queue_item(x, s_item, sq, hq, hkv, seq, pair, kvh, h)) break;
-        if (!DENSE) {                               // long items in pass 0, short ones in pass 1
+        if (!DENSE && passes > 1) {                 // long items in pass 0, short ones in pass 1
           const int nbs = sq.nb[seq], qlo = 2 * pair;
           const int32_t* rp = row_ptr + sq.rp[seq] + (int64_t)h * nbs + qlo;
           const bool two = qlo + 1 < nbs;
@@ -599,9 +603,10 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
     int64_t nb_max = 0;
     for (int i = 0; i < t.nseq; ++i) nb_max = std::max<int64_t>(nb_max, t.nb[i]);
     t.pair_major = 2 * (int64_t)hkv * nb_max * BLK * HD * 2 <= (int64_t(256) << 20);
+    const int passes = (!dense && nb_max >= TWO_PASS_NB) ? NPHASE : 1;
     auto k = dense ? fa_bf16_kernel<true> : fa_bf16_kernel<false>;
     k<<<grid, 512, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)Vt, (bf16*)O, row_ptr, col_idx, queue, t,
-                           nb_total, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2);
+                           nb_total, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, st.o_h, st.o_n, sl2, passes);
   }
   return hipGetLastError();
 }

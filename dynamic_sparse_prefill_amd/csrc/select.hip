@@ -501,16 +501,33 @@ __global__ __launch_bounds__(1024) void vs_rank_kernel(const int32_t* __restrict
 
 // ------------------------------------------------------------------ PE: pooled Q
 
+// The work-groups of head vh also reset its radix-select state for the passes
+// that follow: each clears a slice of the three passes' histograms, work-group
+// (0, vh) the cut state.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, const int32_t* __restrict__ route,
                                                      float* __restrict__ qbar, const SeqList seqs, int hq, int hkv,
-                                                     int64_t sq_h, int64_t sq_n, int* __restrict__ queue) {
+                                                     int64_t sq_h, int64_t sq_n, int* __restrict__ queue,
+                                                     PeCut* __restrict__ cut, uint32_t* __restrict__ hcnt,
+                                                     unsigned long long* __restrict__ hmass, float gamma) {
   constexpr int E = 16 / sizeof(T);         // elements per 16-byte load
   constexpr int CPR = HD / E;               // 16-byte chunks per row
   constexpr int RG = 256 / CPR;             // row groups
   __shared__ float red[RG][HD];
   const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
   if (queue && qb == 0 && vh == 0 && tid == 0) *queue = 0;   // the logits kernel's work counter
+  {
+    uint32_t* c = hcnt + (int64_t)vh * 3 * PE_BUCKETS;
+    unsigned long long* m = hmass + (int64_t)vh * 3 * PE_BUCKETS;
+    const int per = (3 * PE_BUCKETS + gridDim.x - 1) / gridDim.x;
+    const int i1 = min(3 * PE_BUCKETS, (qb + 1) * per);
+    for (int i = qb * per + tid; i < i1; i += 256) { c[i] = 0; m[i] = 0; }
+    if (qb == 0 && tid == 0) {
+      PeCut z = {};
+      z.active = (route[vh] == 0 && gamma < 1.f) ? 1 : 0;
+      cut[vh] = z;
+    }
+  }
   if (route[vh] != 0) return;
   const int h = vh % hq;
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
@@ -762,20 +779,6 @@ __global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict_
 // ------------------------------------------------------------------ PE: radix select of the gamma cut
 
 constexpr int PE_SLICE = 32768;  // entries per histogram work-group
-
-__global__ void pe_cut_init_kernel(const int32_t* __restrict__ route, PeCut* __restrict__ cut,
-                                   uint32_t* __restrict__ hcnt, unsigned long long* __restrict__ hmass,
-                                   float gamma) {
-  const int h = blockIdx.x, tid = threadIdx.x;
-  uint32_t* c = hcnt + (int64_t)h * 3 * PE_BUCKETS;
-  unsigned long long* m = hmass + (int64_t)h * 3 * PE_BUCKETS;
-  for (int i = tid; i < 3 * PE_BUCKETS; i += blockDim.x) { c[i] = 0; m[i] = 0; }
-  if (tid == 0) {
-    PeCut z = {};
-    z.active = (route[h] == 0 && gamma < 1.f) ? 1 : 0;
-    cut[h] = z;
-  }
-}
 
 __host__ __device__ constexpr int pe_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __host__ __device__ constexpr int pe_width(int pass) { return pass == 2 ? 10 : 11; }
@@ -1160,6 +1163,40 @@ __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* 
   for (int i = threadIdx.x; i < b; i += blockDim.x) if (ss_out) ss_out[rowb + i] = ss[rowb + i];
 }
 
+// Every sequence on the dense path (N_b <= 2 or below the length gate): one
+// launch writes the whole selection.  Work-group (qb, vh) writes row qb of
+// virtual head vh; a dense row qb holds key blocks 0..qb, so its offset in the
+// sequence's CSR has the closed form h * N_b(N_b+1)/2 + qb(qb+1)/2.  Work-group
+// (0, vh) also writes the head's route (-1), C_struct (0), empty direction sets
+// and, when the JSD router is on, a zero divergence: what the general kernels
+// write for a dense sequence.
+__global__ __launch_bounds__(256) void dense_selection_kernel(int32_t* __restrict__ route, float* __restrict__ c_struct,
+                                                              int32_t* __restrict__ nv, int32_t* __restrict__ ns,
+                                                              int32_t* nv_out, int32_t* ns_out, double* jsd,
+                                                              int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
+                                                              const SeqList seqs, int hq, int hkv) {
+  const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb, hl = vh % hq;
+  if (qb == 0 && tid == 0) {
+    route[vh] = -1;
+    c_struct[vh] = 0.f;
+    nv[vh] = 0;
+    ns[vh] = 0;
+    if (nv_out) nv_out[vh] = 0;
+    if (ns_out) ns_out[vh] = 0;
+    if (jsd) jsd[vh] = 0.0;
+  }
+  if (qb >= nb) return;
+  const int64_t base = (int64_t)hl * tri(nb) + tri(qb);
+  if (tid == 0) {
+    row_ptr[sp.rp + (int64_t)hl * nb + qb] = (int32_t)base;
+    if (hl == hq - 1 && qb == nb - 1) row_ptr[sp.rp + (int64_t)hq * nb] = (int32_t)(base + qb + 1);
+  }
+  int32_t* out = col + sp.tri + base;
+  for (int k = tid; k <= qb; k += 256) out[k] = k;
+}
+
 // ------------------------------------------------------------------ launcher
 
 hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_max, int hq, int hkv,
@@ -1167,6 +1204,14 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
                          int min_blocks, int dense_below_n, const SelectBufs& b, hipStream_t s) {
   const unsigned vh = (unsigned)(seqs.nseq * hq);   // virtual heads: (sequence, query head)
   const bool jsd_on = b.router == 1;
+  bool all_dense = true;
+  for (int i = 0; i < seqs.nseq; ++i) all_dense = all_dense && seq_dense(seqs.nb[i], dense_below_n);
+  if (all_dense) {
+    dense_selection_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, b.c_struct, b.nv, b.ns, b.nv_out, b.ns_out,
+                                                            jsd_on ? b.jsd : nullptr, b.row_ptr, b.col_idx, seqs,
+                                                            hq, hkv);
+    return hipGetLastError();
+  }
   if (jsd_on) {
     const float scale = 1.f / sqrtf((float)HD);
     if (fp32)
@@ -1193,16 +1238,17 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   const int pe_all = gamma >= 1.f ? 1 : 0;
   const dim3 gq(nb_max, vh);
   if (fp32)
-    pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq);
+    pool_q_kernel<float><<<gq, 256, 0, s>>>((const float*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq,
+                                            cut, b.hcnt, b.hmass, gamma);
   else
-    pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq);
+    pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq,
+                                           cut, b.hcnt, b.hmass, gamma);
   const int nrb = (nb_max + 31) / 32, nseg = pe_segments(nb_max);
   const int pe_items = ((nrb + PE_RB - 1) / PE_RB) * nseg * vh;
   pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
       pe_items);
   pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
-  pe_cut_init_kernel<<<vh, 256, 0, s>>>(b.route, cut, b.hcnt, b.hmass, gamma);
   const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
   pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
   pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);

@@ -181,6 +181,49 @@ def test_dense_fallback_paths():
     P.check_attention_blocks(spec3, Q3, K3, V3, o3, lambda h, qb: [0], range(4), [0])
 
 
+def test_length_gate_whole_batch_dense():
+    """Every sequence of a packed batch below the length gate: the selection is
+    written by one launch (route -1, full lists) and equals single calls; the
+    output equals dense attention on each sequence and the oracle's on sampled
+    blocks."""
+    lens = [2048, 512, 4096]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    hq, hkv = 4, 2
+    parts = []
+    for i, n in enumerate(lens):
+        cfg = synth.custom_config(f"gated{i}", n, hq, hkv, seed=120 + i, conc_frac=0.5)
+        spec = synth.make_spec(cfg)
+        parts.append((spec,) + synth.generate(spec))
+    spec0 = parts[0][0]
+    q = P.to_device(spec0, np.concatenate([p[1] for p in parts], axis=1))
+    k = P.to_device(spec0, np.concatenate([p[2] for p in parts], axis=1))
+    v = P.to_device(spec0, np.concatenate([p[3] for p in parts], axis=1))
+    params = P.params_of(spec0.cfg, dense_below_n=8192, flags=dsp.FLAG_ROUTE_JSD)
+    o, sel = dsp.crisp_prefill_varlen(q, k, v, cu, params)
+    torch.cuda.synchronize()
+    assert sel.route.cpu().tolist() == [-1] * (hq * len(lens))
+    assert torch.all(sel.c_struct == 0) and torch.all(sel.nv == 0) and torch.all(sel.jsd == 0)
+    rp0, col0 = 0, 0
+    for i, n in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        nb = n // 128
+        qi, ki, vi = q[:, a:b].contiguous(), k[:, a:b].contiguous(), v[:, a:b].contiguous()
+        oi, si = dsp.crisp_prefill(qi, ki, vi, params)
+        od = dsp.crisp_dense_attn(qi, ki, vi)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, a:b], oi) and torch.equal(oi, od), f"sequence {i}"
+        assert torch.equal(sel.row_ptr[rp0:rp0 + hq * nb + 1], si.row_ptr)
+        assert np.array_equal(np.diff(si.row_ptr.cpu().numpy()), np.tile(np.arange(1, nb + 1), hq))
+        m = int(si.row_ptr[-1])
+        assert torch.equal(sel.col_idx[col0:col0 + m], si.col_idx[:m])
+        assert si.col_idx[:m].cpu().tolist() == [kb for _ in range(hq) for qb in range(nb) for kb in range(qb + 1)]
+        rp0 += hq * nb + 1
+        col0 += hq * nb * (nb + 1) // 2
+    sp, Q0, K0, V0 = parts[2]
+    P.check_attention_blocks(sp, Q0, K0, V0, o[:, cu[2]:cu[3]], lambda h, qb: range(qb + 1), range(hq),
+                             synth.sample_blocks(sp.cfg.nb, 6, 9))
+
+
 def test_parameter_sweep_and_min_blocks():
     cfg = synth.custom_config("sweep", 8192, 8, 2, seed=31, conc_frac=0.5)
     spec = synth.make_spec(cfg)
