@@ -8,7 +8,8 @@
 //  pool_q      block means of Q for Pooled-Estimation heads.
 //  pe_logits   pooled logits Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb (fp32
 //              MFMA), with per-segment row max / sum;
-//  pe_norm     the causal row softmax in one pass [CRISP §2, PE path].
+//  pe_norm_hist the causal row softmax [CRISP §2, PE path], in place, in
+//              the same sweep as the first radix pass of the cut;
 //  pe_hist/    global gamma-cut over the flattened causal matrix: a radix
 //  pe_scan     select on the float32 bit pattern (11+11+10 bits, three
 //              passes) with per-bucket mass in 2^-46 fixed point, so the sums
@@ -741,41 +742,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
-// Row softmax in place: one work-group per (query block, Pooled-Estimation
-// head) merges the row's segment maxima and sums, then P = exp(L - M) / S.
-__global__ __launch_bounds__(256) void pe_norm_kernel(const int32_t* __restrict__ route, const float2* __restrict__ part,
-                                                      float* __restrict__ P, const SeqList seqs, int hq, int hkv,
-                                                      int nseg) {
-  const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
-  if (route[vh] != 0) return;
-  const int h = vh % hq;
-  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
-  const int nb = sp.nb;
-  if (qb >= nb) return;
-  P += sp.tri;
-  const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;   // segments this row block produced
-  const float2* pp = part + (sp.rows + (int64_t)h * nb + qb) * nseg;
-  float M = -INFINITY;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
-  float S = 0.f;
-  for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * pe_exp(pp[c].x - M);
-  const float inv = 1.f / S;
-  float* row = P + (int64_t)h * tri(nb) + tri(qb);
-  for (int k0 = 0; k0 <= qb; k0 += 2048) {
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kb = k0 + 256 * j + tid;
-      x[j] = kb <= qb ? row[kb] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kb = k0 + 256 * j + tid;
-      if (kb <= qb) row[kb] = pe_exp(x[j] - M) * inv;
-    }
-  }
-}
-
 // ------------------------------------------------------------------ PE: radix select of the gamma cut
 
 constexpr int PE_SLICE = 32768;  // entries per histogram work-group
@@ -861,6 +827,135 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
   __syncthreads();
   uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  for (int i = tid; i < PE_BUCKETS; i += 256)
+    if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
+}
+
+// Row softmax and the first radix pass in one sweep.  Work-group (slice, vh)
+// takes entries [slice * PE_SLICE, +PE_SLICE) of Pooled-Estimation head vh's
+// flattened causal triangle (at most 256 rows: rows 0..255 already hold more
+// than PE_SLICE entries): it merges each of its rows' segment maxima and sums
+// into the row's max M and 1/S, then replaces every logit x in place by
+// P = exp(x - M) / S and, when the head's cut is active, adds P to the pass-0
+// histogram.  The same values as a separate normalising pass, one read of the
+// matrix fewer.
+__device__ __forceinline__ int tri_row(int64_t e) {   // the row qb with tri(qb) <= e < tri(qb + 1)
+  int r = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+  while (tri(r + 1) <= e) ++r;
+  while (tri(r) > e) --r;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void pe_norm_hist_kernel(const int32_t* __restrict__ route,
+                                                           const float2* __restrict__ part, float* __restrict__ P,
+                                                           const PeCut* __restrict__ cut,
+                                                           uint32_t* __restrict__ hcnt,
+                                                           unsigned long long* __restrict__ hmass, const SeqList seqs,
+                                                           int hq, int hkv, int nseg) {
+  __shared__ uint32_t sc[PE_BUCKETS];
+  __shared__ unsigned long long sm[PE_BUCKETS];
+  __shared__ float sM[256], sInv[256];
+  const int h = blockIdx.y, tid = threadIdx.x;   // h: virtual head
+  if (route[h] != 0) return;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  const int64_t total = tri(nb);
+  const int64_t a = (int64_t)blockIdx.x * PE_SLICE;
+  if (a >= total) return;
+  const int64_t b = min(total, a + PE_SLICE);
+  const bool active = cut[h].active;
+  float* Ph = P + sp.tri + (int64_t)(h % hq) * total;
+  const int r0 = tri_row(a), r1 = tri_row(b - 1);
+  if (tid <= r1 - r0) {   // this row's normaliser, as the separate softmax pass forms it
+    const int qb = r0 + tid;
+    const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;
+    const float2* pp = part + (sp.rows + (int64_t)(h % hq) * nb + qb) * nseg;
+    float M = -INFINITY;
+    for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
+    float S = 0.f;
+    for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * pe_exp(pp[c].x - M);
+    sM[tid] = M;
+    sInv[tid] = 1.f / S;
+  }
+  for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
+  __syncthreads();
+  constexpr uint32_t mask = (1u << pe_width(0)) - 1;
+  uint32_t run_b = 0xffffffffu, run_c = 0;
+  unsigned long long run_m = 0;
+  auto take = [&](uint32_t x) {
+    const uint32_t bk = (x >> pe_shift(0)) & mask;
+    if (bk != run_b) {
+      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+      run_b = bk;
+      run_c = 0;
+      run_m = 0;
+    }
+    ++run_c;
+    run_m += fx_mass(x);
+  };
+  // normalise entry e (row r, tracked forward from the previous entry of the thread)
+  auto norm = [&](int64_t e, int& r, float x) -> float {
+    while (tri(r + 1) <= e) ++r;
+    return pe_exp(x - sM[r - r0]) * sInv[r - r0];
+  };
+  constexpr int U = 4;
+  if (((uintptr_t)Ph & 15) == 0) {
+    // 16-byte loads of four consecutive entries, four loads in flight per thread
+    for (int64_t e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
+      float4 xs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 1024 * u;
+        if (e + 4 <= b) xs[u] = *(const float4*)(Ph + e);
+        else xs[u] = make_float4(e < b ? Ph[e] : 0.f, e + 1 < b ? Ph[e + 1] : 0.f, e + 2 < b ? Ph[e + 2] : 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 1024 * u;
+        if (e >= b) break;
+        int r = tri_row(e);
+        float4 y;
+        y.x = norm(e, r, xs[u].x);
+        y.y = e + 1 < b ? norm(e + 1, r, xs[u].y) : 0.f;
+        y.z = e + 2 < b ? norm(e + 2, r, xs[u].z) : 0.f;
+        y.w = e + 3 < b ? norm(e + 3, r, xs[u].w) : 0.f;
+        if (e + 4 <= b) {
+          *(float4*)(Ph + e) = y;
+        } else {
+          Ph[e] = y.x;
+          if (e + 1 < b) Ph[e + 1] = y.y;
+          if (e + 2 < b) Ph[e + 2] = y.z;
+        }
+        if (active) {
+          take(__float_as_uint(y.x));
+          if (e + 1 < b) take(__float_as_uint(y.y));
+          if (e + 2 < b) take(__float_as_uint(y.z));
+          if (e + 3 < b) take(__float_as_uint(y.w));
+        }
+      }
+    }
+  } else {
+    // four strided entries are loaded before any is used
+    for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
+      float xs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? Ph[e0 + 256 * u] : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 256 * u;
+        if (e >= b) break;
+        int r = tri_row(e);
+        const float y = norm(e, r, xs[u]);
+        Ph[e] = y;
+        if (active) take(__float_as_uint(y));
+      }
+    }
+  }
+  if (!active) return;
+  if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+  __syncthreads();
+  uint32_t* gc = hcnt + (int64_t)h * 3 * PE_BUCKETS;
+  unsigned long long* gm = hmass + (int64_t)h * 3 * PE_BUCKETS;
   for (int i = tid; i < PE_BUCKETS; i += 256)
     if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
 }
@@ -1248,9 +1343,9 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
       pe_items);
-  pe_norm_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, seqs, hq, hkv, nseg);
   const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
-  pe_hist_kernel<0><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  pe_norm_hist_kernel<<<gh, 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv,
+                                         nseg);
   pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
   pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
   pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);

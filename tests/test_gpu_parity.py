@@ -224,6 +224,32 @@ def test_length_gate_whole_batch_dense():
                              synth.sample_blocks(sp.cfg.nb, 6, 9))
 
 
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_length_sweep_layers(n):
+    """The Llama-shaped 4k and 8k layers the bench's length sweep times (same
+    generator and seed): every decision of every head bit-exact, every head's
+    proxy scores against the oracle, every output row of every head; then the
+    same layer with the length gate at 8192 tokens (4k: the dense path)."""
+    cfg = synth.custom_config(f"llama-shape-{n // 1024}k", n, 32, 8, seed=7, conc_frac=0.6)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    p = P.params_of(cfg)
+    q, k, v, o, sel = _run_layer(spec, Q, K, V, p)
+    rep = P.check_decisions(sel, cfg.hq, cfg.nb, p, name=cfg.name)
+    assert rep["heads_checked"] + rep["pe_exempt"] == cfg.hq, rep
+    P.log(f"[{cfg.name}] score err", P.check_score_fidelity(spec, Q, K, sel, range(cfg.hq)))
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, _lists_fn(sel, cfg.nb), range(cfg.hq), range(cfg.nb))
+    P.log(f"[{cfg.name}] attention (every row) max {mx:.2e} mean {mean:.2e}")
+    pg = P.params_of(cfg, dense_below_n=8192)
+    og, selg = dsp.crisp_prefill(q, k, v, pg)
+    torch.cuda.synchronize()
+    if n < 8192:
+        assert selg.route.cpu().tolist() == [-1] * cfg.hq
+        assert torch.equal(og, dsp.crisp_dense_attn(q, k, v))
+    else:
+        assert torch.equal(selg.route, sel.route) and torch.equal(og, o)
+
+
 def test_parameter_sweep_and_min_blocks():
     cfg = synth.custom_config("sweep", 8192, 8, 2, seed=31, conc_frac=0.5)
     spec = synth.make_spec(cfg)
