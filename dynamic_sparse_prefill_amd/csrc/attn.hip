@@ -152,6 +152,21 @@ constexpr int TILE_BYTES = BLK * 256;  // one K or V^T tile in LDS
 // (sq.pair_major), units go pair by pair over all KV groups, longest rows
 // first: plain longest-first packing, which evens out the end of a short
 // launch (8k-64k tokens: 5-12% faster; at 512k it costs 8%).
+// Rank rho (0 = longest) of a group's np pairs, dealt to S queues in turn
+// (queue rho % S takes its (rho / S)-th pair), mapped to the pair rank that
+// queue gets: chunks of PAIR_CHUNK consecutive ranks, the S queues taking
+// chunks in turn, so the items an XCD runs at one time are of neighbouring
+// pairs (about equal lengths, nearly the same key blocks) rather than of every
+// S-th pair; the ranks past the last whole round of chunks keep their order.
+// A bijection on [0, np).
+constexpr int PAIR_CHUNK = 16;
+__device__ __forceinline__ int chunked_rank(int rho, int np, int S) {
+  const int round = S * PAIR_CHUNK, whole = (np / round) * round;
+  if (rho >= whole) return rho;
+  const int q = rho % S, k = rho / S;
+  return PAIR_CHUNK * (S * (k / PAIR_CHUNK) + q) + k % PAIR_CHUNK;
+}
+
 __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int hkv, int& seq, int& pair, int& kvh,
                                   int& h) {
   const int G = hq / hkv;
@@ -171,10 +186,10 @@ __device__ inline bool queue_item(int x, int t, const SeqTable& sq, int hq, int 
   const int gp = v / (2 * np), r = v % (2 * np);
   if (2 * gp + 1 < hkv) {
     kvh = 2 * gp + (r & 1);
-    pair = np - 1 - (r >> 1);
+    pair = np - 1 - chunked_rank(r >> 1, np, NQUEUE / 2);
   } else {                                                  // odd group count: the last group alone
     kvh = 2 * gp;
-    pair = np - 1 - r;
+    pair = np - 1 - chunked_rank(r, np, NQUEUE);
   }
   h = kvh * G + t % G;
   return true;
