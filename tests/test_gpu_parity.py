@@ -468,6 +468,81 @@ def test_llama_512k_layer():
     _drop_layers()
 
 
+@pytest.mark.timeout(1200)
+def test_maximum_length_layer():
+    """The longest sequence the ABI takes: N_b = 32768 blocks (4,194,304
+    tokens), one concentrated and one diffuse query head with their own KV
+    heads.  The pooled triangle and the worst-case list capacity hold 537M
+    entries per head, so the 64-bit offsets of the pooled matrix, the lists and
+    the row scan are all exercised.  The Vertical-Slash head: every decision
+    bit-exact against the oracle.  The Pooled-Estimation head (the oracle's
+    sort of 537M entries is out of reach): the properties every correct cut has,
+    checked on the GPU's own float32 P in float64 -- rows that sum to one, the
+    selected mass at least gamma of the total (up to the fixed-point bound),
+    every unselected entry no larger than the smallest selected non-anchor
+    entry, lists ascending with both anchors.  Output rows of both heads on
+    sampled query blocks against the oracle."""
+    n = 32768 * 128
+    cfg = synth.custom_config("max-nb-32768", n, 2, 2, seed=211, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    assert spec.concentrated.tolist() == [True, False]
+    Q, K, V = P.load_layer(spec)
+    q, k, v = P.to_device(spec, Q), P.to_device(spec, K), P.to_device(spec, V)
+    p = P.params_of(cfg)
+    o, sel = dsp.crisp_prefill(q, k, v, p, pe_prob=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    nb = cfg.nb
+    assert sel.route.cpu().tolist() == [1, 0], sel.route
+    rep = P.check_decisions(sel, cfg.hq, nb, p, heads=[0], name=cfg.name)
+    assert rep["heads_checked"] == 1, rep
+    P.log(f"[{cfg.name}] score err (VS head)", P.check_score_fidelity(spec, Q, K, sel, [0]))
+    # the Pooled-Estimation head's cut, on the GPU's own probabilities (float64 on the device)
+    T = nb * (nb + 1) // 2
+    Pf = sel.pe_prob[T:2 * T].double()
+    starts = torch.arange(nb, device="cuda", dtype=torch.int64)
+    starts = starts * (starts + 1) // 2
+    cs = torch.cumsum(Pf, 0)
+    ends = cs[starts + torch.arange(nb, device="cuda")]
+    row_sums = ends - torch.cat([torch.zeros(1, device="cuda", dtype=torch.float64), ends[:-1]])
+    assert float((row_sums - 1).abs().max()) < 1e-4
+    total = float(cs[-1])
+    rp = sel.row_ptr.to(torch.int64)
+    a, b = int(rp[nb]), int(rp[2 * nb])
+    cols = sel.col_idx[a:b].to(torch.int64)
+    lens = (rp[nb + 1:2 * nb + 1] - rp[nb:2 * nb])
+    rows = torch.repeat_interleave(torch.arange(nb, device="cuda"), lens)
+    assert bool((cols <= rows).all()) and bool((cols >= 0).all())
+    first = rp[nb:2 * nb] - a
+    last = rp[nb + 1:2 * nb + 1] - a - 1
+    assert bool((cols[first] == 0).all()) and bool((cols[last] == torch.arange(nb, device="cuda")).all())
+    inner = torch.ones_like(cols, dtype=torch.bool)
+    inner[first] = False
+    assert bool((cols[1:][inner[1:]] > cols[:-1][inner[1:]]).all())          # ascending within each row
+    flat = starts[rows] + cols
+    chosen = torch.zeros(T, dtype=torch.bool, device="cuda")
+    chosen[flat] = True
+    mass = float(Pf[chosen].sum())
+    gamma = float(np.float32(p.gamma))                  # the cut is taken at the float32 parameter
+    assert mass >= gamma * total - T * 2.0 ** -45, (mass, total)
+    anchor = torch.zeros(T, dtype=torch.bool, device="cuda")
+    anchor[starts] = True
+    anchor[starts + torch.arange(nb, device="cuda")] = True
+    smallest_kept = float(Pf[chosen & ~anchor].min())
+    largest_dropped = float(Pf[~chosen].max())
+    assert largest_dropped <= smallest_kept, (largest_dropped, smallest_kept)
+    density = (b - a) / T
+    P.log(f"[{cfg.name}] PE head: kept mass {mass / total:.6f} of {total:.1f}, density {density:.3f}, "
+          f"dropped <= {largest_dropped:.3e} <= kept {smallest_kept:.3e}")
+    del Pf, cs, chosen, anchor, flat, rows
+    torch.cuda.empty_cache()
+    rpn, col = P.gpu_lists(sel, cfg.hq, nb)
+    blocks = synth.sample_blocks(nb, 4, 12)
+    mx, mean = P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: col[rpn[h * nb + qb]: rpn[h * nb + qb + 1]],
+                                        [0, 1], blocks, threads=3)
+    P.log(f"[{cfg.name}] attention (2 heads x {len(blocks)} blocks) max {mx:.2e} mean {mean:.2e}")
+
+
 @pytest.mark.timeout(900)
 def test_odd_kv_count_beyond_cache():
     """Three KV groups at 196,608 tokens: K and V take 302 MB, more than the
