@@ -133,6 +133,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* p, int b
 
 constexpr int TILE_BYTES = BLK * 256;  // one K or V^T tile in LDS
 
+// Offset operand of the V^T reads of one key chunk.  A DS read adds only a
+// 16-bit constant to its address register.  The K stages take the first 64 KiB
+// of LDS, so every K read folds stage, tile and chunk into that constant; the
+// V^T stages lie above, so the register has to carry the stage-0 V^T address.
+// The empty asm stops the compiler from folding that address back into a new
+// constant per read (one VALU op per read); the reads still index the stage
+// arrays, which is how the compiler tells them from the copy into the other
+// stage and issues no wait for it.
+__device__ __forceinline__ uint32_t vt_operand(uint32_t lane_off, uint32_t vbase) {
+  uint32_t r = lane_off + vbase;
+  __asm__ volatile("" : "+v"(r));
+  return r - vbase;
+}
+
 // Work queues.  The kernel is persistent (one work-group per CU).  A unit of
 // work is one (query-block pair, KV head) with its G query heads, whose items
 // are consecutive in a queue so they run side by side and share each K/V tile
@@ -317,6 +331,7 @@ __device__ __forceinline__ void fa_bf16_item(
 
   Tile<bf16>::QFrag qf;
   if (rows_ok) Tile<bf16>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)(qmine * BLK + qrow) * sq_n, g);
+  const uint32_t vbase = (uint32_t)(uintptr_t)(lds_void*)sV0;
   uint32_t kx[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
@@ -357,8 +372,9 @@ __device__ __forceinline__ void fa_bf16_item(
 #pragma unroll
           for (int t = 0; t < 4; ++t) fk[(c + 1) & 1][t] = *(const bf16x8*)(cK + kx[c + 1] + 8192 * t);
         } else {
+          const uint32_t kv = vt_operand(kx[0], vbase);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) fv[0][u] = *(const bf16x8*)(cV + kx[0] + 8192 * u);
+          for (int u = 0; u < 4; ++u) fv[0][u] = *(const bf16x8*)(cV + kv + 8192 * u);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -413,8 +429,9 @@ __device__ __forceinline__ void fa_bf16_item(
 #pragma unroll
       for (int mm = 0; mm < 8; ++mm) {
         if (mm + 1 < 8) {
+          const uint32_t kv = vt_operand(kx[mm + 1], vbase);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) fv[(mm + 1) & 1][u] = *(const bf16x8*)(cV + kx[mm + 1] + 8192 * u);
+          for (int u = 0; u < 4; ++u) fv[(mm + 1) & 1][u] = *(const bf16x8*)(cV + kv + 8192 * u);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -456,10 +473,10 @@ __global__ __launch_bounds__(512, 2) void fa_bf16_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int* __restrict__ queue,
     const SeqTable sq, int nb_total, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n,
     int64_t so_h, int64_t so_n, float sl2, int passes) {
-  // two stages of (K, V^T) tiles, each stage tile its own array
+  // two stages of (K, V^T) tiles, each stage tile its own array; K first (see vt_operand)
   __shared__ __attribute__((aligned(1024))) char sK0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[TILE_BYTES];
   __shared__ int s_item;
   const int home = blockIdx.x % NQUEUE;

@@ -40,8 +40,8 @@ def _equal_selection(a, b, nb, hq):
 
 
 def test_noalloc_prefill_equals_prefill_twice_shrinking():
-    # a layer near the scratch limit first, then a smaller one
-    for n, hq, hkv, seed in ((24576, 16, 4, 301), (2048, 4, 2, 302)):
+    # a layer using about 3/4 of the scratch first, then a smaller one
+    for n, hq, hkv, seed in ((65536, 16, 4, 301), (2048, 4, 2, 302)):
         spec, host, (q, k, v) = _layer(n, hq, hkv, seed)
         cfg = spec.cfg
         p = P.params_of(cfg)
@@ -69,9 +69,12 @@ def test_noalloc_prefill_equals_prefill_twice_shrinking():
         P.check_attention_blocks(spec, Q, K, V, o, lambda h, qb: col[rp[h * cfg.nb + qb]: rp[h * cfg.nb + qb + 1]],
                                  range(hq), synth.sample_blocks(cfg.nb, 6, 3))
         P.log(f"[noalloc n={n}] equal to crisp_prefill; decisions {rep}")
-    # beyond the scratch: rejected, nothing launched
-    spec, _, (q, k, v) = _layer(65536, 8, 8, 303)
-    p = P.params_of(spec.cfg)
+    # beyond the scratch: rejected before anything is launched (inputs need no values)
+    n_big, hq, hkv = 131072, 32, 8
+    z = lambda h: torch.zeros(h, n_big, 128, dtype=torch.bfloat16, device="cuda")
+    q, k, v = z(hq), z(hkv), z(hkv)
+    p = dsp.CrispParams()
+    assert dsp.workspace_bytes(dsp.make_shape(q, k, v, q), p) > dsp.noalloc_scratch_bytes()
     with pytest.raises(dsp.CrispError) as e:
         dsp.crisp_prefill_noalloc(q, k, v, p, dsp.new_selection(q, k), torch.empty_like(q))
     assert e.value.status == -5
