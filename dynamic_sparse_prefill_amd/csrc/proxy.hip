@@ -32,9 +32,6 @@
 namespace crisp {
 
 constexpr int PCH = 16;       // most key blocks per score work-group (fewer when the grid would be small)
-// query heads of a KV group per score work-group: they share each K tile the
-// group loads (bf16; the fp32 path's query fragments are twice as large)
-template <typename T> constexpr int proxy_heads() { return sizeof(T) == 2 ? 2 : 1; }
 constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 
 int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
@@ -71,44 +68,263 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
   }
 }
 
-// K-bar partials of a staged bf16 tile for wave w: column sums over the
-// wave's 32 rows (4w + k + 16i), the lanes that share columns added pairwise
-// (lane ^ 16, then lane ^ 32), written by lanes 0..15 to dst[w][0..127].
-__device__ __forceinline__ void kbar_partials(float (*dst)[HD], const Tile<bf16>::KStage& stg, int w, int lane) {
-  float cs[8];
-  Tile<bf16>::col_sums(cs, stg);
+// ---- bf16 score pass: 8 waves per work-group, one query head per 4 waves
+//
+// Two query heads of a KV group share each K tile, which is
+// copied into LDS by the tile loads themselves (buffer_load ... lds, no
+// register staging), two stages deep.  Wave w serves head h0 + w/4 and query
+// rows 32(w%4) .. +31; it takes S^T of a tile in two halves of 64 keys, so a
+// wave needs about half the registers of a whole tile and four waves fit on
+// each SIMD (two work-groups per CU, 72 KiB of LDS each, which keeps the two
+// out of step with each other).  The row's tile max is the max of the two half
+// maxima: the sums of the first half, taken relative to its own max, are
+// rescaled once when the second half raises it.
+constexpr int PX_HEADS = 2, PX_WAVES = 4 * PX_HEADS, PX_ROWS = BLK / PX_WAVES;   // PX_ROWS: K rows copied per wave
+
+typedef __attribute__((address_space(3))) void px_lds_void;
+constexpr int PX_WAIT_VM0 = 0x0F70;   // s_waitcnt: vector-memory count 0 only
+
+__device__ __forceinline__ void px_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 16-byte chunk c of K row r sits at chunk c ^ (r & 15) of the row's 256 bytes:
+// the 32 lanes reading one chunk of 32 consecutive rows hit 16 bank groups
+// twice, every pair conflict-free.  Wave w copies rows PX_ROWS w .. + PX_ROWS-1
+// with 1 KB loads (lane L of load i: row PX_ROWS w + 4i + L/16, physical chunk
+// L % 16).
+struct PxCopy {   // the offsets are formed at each issue: a few ALU ops per tile, no registers held
+  uint32_t row_bytes;
+  int w, lane;
+  __device__ void issue(const bf16* tile, int bytes, char* dst) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, bytes, 0x00020000);
+    const int pc = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) cs[j] = pair_sum(row_pair_sum(cs[j]));
-  if (lane < 16) {
-    *(f32x4*)&dst[w][8 * lane] = f32x4{cs[0], cs[1], cs[2], cs[3]};
-    *(f32x4*)&dst[w][8 * lane + 4] = f32x4{cs[4], cs[5], cs[6], cs[7]};
+    for (int i = 0; i < PX_ROWS / 4; ++i) {
+      const int r = PX_ROWS * w + 4 * i + (lane >> 4);
+      const uint32_t off = (uint32_t)r * row_bytes + ((uint32_t)(pc ^ (r & 15)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (px_lds_void*)(dst + (PX_ROWS * w + 4 * i) * 256), 16, off, 0,
+                                               0, 0);
+    }
+  }
+};
+
+__global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void proxy_scores_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, float4* __restrict__ tstat, float* __restrict__ kbar,
+    const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
+    int w_local, int dense_below_n, float sl2, int kpc) {
+  __shared__ __attribute__((aligned(1024))) char sK0[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char sK1[BLK * 256];
+  __shared__ __attribute__((aligned(16))) float red[2][PX_WAVES][HD];   // K-bar partials per (tile parity, wave)
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = w >> 2, wq = w & 3;   // head of the group, row group (wave-uniform)
+  const int G = hq / hkv, npg = (G + PX_HEADS - 1) / PX_HEADS;
+  const int chunk = blockIdx.x / (hkv * npg), rem = blockIdx.x % (hkv * npg);
+  const int kvh = rem % hkv, hp = rem / hkv;
+  const int h0 = kvh * G + PX_HEADS * hp, nh = min(PX_HEADS, G - PX_HEADS * hp);
+  const bool kbar_wg = hp == 0;        // block means of K, once per KV head
+  const bool scores = hg < nh;         // this wave has a head
+  const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
+  const int nb = sp.nb;
+  const int64_t n = (int64_t)nb * BLK;
+  if (chunk * kpc >= nb || seq_dense(nb, dense_below_n)) return;
+  Q += sp.tok * sq_n;
+  K += sp.tok * sk_n;
+  float4* ts = tstat + (sp.rows + (int64_t)(h0 + hg) * nb) * BLK;
+  kbar += sp.kvrows * HD;
+  const int qrow = 32 * wq + l32;
+  Tile<bf16>::QFrag qf;
+  if (scores) Tile<bf16>::load_q(qf, Q + (int64_t)(h0 + hg) * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
+  const int kb0 = chunk * kpc, kb1 = min(nb, kb0 + kpc);
+  const bf16* Kh = K + (int64_t)kvh * sk_h;
+  const uint32_t krow = (uint32_t)(sk_n * 2);
+  const int kspan = (int)((BLK - 1) * krow + 256);
+  const PxCopy kc{krow, w, lane};
+  uint32_t kx[8];   // S^T A operand: key row 32t + l32, d chunk 2c + g (t adds 8192 bytes)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
+  // K-bar partials: lane L of wave w sums rows PX_ROWS w + 4i + L/16 of columns 8(L%16) .. +7
+  const int kb_r0 = PX_ROWS * w + (lane >> 4), kb_c = lane & 15;
+  const bf16x2 px_e0 = {(bf16)1.f, (bf16)0.f}, px_e1 = {(bf16)0.f, (bf16)1.f};
+  auto kbar_partials = [&](const char* cur, int par) __attribute__((always_inline)) {
+    float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PX_ROWS / 4; ++i) {
+      const int r = kb_r0 + 4 * i;
+      // one v_dot2 per element: (x, y) . (1, 0) + acc adds x exactly as a
+      // float add would (the other product is zero)
+      const bf16x8 u = *(const bf16x8*)(cur + r * 256 + ((kb_c ^ (r & 15)) << 4));
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const bf16x2 pr = {u[2 * p], u[2 * p + 1]};
+        cs[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(pr, px_e0, cs[2 * p], false);
+        cs[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, px_e1, cs[2 * p + 1], false);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cs[j] += __shfl_xor(cs[j], 16, 64);
+      cs[j] += __shfl_xor(cs[j], 32, 64);
+    }
+    if (lane < 16) {
+      *(f32x4*)&red[par][w][8 * lane] = f32x4{cs[0], cs[1], cs[2], cs[3]};
+      *(f32x4*)&red[par][w][8 * lane + 4] = f32x4{cs[4], cs[5], cs[6], cs[7]};
+    }
+  };
+  auto kbar_final = [&](int kb, int par) __attribute__((always_inline)) {
+    if (tid < HD) {
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < PX_WAVES; ++v) sum += red[par][v][tid];
+      kbar[((int64_t)kvh * nb + kb) * HD + tid] = sum * (1.f / BLK);
+    }
+  };
+
+  auto tile = [&](int kb, const char* cur, char* nxt, int par) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(PX_WAIT_VM0);   // this wave's share of tile kb has landed
+    px_barrier();                              // all of it has; every wave left the other stage
+    if (kb + 1 < kb1) kc.issue(Kh + (int64_t)(kb + 1) * BLK * sk_n, kspan, nxt);
+    if (kbar_wg) {
+      if (kb > kb0) kbar_final(kb - 1, par ^ 1);   // the last tile's partials were written before the barrier
+      kbar_partials(cur, par);
+    }
+    if (!scores) return;
+    const bool last = kb == nb - 1;
+    const int64_t j0 = (int64_t)kb * BLK;
+    const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
+    // anchor windows relative to the tile, clamped to [-1, BLK]: key c of the
+    // tile is in the sink window iff c < ws_lim, in the local one iff c >= wl_lim
+    const int ws_lim = (int)min<int64_t>(BLK, max<int64_t>(-1, (int64_t)w_sink - j0));
+    const int wl_lim = (int)min<int64_t>(BLK + 1, max<int64_t>(-1, n - w_local - j0));
+    float m = -INFINITY, lo = 0.f, up = 0.f, an = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      // fragments double-buffered in source order (the reads for step c + 1 go
+      // out before the MFMAs of step c), which bounds the registers in flight
+      bf16x8 fk[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) fk[0][t] = *(const bf16x8*)(cur + kx[0] + 8192 * (2 * hf + t));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c + 1 < 8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) fk[(c + 1) & 1][t] = *(const bf16x8*)(cur + kx[c + 1] + 8192 * (2 * hf + t));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) s[t] = mfma_bf16(fk[c & 1][t], qf.v[c], s[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (last) {   // keys after the query row are masked
+        int lim = qrow;
+        asm volatile("" : "+v"(lim));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * (2 * hf + t) + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = pair_max(mx);   // half 0 holds key 0 of every row: finite after it
+      if (hf == 1 && mx > m) {
+        const float r = fast_exp2((m - mx) * sl2);
+        lo *= r;
+        up *= r;
+        an *= r;
+      }
+      m = fmaxf(m, mx);
+      const float mb = m * sl2;
+      // key c = 32t' + .. (t' = 2hf + t) against rows 32wq .. 32wq+31: t' < wq
+      // all lower, t' > wq all upper, t' = wq split per score
+      if (!last && !touches_anchor) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int tt = 2 * hf + t;
+          float a = 0.f, b = 0.f;
+          if (tt == wq) {
+            int lim = l32 - 4 * g;   // key 32tt + 8(i/4) + 4g + i%4 <= row 32wq + l32
+            asm volatile("" : "+v"(lim));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
+              if (8 * (i >> 2) + (i & 3) <= lim) a += p;
+              else b += p;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a += fast_exp2(fmaf(s[t][i], sl2, -mb));
+            if (tt > wq) { b = a; a = 0.f; }
+          }
+          lo += a;
+          up += b;
+        }
+      } else {
+        // score i of sub-tile tt is key 32tt + 4g + ci, ci = 8(i/4) + i%4: the
+        // tests against the row and the anchor windows become tests of the
+        // compile-time ci against three per-lane limits
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int tt = 2 * hf + t;
+          if (tt > wq && last) continue;
+          int dl = qrow - 32 * tt - 4 * g;   // lower part: ci <= dl
+          int ds = ws_lim - 32 * tt - 4 * g; // sink window: ci < ds
+          int dw = wl_lim - 32 * tt - 4 * g; // local window: ci >= dw
+          asm volatile("" : "+v"(dl), "+v"(ds), "+v"(dw));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ci = 8 * (i >> 2) + (i & 3);
+            const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
+            const bool lower = tt < wq || (tt == wq && ci <= dl);
+            if (lower) lo += p;
+            else if (!last) up += p;
+            if (touches_anchor && (lower || !last) && (ci < ds || ci >= dw)) an += p;
+          }
+        }
+      }
+    }
+    lo = pair_sum(lo);
+    up = pair_sum(up);
+    an = pair_sum(an);
+    if (g == 0) ts[(int64_t)kb * BLK + qrow] = make_float4(m, lo, up, an);
+  };
+
+  kc.issue(Kh + (int64_t)kb0 * BLK * sk_n, kspan, sK0);
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    tile(kb, sK0, sK1, 0);
+    if (kb + 1 < kb1) tile(kb + 1, sK1, sK0, 1);
+  }
+  if (kbar_wg) {
+    __builtin_amdgcn_s_waitcnt(0);
+    px_barrier();
+    kbar_final(kb1 - 1, (kb1 - 1 - kb0) & 1);
   }
 }
 
-// Scores of the last query block against kpc <= PCH key blocks; per (tile, row):
-// tile max m of the row and the sums of exp(s - m) over the lower part (key
-// column <= row: slash bin N_b-1-kb), the upper part (bin N_b-2-kb) and the
-// anchor windows.
-template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proxy_tiles_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                          float4* __restrict__ tstat, float* __restrict__ kbar,
-                                                          const SeqList seqs, int hq, int hkv, int64_t sq_h,
-                                                          int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
-                                                          int w_local, int dense_below_n, float sl2, int kpc) {
-  // bf16: two K tiles (the next one is written while the current one is read);
-  // fp32 keeps one (its staging would not fit in registers)
-  constexpr bool PIPE = sizeof(T) == 2;
-  constexpr int TILE = BLK * Tile<T>::KP;
-  __shared__ __attribute__((aligned(16))) T sK[(PIPE ? 2 : 1) * TILE];
-  // K-bar partial column sums: bf16 per (tile parity, wave), fp32 per half tile
-  __shared__ __attribute__((aligned(16))) float red[2][4][HD];
+// fp32 score pass: scores of the last query block against kpc <= PCH key
+// blocks, one query head per work-group of 4 waves, one K tile in LDS at a
+// time; per (tile, row): tile max m of the row and the sums of exp(s - m)
+// over the lower part (key column <= row: slash bin N_b-1-kb), the upper part
+// (bin N_b-2-kb) and the anchor windows.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proxy_tiles_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, float4* __restrict__ tstat, float* __restrict__ kbar,
+    const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
+    int w_local, int dense_below_n, float sl2, int kpc) {
+  __shared__ __attribute__((aligned(16))) float sK[BLK * Tile<float>::KP];
+  __shared__ __attribute__((aligned(16))) float red[2][HD];   // K-bar column sums per half tile
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the t-vs-w branches are scalar
-  constexpr int HPW = proxy_heads<T>();
-  const int G = hq / hkv, npg = (G + HPW - 1) / HPW;   // head groups per KV head
-  const int chunk = blockIdx.x / (hkv * npg), rem = blockIdx.x % (hkv * npg);
+  const int G = hq / hkv;
+  const int chunk = blockIdx.x / (hkv * G), rem = blockIdx.x % (hkv * G);
   const int kvh = rem % hkv, hp = rem / hkv;
-  const int h0 = kvh * G + HPW * hp, nh = min(HPW, G - HPW * hp);   // heads h0 .. h0 + nh - 1
+  const int h = kvh * G + hp;
   const bool kbar_wg = hp == 0;   // block means of K, once per KV head
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
@@ -116,113 +332,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (chunk * kpc >= nb || seq_dense(nb, dense_below_n)) return;
   Q += sp.tok * sq_n;
   K += sp.tok * sk_n;
-  tstat += (sp.rows + (int64_t)h0 * nb) * BLK;   // head h0 + hh at tstat + hh * nb * BLK
+  tstat += (sp.rows + (int64_t)h * nb) * BLK;
   kbar += sp.kvrows * HD;
   const int qrow = 32 * w + l32;
-  typename Tile<T>::QFrag qf[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j)
-    if (j < nh) Tile<T>::load_q(qf[j], Q + (int64_t)(h0 + j) * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
+  Tile<float>::QFrag qf;
+  Tile<float>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const int kb0 = chunk * kpc, kb1 = min(nb, kb0 + kpc);
-  const T* Kh = K + (int64_t)kvh * sk_h;
-  typename Tile<bf16>::KStage stg;
-  if constexpr (PIPE) {
-    Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)kb0 * BLK * sk_n, sk_n, tid);
-    Tile<bf16>::store_k((bf16*)sK, stg, tid);
-    if (kbar_wg) kbar_partials(red[0], stg, w, lane);
-    __syncthreads();
-  }
+  const float* Kh = K + (int64_t)kvh * sk_h;
   for (int kb = kb0; kb < kb1; ++kb) {
-    const int par = (kb - kb0) & 1;
-    T* cur = sK + (PIPE ? par * TILE : 0);
-    if constexpr (PIPE) {
-      if (kb + 1 < kb1) Tile<bf16>::fetch_k(stg, (const bf16*)Kh + (int64_t)(kb + 1) * BLK * sk_n, sk_n, tid);
-    } else {
-      __syncthreads();
-      Tile<T>::load_k(cur, Kh + (int64_t)kb * BLK * sk_n, sk_n, tid);
-      __syncthreads();
-    }
+    __syncthreads();
+    Tile<float>::load_k(sK, Kh + (int64_t)kb * BLK * sk_n, sk_n, tid);
+    __syncthreads();
     if (kbar_wg) {  // block mean of K for Pooled Estimation
-      if constexpr (PIPE) {
-        // the partials of this tile were written before the last barrier
-        if (tid < HD)
-          kbar[((int64_t)kvh * nb + kb) * HD + tid] =
-              (((red[par][0][tid] + red[par][1][tid]) + red[par][2][tid]) + red[par][3][tid]) * (1.f / BLK);
-      } else {
-        const int d = tid & 127, half = tid >> 7;
-        float sum = 0.f;
-        for (int r = 0; r < 64; ++r) sum += to_f32(cur[(64 * half + r) * Tile<T>::KP + d]);
-        red[0][half][d] = sum;
-        __syncthreads();
-        if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][0][d] + red[0][1][d]) * (1.f / BLK);
-      }
+      const int d = tid & 127, half = tid >> 7;
+      float sum = 0.f;
+      for (int r = 0; r < 64; ++r) sum += sK[(64 * half + r) * Tile<float>::KP + d];
+      red[half][d] = sum;
+      __syncthreads();
+      if (half == 0) kbar[((int64_t)kvh * nb + kb) * HD + d] = (red[0][d] + red[1][d]) * (1.f / BLK);
     }
-    // every head of the group against the same K tile
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      if (hh >= nh) break;
-      f32x16 s[4];
-      Tile<T>::st(s, cur, qf[hh], l32, g);
-      const bool last = (kb == nb - 1);
-      if (last) {
-        int lim = qrow;
-        asm volatile("" : "+v"(lim));   // compares stay in this once-per-row branch (no hoisted SGPR masks)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * t + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
+    f32x16 s[4];
+    Tile<float>::st(s, sK, qf, l32, g);
+    const bool last = (kb == nb - 1);
+    if (last) {
+      int lim = qrow;
+      asm volatile("" : "+v"(lim));   // compares stay in this once-per-row branch (no hoisted SGPR masks)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = pair_max(mx);   // every row keeps at least its diagonal key: finite
-      const float mb = mx * sl2;
-      const int64_t j0 = (int64_t)kb * BLK;
-      const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
-      float lo = 0.f, up = 0.f, an = 0.f;
-      // key c = 32t + .. against this wave's rows 32w .. 32w+31: t < w all lower,
-      // t > w all upper, t = w split per score; interior tiles take the short
-      // path, the last tile and the anchor tiles the general one
-      if (!last && !touches_anchor) {
-        interior_sums(s, sl2, mb, w, l32, g, lo, up);
-      } else {
-        int lim = qrow;
-        asm volatile("" : "+v"(lim));   // as above: the per-score compares stay in this branch
+        for (int i = 0; i < 16; ++i)
+          if (32 * t + mfma32_row(i, g) > lim) s[t][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t > w && last) continue;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = 32 * t + mfma32_row(i, g);
-            const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
-            bool lower = t < w;
-            if (t == w) lower = c <= lim;
-            if (lower) lo += p;
-            else if (!last) up += p;
-            if (touches_anchor && (lower || !last)) {
-              const int64_t j = j0 + c;
-              if (j < w_sink || j >= n - w_local) an += p;
-            }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+    mx = pair_max(mx);   // every row keeps at least its diagonal key: finite
+    const float mb = mx * sl2;
+    const int64_t j0 = (int64_t)kb * BLK;
+    const bool touches_anchor = (j0 < w_sink) || (j0 + BLK > n - w_local);
+    float lo = 0.f, up = 0.f, an = 0.f;
+    // key c = 32t + .. against this wave's rows 32w .. 32w+31: t < w all lower,
+    // t > w all upper, t = w split per score; interior tiles take the short
+    // path, the last tile and the anchor tiles the general one
+    if (!last && !touches_anchor) {
+      interior_sums(s, sl2, mb, w, l32, g, lo, up);
+    } else {
+      int lim = qrow;
+      asm volatile("" : "+v"(lim));   // as above: the per-score compares stay in this branch
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t > w && last) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * t + mfma32_row(i, g);
+          const float p = fast_exp2(fmaf(s[t][i], sl2, -mb));
+          bool lower = t < w;
+          if (t == w) lower = c <= lim;
+          if (lower) lo += p;
+          else if (!last) up += p;
+          if (touches_anchor && (lower || !last)) {
+            const int64_t j = j0 + c;
+            if (j < w_sink || j >= n - w_local) an += p;
           }
         }
       }
-      lo = pair_sum(lo);
-      up = pair_sum(up);
-      an = pair_sum(an);
-      if (g == 0) tstat[((int64_t)hh * nb + kb) * BLK + qrow] = make_float4(mx, lo, up, an);
     }
-    if constexpr (PIPE) {
-      // the other buffer and the other partials were last read before the
-      // previous barrier
-      if (kb + 1 < kb1) {
-        Tile<bf16>::store_k((bf16*)sK + (par ^ 1) * TILE, stg, tid);
-        if (kbar_wg) kbar_partials(red[par ^ 1], stg, w, lane);
-        __syncthreads();
-      }
-    }
+    lo = pair_sum(lo);
+    up = pair_sum(up);
+    an = pair_sum(an);
+    if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
   }
 }
 
@@ -319,8 +499,8 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int nseq = seqs.nseq;
   const int G = hq / hkv;
-  const int groups = hkv * ((G + (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()) - 1) /
-                            (fp32 ? proxy_heads<float>() : proxy_heads<bf16>()));
+  const int hpw = fp32 ? 1 : PX_HEADS;   // query heads per score work-group
+  const int groups = hkv * ((G + hpw - 1) / hpw);
   // key blocks per work-group: PCH, or fewer so that about two work-groups per
   // CU exist (short sequences would otherwise run a few long serial chains)
   const int64_t want = 2 * (int64_t)device_cu_count();
@@ -329,13 +509,13 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const int kpc = (int)std::max<int64_t>(1, std::min<int64_t>(PCH, (nb_max + chunks - 1) / chunks));
   const dim3 grid((unsigned)(((nb_max + kpc - 1) / kpc) * groups), (unsigned)nseq);
   if (fp32) {
-    proxy_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
-                                                   hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
-                                                   dense_below_n, sl2, kpc);
+    proxy_tiles_f32_kernel<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
+                                                 hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local, dense_below_n,
+                                                 sl2, kpc);
   } else {
-    proxy_tiles_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar, seqs, hq,
-                                                  hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local,
-                                                  dense_below_n, sl2, kpc);
+    proxy_scores_bf16_kernel<<<grid, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
+                                                            seqs, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink,
+                                                            w_local, dense_below_n, sl2, kpc);
   }
   const int nchunk = proxy_chunks(nb_max);
   const unsigned vheads = (unsigned)(nseq * hq);

@@ -1016,27 +1016,50 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
 
 // count of entries equal to the cut value per row, then an exclusive scan per head (only when the cut
 // splits a run of equal values)
+// Per row of an active Pooled-Estimation head, from one read of the row: the
+// entries above the cut value (G), equal to it (E), and whether the two forced
+// entries (key blocks 0 and qb) lie below it.  The row's list length follows:
+// without a split run of equal values it is G + E + the forced entries below
+// the cut, written to counts here; with one, eqrow gets E (for the flat-order
+// scan) and counts the part that does not depend on the scan, completed by
+// the count pass of list_kernel.
 __global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
-                                                          int32_t* __restrict__ eqrow, const SeqList seqs, int hq,
-                                                          int hkv) {
+                                                          int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
+                                                          const SeqList seqs, int hq, int hkv) {
   const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
   const int qb = blockIdx.x * 4 + w;
   const PeCut c = cut[h];
-  if (!c.active || c.take >= c.eq_cnt) return;
+  if (!c.active) return;
   const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
   const int nb = sp.nb;
   if (qb >= nb) return;
   const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
-  int cnt = 0;
+  int eq = 0, gt = 0;
   for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
     uint32_t xs[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : ~c.vstar;
+    for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cnt += (xs[u] == c.vstar);
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = k0 + 64 * u <= qb;
+      eq += valid && xs[u] == c.vstar;
+      gt += valid && xs[u] > c.vstar;
+    }
   }
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-  if (lane == 0) eqrow[sp.rows + (int64_t)(h % hq) * nb + qb] = cnt;
+  for (int o = 32; o > 0; o >>= 1) {
+    eq += __shfl_xor(eq, o, 64);
+    gt += __shfl_xor(gt, o, 64);
+  }
+  if (lane == 0) {
+    const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
+    const int forced_below = (row[0] < c.vstar) + (qb > 0 && row[qb] < c.vstar);
+    if (c.take < c.eq_cnt) {
+      eqrow[r] = eq;
+      counts[r] = gt + forced_below;
+    } else {
+      counts[r] = gt + eq + forced_below;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict__ cut, int32_t* __restrict__ eqrow,
@@ -1063,8 +1086,9 @@ __device__ __forceinline__ int lane_prefix(unsigned long long m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// One wave per (head, query block).  FILL = false writes the row's count,
-// FILL = true writes its ascending key blocks at row_ptr[row].
+// One wave per (head, query block).  FILL = false writes the row's count
+// (Pooled-Estimation rows: completes what pe_eq_count wrote, without reading
+// the matrix), FILL = true writes its ascending key blocks at row_ptr[row].
 template <bool FILL>
 __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ route,
                                                    const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
@@ -1093,6 +1117,23 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
     const PeCut c = cut[h];
     const uint32_t* bits = (const uint32_t*)(P + sp.tri + (int64_t)hl * tri(nb) + tri(qb));
     const bool split = c.take < c.eq_cnt;
+    if (!FILL) {
+      // pe_eq_count wrote the count, or with a split run its part without the
+      // tied entries: of the row's E tied entries the first T in flat order
+      // are taken, T = clamp(take - (tied entries before the row), 0, E); a
+      // forced entry that is tied but not among them is added on its own (key
+      // block 0 is the row's first tied entry, qb its last)
+      if (split && lane == 0) {
+        const int32_t* e = eqrow + sp.rows + (int64_t)hl * nb;
+        const long long before = e[qb];
+        const long long E = (qb + 1 < nb ? (long long)e[qb + 1] : (long long)c.eq_cnt) - before;
+        const long long room = (long long)c.take - before;
+        const long long T = room < 0 ? 0 : (room > E ? E : room);
+        const int extra = (bits[0] == c.vstar && T == 0) + (qb > 0 && bits[qb] == c.vstar && T < E);
+        counts[row] += (int)T + extra;
+      }
+      return;
+    }
     int base = 0;
     long long eqb = split ? eqrow[row] : 0;
     // eight 64-entry pieces are loaded before any is used, then taken in order
@@ -1118,11 +1159,10 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
           eqb += __popcll(em);
         }
         const unsigned long long m = __ballot(sel);
-        if (FILL && sel) out[base + lane_prefix(m)] = k;
+        if (sel) out[base + lane_prefix(m)] = k;
         base += __popcll(m);
       }
     }
-    if (!FILL && lane == 0) counts[row] = base;
     return;
   }
   // Vertical-Slash: set bits in a per-wave bitmap, then read them out in order
@@ -1351,7 +1391,7 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
   pe_hist_kernel<2><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
   pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_eq_count_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.eqrow, seqs, hq, hkv);
+  pe_eq_count_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.eqrow, b.counts, seqs, hq, hkv);
   pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
   const dim3 gl((nb_max + 3) / 4, vh);
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);

@@ -14,64 +14,11 @@ namespace crisp {
 template <typename T> struct Tile;
 
 template <> struct Tile<bf16> {
-  static constexpr int KP = 136;            // LDS pitch of a K row (272 B): conflict-free 16-B reads
   struct QFrag { bf16x8 v[8]; };
   // lane's query row, d-slices 16c + 8g .. +8 (B operand of v_mfma_f32_32x32x16_bf16)
   __device__ static void load_q(QFrag& f, const bf16* row, int g) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) f.v[c] = *(const bf16x8*)(row + 16 * c + 8 * g);
-  }
-  // the same copy split in two, so that the next tile's global loads can be in
-  // flight (in 32 registers) while the current tile is used
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  struct KStage { u32x4 v[8]; };
-  __device__ static void fetch_k(KStage& st, const bf16* kbase, int64_t ld, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
-      st.v[i] = *(const u32x4*)(kbase + (int64_t)r * ld + gr * 8);
-    }
-  }
-  __device__ static void store_k(bf16* sK, const KStage& st, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
-      *(u32x4*)(sK + r * KP + gr * 8) = st.v[i];
-    }
-  }
-  // column sums of the staged copy: thread tid holds rows tid/16 + 16i
-  // (i = 0..7) of columns 8(tid%16) .. +7; cs[j] = sum over its rows, in i order
-  __device__ static void col_sums(float (&cs)[8], const KStage& st) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cs[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const unsigned u = st.v[i][p];               // columns 2p (low half) and 2p + 1
-        cs[2 * p] += __uint_as_float(u << 16);
-        cs[2 * p + 1] += __uint_as_float(u & 0xffff0000u);
-      }
-  }
-  // 128 x 128 tile, rows kbase[r * ld] -> sK[r * KP]
-  __device__ static void load_k(bf16* sK, const bf16* kbase, int64_t ld, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, r = c >> 4, gr = c & 15;
-      *(uint4*)(sK + r * KP + gr * 8) = *(const uint4*)(kbase + (int64_t)r * ld + gr * 8);
-    }
-  }
-  __device__ static void st(f32x16 (&s)[4], const bf16* sK, const QFrag& f, int l32, int g) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) s[t] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 a = *(const bf16x8*)(sK + (32 * t + l32) * KP + 16 * c + 8 * g);
-        s[t] = mfma_bf16(a, f.v[c], s[t]);
-      }
-    }
   }
 };
 
