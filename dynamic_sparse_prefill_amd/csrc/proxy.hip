@@ -148,20 +148,17 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
   // K-bar partials: lane L of wave w sums rows PX_ROWS w + 4i + L/16 of columns 8(L%16) .. +7
   const int kb_r0 = PX_ROWS * w + (lane >> 4), kb_c = lane & 15;
-  const bf16x2 px_e0 = {(bf16)1.f, (bf16)0.f}, px_e1 = {(bf16)0.f, (bf16)1.f};
   auto kbar_partials = [&](const char* cur, int par) __attribute__((always_inline)) {
     float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < PX_ROWS / 4; ++i) {
       const int r = kb_r0 + 4 * i;
-      // one v_dot2 per element: (x, y) . (1, 0) + acc adds x exactly as a
-      // float add would (the other product is zero)
-      const bf16x8 u = *(const bf16x8*)(cur + r * 256 + ((kb_c ^ (r & 15)) << 4));
+      const uint4 u = *(const uint4*)(cur + r * 256 + ((kb_c ^ (r & 15)) << 4));
+      const unsigned v[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const bf16x2 pr = {u[2 * p], u[2 * p + 1]};
-        cs[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(pr, px_e0, cs[2 * p], false);
-        cs[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, px_e1, cs[2 * p + 1], false);
+        cs[2 * p] += __uint_as_float(v[p] << 16);
+        cs[2 * p + 1] += __uint_as_float(v[p] & 0xffff0000u);
       }
     }
 #pragma unroll
