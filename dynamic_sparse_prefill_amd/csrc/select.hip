@@ -567,21 +567,37 @@ constexpr int PE_RB = 4;     // 32-query-block row blocks (one wave each) per lo
 // about |x| 2^-24 beyond the instruction's own, far below the probabilities'
 // use (they are compared to 1e-5 and cut on their own float32 values).
 __device__ __forceinline__ float pe_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-constexpr int KT_PITCH = 132; // LDS pitch (floats) of a key-block-mean row: conflict-free 16-byte reads
+constexpr int KT_PITCH = 136; // LDS pitch (bf16) of a key-block-mean row plane: conflict-free 16-byte reads
+
+// x = x1 + x2 + x3 exactly to float32 precision, each part bf16 (8 significant
+// bits; the remainders are exact in float32).  A float32 dot product then
+// takes six bf16 products per element pair, x1 y1 + (x1 y2 + x2 y1) + (x1 y3 +
+// x2 y2 + x3 y1); the terms left out are below 2^-24 of x y.
+struct Split3 { bf16 a, b, c; };
+__device__ __forceinline__ Split3 split3(float x) {
+  const bf16 a = (bf16)x;
+  const float r1 = x - (float)a;
+  const bf16 b = (bf16)r1;
+  const float r2 = r1 - (float)b;
+  return {a, b, (bf16)r2};
+}
 
 // Logits: one item per (PE_RB row blocks of 32 query blocks, segment cs of
 // PE_SEG key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
 // L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb is formed 32 key blocks
-// at a time with v_mfma_f32_32x32x2f32 in the transposed form L^T = Kbar Qbar^T
-// (lane l owns query block 32 rb + l%32 and 16 of the 32 key blocks; the d
-// index of MFMA step s, lane half g is 64 g + s).  The 32 key-block means of a
-// tile are staged once in LDS (double-buffered, the next tile's copy in flight
-// during the MFMAs) and shared by the work-group's waves.  Each tile is turned
+// at a time in the transposed form L^T = Kbar Qbar^T on the bf16 matrix unit
+// (v_mfma_f32_32x32x16_bf16) with both operands split in three bf16 parts
+// (split3): float32 accuracy at 48 bf16 MFMAs per tile instead of 64 float32
+// ones of a quarter the rate.  Lane l owns query block 32 rb + l%32 and 16 of
+// the 32 key blocks; MFMA step s takes d = 16 s + 8 g .. + 7 on lane half g.
+// The 32 key-block means of a tile are split and staged once in LDS (three
+// planes, double-buffered, the next tile's copy in flight during the MFMAs)
+// and shared by the work-group's waves.  Each tile is turned
 // row-major through LDS and stored with whole 128-byte row segments; the
 // segment's row max and sum of exp(L - max) go to `part` for the softmax.
 // One item: row group rg_from_end counted from the bottom of the sequence's
 // triangle (0 = the longest rows), segment cs, virtual head vh.
-__device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], float (&tileT)[PE_RB][32][33],
+__device__ __forceinline__ void pe_logits_item(bf16 (&kt)[2][3][32 * KT_PITCH], float (&tileT)[PE_RB][32][33],
                                                const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                float* __restrict__ P, float2* __restrict__ part, const SeqList& seqs,
                                                int hq, int hkv, int nseg, float scale, int vh, int rg_from_end, int cs) {
@@ -606,13 +622,21 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
   const int kvh = h / (hq / hkv);
   const int qb = rb * 32 + l32;
   const bool row_ok = qb < nb;
-  float qv[64];
+  bf16x8 q1[8], q2[8], q3[8];   // step s: d = 16 s + 8 g + e, e = 0..7, in three parts
   {
-    const float4* src = (const float4*)(qbar + ((int64_t)h * nb + (row_ok ? qb : 0)) * HD + 64 * g);
+    const float4* src = (const float4*)(qbar + ((int64_t)h * nb + (row_ok ? qb : 0)) * HD + 8 * g);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 x = row_ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      qv[4 * i] = x.x; qv[4 * i + 1] = x.y; qv[4 * i + 2] = x.z; qv[4 * i + 3] = x.w;
+    for (int st = 0; st < 8; ++st) {
+      const float4 x0 = row_ok ? src[4 * st] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x1 = row_ok ? src[4 * st + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const Split3 p = split3(xs[e]);
+        q1[st][e] = p.a;
+        q2[st][e] = p.b;
+        q3[st][e] = p.c;
+      }
     }
   }
   float* Ph = P + (int64_t)h * tri(nb);
@@ -627,8 +651,22 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
     for (int i = 0; i < 4; ++i) stg[i] = src[i];
   };
   auto kstore = [&](int buf) {
+    bf16x8 p1[2], p2[2], p3[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(f32x4*)&kt[buf][cr * KT_PITCH + cc + 4 * i] = stg[i];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const Split3 p = split3(stg[i][e]);
+        p1[i >> 1][4 * (i & 1) + e] = p.a;
+        p2[i >> 1][4 * (i & 1) + e] = p.b;
+        p3[i >> 1][4 * (i & 1) + e] = p.c;
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *(bf16x8*)&kt[buf][0][cr * KT_PITCH + cc + 8 * j] = p1[j];
+      *(bf16x8*)&kt[buf][1][cr * KT_PITCH + cc + 8 * j] = p2[j];
+      *(bf16x8*)&kt[buf][2][cr * KT_PITCH + cc + 8 * j] = p3[j];
+    }
   };
   kfetch(ct0);
   kstore(0);
@@ -638,34 +676,40 @@ __device__ __forceinline__ void pe_logits_item(float (&kt)[2][32 * KT_PITCH], fl
     const int buf = (ct - ct0) & 1;
     if (ct + 1 < ct1) kfetch(ct + 1);
     if (ct < ntile) {
-      // two independent chains (d slices 4i..4i+1 and 4i+2..4i+3) keep the
-      // matrix unit fed from one wave, summed at the end; the operands are
-      // read one step ahead of the four MFMAs that use them (the order is
-      // pinned: left to itself the compiler waits on each read just before
-      // its use)
-      f32x16 acc = {}, acc2 = {};
-      const float* ka = &kt[buf][l32 * KT_PITCH + 64 * g];
+      // two accumulators taken in turn, x1 y1 + x1 y2 + x2 y1 and the three
+      // smallest terms, added at the end; the operand parts of step
+      // s + 1 are read before the MFMAs of step s (the order is pinned: left to
+      // itself the compiler waits on each read just before its use)
+      f32x16 acc = {}, accl = {};
+      const bf16* ka = &kt[buf][0][l32 * KT_PITCH + 8 * g];
+      constexpr int PL = 32 * KT_PITCH;   // one plane
       __builtin_amdgcn_sched_barrier(0);
-      float4 a = *(const float4*)ka;
+      bf16x8 a1 = *(const bf16x8*)ka, a2 = *(const bf16x8*)(ka + PL), a3 = *(const bf16x8*)(ka + 2 * PL);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float4 an = a;
-        if (i < 15) an = *(const float4*)(ka + 4 * (i + 1));
-        acc = mfma_f32(a.x, qv[4 * i], acc);
-        acc2 = mfma_f32(a.z, qv[4 * i + 2], acc2);
-        acc = mfma_f32(a.y, qv[4 * i + 1], acc);
-        acc2 = mfma_f32(a.w, qv[4 * i + 3], acc2);
-        a = an;
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 n1 = a1, n2 = a2, n3 = a3;
+        if (st < 7) {
+          n1 = *(const bf16x8*)(ka + 16 * (st + 1));
+          n2 = *(const bf16x8*)(ka + PL + 16 * (st + 1));
+          n3 = *(const bf16x8*)(ka + 2 * PL + 16 * (st + 1));
+        }
+        accl = mfma_bf16(a1, q3[st], accl);
+        acc = mfma_bf16(a1, q1[st], acc);
+        accl = mfma_bf16(a2, q2[st], accl);
+        acc = mfma_bf16(a1, q2[st], acc);
+        accl = mfma_bf16(a3, q1[st], accl);
+        acc = mfma_bf16(a2, q1[st], acc);
+        a1 = n1; a2 = n2; a3 = n3;
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // three LDS reads
 #pragma unroll
-      for (int i = 0; i < 15; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // four MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // the next read
+      for (int st = 0; st < 7; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0); // six MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); // the next step's reads
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
       __builtin_amdgcn_sched_barrier(0);
-      acc += acc2;
+      acc += accl;
       // an interior tile (below the diagonal tile, rows inside the sequence)
       // needs no causal mask, no -inf test and no per-row store predicate: the
       // same values by a shorter path (a scalar branch: rb and ct are
@@ -727,7 +771,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const float* __restrict__ qbar, const float* __restrict__ kbar, const int32_t* __restrict__ route,
     float* __restrict__ P, float2* __restrict__ part, const SeqList seqs, int hq, int hkv, int nseg, float scale,
     int* __restrict__ queue, int nvh, int nitems) {
-  __shared__ __attribute__((aligned(16))) float kt[2][32 * KT_PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 kt[2][3][32 * KT_PITCH];
   __shared__ float tileT[PE_RB][32][33];
   __shared__ int s_item;
   for (;;) {
