@@ -44,12 +44,13 @@ TILE_FLOPS = 4 * 128 * 128 * 128          # QK^T + PV for one 128 x 128 tile at 
 # causal part of a diagonal tile: query row r sees keys 0..r, 129/256 of the tile's pairs
 DIAG_USEFUL = 129 / 256
 PEAK_BF16_TFLOPS = 2500.0                  # MI355X dense bf16 MFMA
-PEAK_FP32_MFMA_TFLOPS = 157.3              # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 # VALU model of the chip (256 CUs at 2.4 GHz, 4 SIMDs of 16 lanes each): a
-# full-rate vector op costs one lane-cycle per lane, a transcendental (v_exp_f32)
-# four; 64 lane-cycles per clock per CU.
+# full-rate vector op costs one lane-cycle per lane, v_exp_f32 two (measured on
+# gfx950: 8 clocks per wave64 instruction against 4 for v_fma_f32, and the two
+# do not issue together); 64 lane-cycles per clock per CU.
 CU, CLOCK_GHZ, LANE_CYCLES_PER_CLK = 256, 2.4, 64
+EXP_LANE_CYCLES = 2
 
 
 def log(*a):
@@ -135,20 +136,21 @@ def head_mix(spec, sel_route, c_struct):
 def selection_stage_bounds(cfg, route, tiles):
     """Lower bounds of the selection's stages from their algorithmic work.
     proxy: K once (HBM), 2*128*n*d flops per query head (bf16 MFMA) and, per
-    score, one v_exp_f32 (4 lane-cycles) plus three full-rate ops (scale and
-    shift, sum, max): the VALU bound is the largest of the three.  Pooled
-    estimation: Q of the PE heads once (pooling), pooled logits on fp32 MFMA
-    (2 * d flops per causal block pair), the pooled matrix written once and read
-    by the cut.  Lists: 4 bytes per entry written."""
+    score, one v_exp_f32 (EXP_LANE_CYCLES lane-cycles) plus three full-rate ops
+    (scale and shift, sum, max): the VALU bound is the largest of the three.
+    Pooled estimation: Q of the PE heads once (pooling), pooled logits on the
+    bf16 matrix unit as six bf16 products per float32 product (the three-part
+    split: 6 * 2 * d flops per causal block pair), the pooled matrix written
+    once and read by the cut.  Lists: 4 bytes per entry written."""
     nb = cfg.n // 128
     h_pe = int((route == 0).sum())
     tri = nb * (nb + 1) // 2
     scores = cfg.hq * 128 * cfg.n
     proxy = {"hbm_ms": cfg.hkv * cfg.n * 128 * 2 / (PEAK_HBM_GBS * 1e9) * 1e3,
              "mfma_ms": 2 * 128 * cfg.n * 128 * cfg.hq / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
-             "valu_ms": scores * (4 + 3) / (CU * LANE_CYCLES_PER_CLK * CLOCK_GHZ * 1e9) * 1e3}
+             "valu_ms": scores * (EXP_LANE_CYCLES + 3) / (CU * LANE_CYCLES_PER_CLK * CLOCK_GHZ * 1e9) * 1e3}
     pool = {"hbm_ms": h_pe * cfg.n * 128 * 2 / (PEAK_HBM_GBS * 1e9) * 1e3}
-    logits = {"mfma_fp32_ms": h_pe * tri * 2 * 128 / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e3,
+    logits = {"mfma_bf16x6_ms": h_pe * tri * 6 * 2 * 128 / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
               "hbm_ms": h_pe * tri * 4 / (PEAK_HBM_GBS * 1e9) * 1e3}
     cut = {"hbm_ms": 2 * h_pe * tri * 4 / (PEAK_HBM_GBS * 1e9) * 1e3}
     lists = {"hbm_ms": 4 * tiles / (PEAK_HBM_GBS * 1e9) * 1e3}
