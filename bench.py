@@ -233,7 +233,9 @@ def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=
     """CRISP vs dense ms per layer on Llama-shaped layers of growing length (4k-64k):
     where sparse prefill starts to pay (the length gate).  CRISP is timed as
     enqueued call by call, as one HIP graph replay of the same prefill, and with
-    the length gate at LENGTH_GATE tokens (shorter layers take the dense path)."""
+    the length gate at LENGTH_GATE tokens (shorter layers take the dense path).
+    Also the mean per-direction block budget of the Vertical-Slash heads under
+    the noise floor and under a gamma = 0.95 coverage budget (same routing)."""
     res = {}
     for n in ns:
         cfg = synth.custom_config(f"llama-shape-{n // 1024}k", n, 32, 8, seed=7, conc_frac=0.6)
@@ -259,10 +261,23 @@ def length_sweep(dsp, torch, synth, ns=(4096, 8192, 16384, 32768, 65536), steps=
         # with the length gate at the measured crossover: below it the prefill takes the dense path
         pg = dsp.CrispParams(tau=cfg.tau, alpha=cfg.alpha, gamma=cfg.gamma, dense_below_n=LENGTH_GATE)
         gated = timed(lambda: dsp.crisp_prefill(q, k, v, pg, sel=sel, o=o, ws=ws), reps, 2, torch) if n < LENGTH_GATE else ms
+        # per-direction budget of the Vertical-Slash heads under CRISP's noise
+        # floor and under a gamma-coverage budget on the same routing: the flat
+        # budget against one that grows with n
+        budgets = {}
+        for rule, over in (("crisp", {}), ("coverage-g0.95", dict(flags=dsp.FLAG_VS_COVERAGE))):
+            pb = dsp.CrispParams(tau=cfg.tau, alpha=cfg.alpha, gamma=cfg.gamma)
+            for a, b in over.items():
+                setattr(pb, a, b)
+            sb = dsp.crisp_select(q, k, pb)
+            vs = sb.route.cpu().numpy() == 1
+            nvs = (sb.nv.cpu().numpy() + sb.ns.cpu().numpy())[vs]
+            budgets[rule] = round(float(nvs.mean()) / 2, 2) if vs.any() else None
+            del sb
         res[n] = {"crisp_ms": round(ms, 3), "crisp_graph_ms": round(gms, 3), "dense_ms": round(dms, 3),
                   "speedup": round(dms / ms, 3), "speedup_graph": round(dms / gms, 3),
                   "crisp_gated_ms": round(gated, 3), "speedup_gated": round(dms / gated, 3),
-                  "density": round(density, 4)}
+                  "density": round(density, 4), "vs_budget_blocks": budgets}
         log(f"[bench] length {n}: {res[n]}")
         del graph, q, k, v, o, sel, ws, aws
         torch.cuda.empty_cache()
