@@ -148,17 +148,24 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
   // K-bar partials: lane L of wave w sums rows PX_ROWS w + 4i + L/16 of columns 8(L%16) .. +7
   const int kb_r0 = PX_ROWS * w + (lane >> 4), kb_c = lane & 15;
+  const bf16x2 px_ones = {(bf16)1.f, (bf16)1.f};
   auto kbar_partials = [&](const char* cur, int par) __attribute__((always_inline)) {
     float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // rows r and r + 4 at a time: the same column of both side by side
+    // (v_perm), then both added with one v_dot2 against (1, 1), two
+    // instructions per pair of elements
 #pragma unroll
-    for (int i = 0; i < PX_ROWS / 4; ++i) {
+    for (int i = 0; i < PX_ROWS / 4; i += 2) {
       const int r = kb_r0 + 4 * i;
-      const uint4 u = *(const uint4*)(cur + r * 256 + ((kb_c ^ (r & 15)) << 4));
-      const unsigned v[4] = {u.x, u.y, u.z, u.w};
+      const uint4 u0 = *(const uint4*)(cur + r * 256 + ((kb_c ^ (r & 15)) << 4));
+      const uint4 u1 = *(const uint4*)(cur + (r + 4) * 256 + ((kb_c ^ ((r + 4) & 15)) << 4));
+      const unsigned a[4] = {u0.x, u0.y, u0.z, u0.w}, b[4] = {u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        cs[2 * p] += __uint_as_float(v[p] << 16);
-        cs[2 * p + 1] += __uint_as_float(v[p] & 0xffff0000u);
+        const unsigned lo = __builtin_amdgcn_perm(b[p], a[p], 0x05040100u);   // column 2p of both rows
+        const unsigned hi = __builtin_amdgcn_perm(b[p], a[p], 0x07060302u);   // column 2p + 1
+        cs[2 * p] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), px_ones, cs[2 * p], false);
+        cs[2 * p + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), px_ones, cs[2 * p + 1], false);
       }
     }
 #pragma unroll
