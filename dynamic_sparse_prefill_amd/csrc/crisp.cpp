@@ -111,7 +111,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
     tris += hq * tri(nb);
     if (nb > nb_max) nb_max = nb;
   }
-  const int64_t nch = proxy_chunks((int)nb_max);
+  const int64_t nch = proxy_chunks(s->dtype == CRISP_FP32, seqs, (int)hq, (int)hkv);
   const int64_t nseg = pe_segments(nb_max);
   SelectLayout L;
   size_t o = 0;

@@ -74,8 +74,9 @@ hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, 
                             int nb_total, int hq, int hkv, const Strides& st, hipStream_t s);
 
 // ---- proxy (proxy.hip)
-int proxy_chunks(int nb);   // row-statistics chunks of the proxy
-// nb_max: the longest sequence's N_b; stats holds proxy_chunks(nb_max) chunks per virtual head
+// row-partial chunks per virtual head that stats holds (the most any sequence
+// of the list is cut into by the score pass)
+int proxy_chunks(int fp32, const SeqList& seqs, int hq, int hkv);
 hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& seqs, int nb_max, int hq, int hkv,
                         const Strides& st, int w_sink, int w_local, int dense_below_n,
                         void* tstat /*[rows*128] float4*/, void* stats /*[nseq*hq*nchunk*128] float2*/,

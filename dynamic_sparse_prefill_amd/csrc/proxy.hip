@@ -32,10 +32,33 @@
 namespace crisp {
 
 constexpr int PCH = 16;       // most key blocks per score work-group (fewer when the grid would be small)
-constexpr int RS_TILES = 64;  // key blocks per row-statistics work-group
 
-int proxy_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
-__device__ __forceinline__ int rs_chunks(int nb) { return (nb + RS_TILES - 1) / RS_TILES; }
+// Key blocks per score work-group: PCH, or fewer so that a sequence alone
+// would give about two work-groups per CU (short sequences would otherwise run
+// a few long serial chains).  It depends on the sequence's own N_b only, so a
+// sequence is chunked the same way alone and in a packed batch; the score pass
+// writes one (max, sum) row partial per chunk, merged in chunk order.
+// chunks1: target chunk count of a sequence, ceil(2 * CUs / work-groups per chunk).
+__host__ __device__ inline int seq_kpc(int nb, int chunks1) {
+  const int k = (nb + chunks1 - 1) / chunks1;
+  return k < 1 ? 1 : (k > PCH ? PCH : k);
+}
+int proxy_chunks1(int fp32, int hq, int hkv) {
+  const int G = hq / hkv;
+  const int hpw = fp32 ? 1 : 2;   // query heads per score work-group (PX_HEADS for bf16)
+  const int groups = hkv * ((G + hpw - 1) / hpw);
+  const int want = 2 * device_cu_count();
+  return (want + groups - 1) / groups;
+}
+int proxy_chunks(int fp32, const SeqList& seqs, int hq, int hkv) {
+  const int c1 = proxy_chunks1(fp32, hq, hkv);
+  int nch = 1;
+  for (int i = 0; i < seqs.nseq; ++i) {
+    const int nb = seqs.nb[i], kpc = seq_kpc(nb, c1);
+    nch = std::max(nch, (nb + kpc - 1) / kpc);
+  }
+  return nch;
+}
 
 // Lower / upper sums of one interior tile for the wave owning rows 32w ..
 // 32w+31, p = exp2(s sl2 - mb): key sub-tile t < w lies wholly below the
@@ -68,6 +91,17 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
   }
 }
 
+// Online merge of a tile's (max m, sum of exp(s - m)) into a row's running
+// (M, L), in tile order.
+__device__ __forceinline__ void merge_row(float& M, float& L, float m, float tot, float sl2) {
+  if (m > M) {
+    L = L * fast_exp2((M - m) * sl2) + tot;
+    M = m;
+  } else {
+    L += tot * fast_exp2((m - M) * sl2);
+  }
+}
+
 // ---- bf16 score pass: 8 waves per work-group, one query head per 4 waves
 //
 // Two query heads of a KV group share each K tile, which is
@@ -80,6 +114,7 @@ __device__ __forceinline__ void interior_sums(const f32x16 (&s)[4], float sl2, f
 // maxima: the sums of the first half, taken relative to its own max, are
 // rescaled once when the second half raises it.
 constexpr int PX_HEADS = 2, PX_WAVES = 4 * PX_HEADS, PX_ROWS = BLK / PX_WAVES;   // PX_ROWS: K rows copied per wave
+static_assert(PX_HEADS == 2, "proxy_kpc counts two query heads per bf16 score work-group");
 
 typedef __attribute__((address_space(3))) void px_lds_void;
 constexpr int PX_WAIT_VM0 = 0x0F70;   // s_waitcnt: vector-memory count 0 only
@@ -113,8 +148,8 @@ struct PxCopy {   // the offsets are formed at each issue: a few ALU ops per til
 
 __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void proxy_scores_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, float4* __restrict__ tstat, float* __restrict__ kbar,
-    const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
-    int w_local, int dense_below_n, float sl2, int kpc) {
+    float2* __restrict__ stats, const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h,
+    int64_t sk_n, int w_sink, int w_local, int dense_below_n, float sl2, int chunks1, int nchunk) {
   __shared__ __attribute__((aligned(1024))) char sK0[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char sK1[BLK * 256];
   __shared__ __attribute__((aligned(16))) float red[2][PX_WAVES][HD];   // K-bar partials per (tile parity, wave)
@@ -130,6 +165,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
   const int64_t n = (int64_t)nb * BLK;
+  const int kpc = seq_kpc(nb, chunks1);
   if (chunk * kpc >= nb || seq_dense(nb, dense_below_n)) return;
   Q += sp.tok * sq_n;
   K += sp.tok * sk_n;
@@ -140,6 +176,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   if (scores) Tile<bf16>::load_q(qf, Q + (int64_t)(h0 + hg) * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const int kb0 = chunk * kpc, kb1 = min(nb, kb0 + kpc);
   const bf16* Kh = K + (int64_t)kvh * sk_h;
+  float rM = -1e30f, rL = 0.f;   // the row's max and sum over this chunk's key blocks
   const uint32_t krow = (uint32_t)(sk_n * 2);
   const int kspan = (int)((BLK - 1) * krow + 256);
   const PxCopy kc{krow, w, lane};
@@ -298,6 +335,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     up = pair_sum(up);
     an = pair_sum(an);
     if (g == 0) ts[(int64_t)kb * BLK + qrow] = make_float4(m, lo, up, an);
+    merge_row(rM, rL, m, lo + up, sl2);
   };
 
   kc.issue(Kh + (int64_t)kb0 * BLK * sk_n, kspan, sK0);
@@ -305,6 +343,8 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     tile(kb, sK0, sK1, 0);
     if (kb + 1 < kb1) tile(kb + 1, sK1, sK0, 1);
   }
+  if (scores && g == 0)
+    stats[(((int64_t)blockIdx.y * hq + h0 + hg) * nchunk + chunk) * BLK + qrow] = make_float2(rM, rL);
   if (kbar_wg) {
     __builtin_amdgcn_s_waitcnt(0);
     px_barrier();
@@ -319,8 +359,8 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
 // (bin N_b-2-kb) and the anchor windows.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proxy_tiles_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, float4* __restrict__ tstat, float* __restrict__ kbar,
-    const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h, int64_t sk_n, int w_sink,
-    int w_local, int dense_below_n, float sl2, int kpc) {
+    float2* __restrict__ stats, const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h,
+    int64_t sk_n, int w_sink, int w_local, int dense_below_n, float sl2, int chunks1, int nchunk) {
   __shared__ __attribute__((aligned(16))) float sK[BLK * Tile<float>::KP];
   __shared__ __attribute__((aligned(16))) float red[2][HD];   // K-bar column sums per half tile
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -333,6 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
   const int64_t n = (int64_t)nb * BLK;
+  const int kpc = seq_kpc(nb, chunks1);
   if (chunk * kpc >= nb || seq_dense(nb, dense_below_n)) return;
   Q += sp.tok * sq_n;
   K += sp.tok * sk_n;
@@ -343,6 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   Tile<float>::load_q(qf, Q + (int64_t)h * sq_h + (int64_t)((nb - 1) * BLK + qrow) * sq_n, g);
   const int kb0 = chunk * kpc, kb1 = min(nb, kb0 + kpc);
   const float* Kh = K + (int64_t)kvh * sk_h;
+  float rM = -1e30f, rL = 0.f;   // the row's max and sum over this chunk's key blocks
   for (int kb = kb0; kb < kb1; ++kb) {
     __syncthreads();
     Tile<float>::load_k(sK, Kh + (int64_t)kb * BLK * sk_n, sk_n, tid);
@@ -407,48 +449,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     up = pair_sum(up);
     an = pair_sum(an);
     if (g == 0) tstat[(int64_t)kb * BLK + qrow] = make_float4(mx, lo, up, an);
+    merge_row(rM, rL, mx, lo + up, sl2);
   }
+  if (g == 0) stats[(((int64_t)blockIdx.y * hq + h) * nchunk + chunk) * BLK + qrow] = make_float2(rM, rL);
 }
 
-// Row statistics over RS_TILES tiles: M = max of the tile maxima, L = sum of
-// the tile sums rescaled to M (online, in tile order).
-__global__ __launch_bounds__(BLK) void proxy_rowstat_kernel(const float4* __restrict__ tstat,
-                                                            float2* __restrict__ stats, const SeqList seqs, int hq,
-                                                            int hkv, int nchunk, int dense_below_n, float sl2) {
-  const int chunk = blockIdx.x, vh = blockIdx.y, r = threadIdx.x;
-  const int h = vh % hq;
-  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
-  const int nb = sp.nb;
-  if (seq_dense(nb, dense_below_n)) return;
-  const int t0 = chunk * RS_TILES, t1 = min(nb, t0 + RS_TILES);
-  tstat += (sp.rows + (int64_t)h * nb) * BLK;
-  float M = -1e30f, L = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    const float4 v = tstat[(int64_t)t * BLK + r];
-    const float tot = v.y + v.z;
-    if (v.x > M) {
-      L = L * fast_exp2((M - v.x) * sl2) + tot;
-      M = v.x;
-    } else {
-      L += tot * fast_exp2((v.x - M) * sl2);
-    }
-  }
-  stats[((int64_t)vh * nchunk + chunk) * BLK + r] = make_float2(M, L);
-}
-
-// Row normaliser of the proxy rows: M = max over chunks, 1/L with L rescaled to
-// M.  Eight groups of 128 threads take every eighth chunk; their partial
+// Row normaliser of the proxy rows from the score pass's chunk partials: M =
+// max over chunks, 1/L with L rescaled to M.  Eight groups of 128 threads take every eighth chunk; their partial
 // (max, sum) pairs are merged in group order, so the result is reproducible.
 constexpr int CMB_GROUPS = 8;
 __global__ __launch_bounds__(BLK * CMB_GROUPS) void proxy_combine_kernel(const float2* __restrict__ stats,
                                                                          float2* __restrict__ rowstat,
                                                                          const SeqList seqs, int hq, int nchunk,
-                                                                         int dense_below_n, float sl2) {
+                                                                         int chunks1, int dense_below_n, float sl2) {
   __shared__ float2 part[CMB_GROUPS][BLK];
   const int h = blockIdx.x, r = threadIdx.x % BLK, grp = threadIdx.x / BLK;   // h: virtual head
   const int nb = seqs.nb[h / hq];
   if (seq_dense(nb, dense_below_n)) return;
-  const int nc = rs_chunks(nb);
+  const int kpc = seq_kpc(nb, chunks1);
+  const int nc = (nb + kpc - 1) / kpc;   // the score pass's chunks of this sequence
   const float2* p = stats + (int64_t)h * nchunk * BLK + r;
   float M = -1e30f;
   for (int c = grp; c < nc; c += CMB_GROUPS) M = fmaxf(M, p[(int64_t)c * BLK].x);
@@ -505,28 +524,22 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const int G = hq / hkv;
   const int hpw = fp32 ? 1 : PX_HEADS;   // query heads per score work-group
   const int groups = hkv * ((G + hpw - 1) / hpw);
-  // key blocks per work-group: PCH, or fewer so that about two work-groups per
-  // CU exist (short sequences would otherwise run a few long serial chains)
-  const int64_t want = 2 * (int64_t)device_cu_count();
-  const int64_t per_chunk = (int64_t)groups * nseq;
-  const int64_t chunks = (want + per_chunk - 1) / per_chunk;
-  const int kpc = (int)std::max<int64_t>(1, std::min<int64_t>(PCH, (nb_max + chunks - 1) / chunks));
-  const dim3 grid((unsigned)(((nb_max + kpc - 1) / kpc) * groups), (unsigned)nseq);
+  const int chunks1 = proxy_chunks1(fp32, hq, hkv);
+  const int nchunk = proxy_chunks(fp32, seqs, hq, hkv);
+  const dim3 grid((unsigned)(nchunk * groups), (unsigned)nseq);
   if (fp32) {
-    proxy_tiles_f32_kernel<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar, seqs, hq,
-                                                 hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink, w_local, dense_below_n,
-                                                 sl2, kpc);
+    proxy_tiles_f32_kernel<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar,
+                                                 (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink,
+                                                 w_local, dense_below_n, sl2, chunks1, nchunk);
   } else {
     proxy_scores_bf16_kernel<<<grid, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
-                                                            seqs, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink,
-                                                            w_local, dense_below_n, sl2, kpc);
+                                                            (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
+                                                            st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
+                                                            nchunk);
   }
-  const int nchunk = proxy_chunks(nb_max);
   const unsigned vheads = (unsigned)(nseq * hq);
-  proxy_rowstat_kernel<<<dim3(nchunk, vheads), BLK, 0, s>>>((const float4*)tstat, (float2*)stats, seqs, hq, hkv,
-                                                             nchunk, dense_below_n, sl2);
   proxy_combine_kernel<<<vheads, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, seqs, hq, nchunk,
-                                                           dense_below_n, sl2);
+                                                           chunks1, dense_below_n, sl2);
   proxy_tilesum_kernel<<<dim3((nb_max + 3) / 4, vheads), 256, 0, s>>>((const float4*)tstat, (const float2*)rowstat,
                                                                       (float4*)tiles, seqs, hq, hkv, dense_below_n,
                                                                       sl2);
