@@ -88,7 +88,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
   size_t tstat, stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
-      pepart, peq, rtsum, total;
+      cand, pepart, peq, rtsum, total;
 };
 
 SeqList one_sequence(const crisp_shape* s) {
@@ -134,6 +134,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
   L.cut = take(vh * pe_cut_state_bytes());
   L.eqrow = take(rows * 4);
   L.counts = take(rows * 4);
+  L.cand = take((size_t)vh * pe_cand_cap(nb_max) * 8);
   L.jsd = take(vh * 8);
   L.abar = take(rows * 4);
   L.pepart = take(rows * nseg * 8);
@@ -214,6 +215,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.cut = w + L.cut;
   b.eqrow = (int32_t*)(w + L.eqrow);
   b.counts = (int32_t*)(w + L.counts);
+  b.cand = w + L.cand;
   b.pepart = w + L.pepart;
   b.peq = (int*)(w + L.peq);
   b.rtsum = (int32_t*)(w + L.rtsum);

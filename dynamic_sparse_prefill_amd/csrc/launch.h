@@ -91,6 +91,15 @@ struct PeCut;                       // per-head radix-select state (select.hip)
 size_t pe_cut_state_bytes();
 constexpr int PE_BUCKETS = 2048;    // histogram size of one radix pass
 int row_tiles(int64_t rows);        // tiles of the row-pointer scan
+// entries per Pooled-Estimation head kept by the last radix pass (those that
+// share the cut's top 22 bits); a head with more falls back to a full read
+inline int pe_cand_cap(int64_t nb_max) {
+  const int64_t c = nb_max * (nb_max + 1) / 2 / 256;
+  return (int)(c < 1024 ? 1024 : (c > 65536 ? 65536 : c));
+}
+// the capacity used: pe_cand_cap, or less where CRISP_PE_CAND_CAP asks for it
+// (both paths give the same counts; a smaller value sends heads to the full read)
+int pe_cand_limit(int64_t nb_max);
 
 struct SelectBufs {
   // inputs from the proxy
@@ -101,6 +110,7 @@ struct SelectBufs {
   int32_t *sv, *nv, *ss, *ns;
   uint32_t* hcnt;  unsigned long long* hmass;  void* cut;
   int32_t *eqrow, *counts;
+  void* cand;                       // [vh * pe_cand_cap(nb_max)] uint2: (packed row, value bits) of cut candidates
   void* pepart;                     // [hq * nb * nseg] float2: per-segment row max / sum of the pooled logits
   int* peq;                         // work counter of the pooled-logits kernel
   int32_t* rtsum;                   // [nseq * row_tiles(hq * nb_max)]: sums of tiles of row counts

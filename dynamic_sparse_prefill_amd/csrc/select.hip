@@ -34,6 +34,7 @@
 // round-to-nearest float32 operations in a fixed order so that it can be
 // reproduced exactly on the host from the same float32 scores.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -46,7 +47,7 @@ struct PeCut {
   unsigned long long total, target, need, above_mass, take, eq_cnt;
   uint32_t prefix, vstar;
   int32_t active;
-  int32_t pad;
+  int32_t ncand;   // entries the last radix pass kept as candidates (may exceed the capacity)
 };
 size_t pe_cut_state_bytes() { return sizeof(PeCut); }
 
@@ -1058,27 +1059,51 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
   cut[h] = c;
 }
 
-// count of entries equal to the cut value per row, then an exclusive scan per head (only when the cut
-// splits a run of equal values)
-// Per row of an active Pooled-Estimation head, from one read of the row: the
-// entries above the cut value (G), equal to it (E), and whether the two forced
-// entries (key blocks 0 and qb) lie below it.  The row's list length follows:
-// without a split run of equal values it is G + E + the forced entries below
-// the cut, written to counts here; with one, eqrow gets E (for the flat-order
-// scan) and counts the part that does not depend on the scan, completed by
-// the count pass of list_kernel.
-__global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
-                                                          int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
-                                                          const SeqList seqs, int hq, int hkv) {
+__device__ __forceinline__ int lane_prefix(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Last radix pass, one wave per row of an active Pooled-Estimation head (the
+// rows of the head's causal triangle, read once).  With the cut's top 22 bits
+// p22 fixed by the first two passes, an entry x with x >> 10 > p22 lies above
+// the cut value whatever its last 10 bits: the row's count of those goes to
+// counts (eqrow is cleared).  The entries with x >> 10 == p22 are the only
+// ones the cut can still fall among: they are added to the pass-2 histogram of
+// the last 10 bits and kept as (row, x) candidates, so that the entries above
+// or equal to the exact cut value are counted from the candidates alone.  All
+// entries of one pass-2 bucket are one float value, so a bucket's mass is its
+// count times that value's fixed-point mass: lanes holding the same value add
+// them with one pair of atomics.  Integer sums only: the histogram is the same
+// as a flat pass over the matrix gives.
+int pe_cand_limit(int64_t nb_max) {
+  int cap = pe_cand_cap(nb_max);
+  if (const char* e = std::getenv("CRISP_PE_CAND_CAP")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 0 && v < cap) cap = (int)v;
+  }
+  return cap;
+}
+
+static_assert(pe_shift(2) == 0 && pe_shift(1) == pe_width(2), "the last pass buckets the low bits under a 22-bit prefix");
+__global__ __launch_bounds__(256) void pe_last_pass_kernel(const float* __restrict__ P, PeCut* __restrict__ cut,
+                                                           uint32_t* __restrict__ hcnt,
+                                                           unsigned long long* __restrict__ hmass,
+                                                           int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
+                                                           uint2* __restrict__ cand, int cap, const SeqList seqs,
+                                                           int hq, int hkv) {
   const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
   const int qb = blockIdx.x * 4 + w;
-  const PeCut c = cut[h];
-  if (!c.active) return;
+  if (!cut[h].active) return;
+  const uint32_t p22 = cut[h].prefix >> 10;
   const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
   const int nb = sp.nb;
   if (qb >= nb) return;
+  const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
   const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
-  int eq = 0, gt = 0;
+  uint32_t* gc = hcnt + ((int64_t)h * 3 + 2) * PE_BUCKETS;
+  unsigned long long* gm = hmass + ((int64_t)h * 3 + 2) * PE_BUCKETS;
+  uint2* ch = cand + (int64_t)h * cap;
+  int above = 0;
   for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
     uint32_t xs[4];
 #pragma unroll
@@ -1086,26 +1111,97 @@ __global__ __launch_bounds__(256) void pe_eq_count_kernel(const float* __restric
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool valid = k0 + 64 * u <= qb;
-      eq += valid && xs[u] == c.vstar;
-      gt += valid && xs[u] > c.vstar;
+      const uint32_t x = xs[u], t = x >> 10;
+      above += valid && t > p22;
+      const bool match = valid && t == p22;
+      const unsigned long long mm = __ballot(match);
+      if (mm == 0) continue;   // wave-uniform: the common case
+      const int first = __builtin_ctzll(mm);
+      int base = 0;
+      if (lane == first) base = atomicAdd(&cut[h].ncand, __popcll(mm));
+      base = __shfl(base, first, 64);
+      if (match) {
+        const int at = base + lane_prefix(mm);
+        if (at < cap) ch[at] = make_uint2((uint32_t)r, x);
+      }
+      for (unsigned long long rest = mm; rest;) {   // one pair of atomics per distinct value
+        const int L0 = __builtin_ctzll(rest);
+        const uint32_t v = __shfl(x, L0, 64);
+        const unsigned long long same = __ballot(match && x == v);
+        if (lane == L0) {
+          const uint32_t n = (uint32_t)__popcll(same);
+          atomicAdd(&gc[v & ((1u << pe_width(2)) - 1)], n);
+          atomicAdd(&gm[v & ((1u << pe_width(2)) - 1)], (unsigned long long)n * fx_mass(v));
+        }
+        rest &= ~same;
+      }
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    eq += __shfl_xor(eq, o, 64);
-    gt += __shfl_xor(gt, o, 64);
-  }
+  for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o, 64);
   if (lane == 0) {
-    const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
-    const int forced_below = (row[0] < c.vstar) + (qb > 0 && row[qb] < c.vstar);
-    if (c.take < c.eq_cnt) {
+    counts[r] = above;
+    eqrow[r] = 0;
+  }
+}
+
+// After the last scan (cut value vstar): each candidate above vstar adds one
+// to its row's count, each equal to it one to the row's eqrow.  Heads whose
+// candidates overflowed the buffer are left to pe_eq_full_kernel.
+__global__ __launch_bounds__(256) void pe_cand_kernel(const PeCut* __restrict__ cut, const uint2* __restrict__ cand,
+                                                      int cap, int32_t* __restrict__ eqrow,
+                                                      int32_t* __restrict__ counts) {
+  const int h = blockIdx.y;
+  const PeCut c = cut[h];
+  if (!c.active || c.ncand > cap) return;
+  const uint2* ch = cand + (int64_t)h * cap;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < c.ncand; i += gridDim.x * 256) {
+    const uint2 e = ch[i];
+    if (e.y > c.vstar) atomicAdd(&counts[e.x], 1);
+    else if (e.y == c.vstar) atomicAdd(&eqrow[e.x], 1);
+  }
+}
+
+// The same per-row counts from a full read of every row, for a head whose
+// candidates did not fit (many entries sharing the cut's top 22 bits): count
+// of entries above vstar to counts, equal to it to eqrow.  Work-groups stride
+// over the rows; every other head returns at once.
+__global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
+                                                         int cap, int32_t* __restrict__ eqrow,
+                                                         int32_t* __restrict__ counts, const SeqList seqs, int hq,
+                                                         int hkv) {
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
+  const PeCut c = cut[h];
+  if (!c.active || c.ncand <= cap) return;
+  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
+  const int nb = sp.nb;
+  for (int qb = blockIdx.x * 4 + w; qb < nb; qb += gridDim.x * 4) {
+    const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
+    int eq = 0, gt = 0;
+    for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
+      uint32_t xs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool valid = k0 + 64 * u <= qb;
+        eq += valid && xs[u] == c.vstar;
+        gt += valid && xs[u] > c.vstar;
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      eq += __shfl_xor(eq, o, 64);
+      gt += __shfl_xor(gt, o, 64);
+    }
+    if (lane == 0) {
+      const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
+      counts[r] = gt;
       eqrow[r] = eq;
-      counts[r] = gt + forced_below;
-    } else {
-      counts[r] = gt + eq + forced_below;
     }
   }
 }
 
+// Exclusive scan of eqrow per head, in flat (row-major) order, when the cut
+// splits a run of equal values.
 __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict__ cut, int32_t* __restrict__ eqrow,
                                                          const SeqList seqs, int hq, int hkv) {
   __shared__ int sh[256];
@@ -1125,10 +1221,6 @@ __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict
 }
 
 // ------------------------------------------------------------------ lists
-
-__device__ __forceinline__ int lane_prefix(unsigned long long m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-}
 
 // One wave per (head, query block).  FILL = false writes the row's count
 // (Pooled-Estimation rows: completes what pe_eq_count wrote, without reading
@@ -1162,19 +1254,26 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
     const uint32_t* bits = (const uint32_t*)(P + sp.tri + (int64_t)hl * tri(nb) + tri(qb));
     const bool split = c.take < c.eq_cnt;
     if (!FILL) {
-      // pe_eq_count wrote the count, or with a split run its part without the
-      // tied entries: of the row's E tied entries the first T in flat order
-      // are taken, T = clamp(take - (tied entries before the row), 0, E); a
-      // forced entry that is tied but not among them is added on its own (key
-      // block 0 is the row's first tied entry, qb its last)
-      if (split && lane == 0) {
-        const int32_t* e = eqrow + sp.rows + (int64_t)hl * nb;
-        const long long before = e[qb];
-        const long long E = (qb + 1 < nb ? (long long)e[qb + 1] : (long long)c.eq_cnt) - before;
-        const long long room = (long long)c.take - before;
-        const long long T = room < 0 ? 0 : (room > E ? E : room);
-        const int extra = (bits[0] == c.vstar && T == 0) + (qb > 0 && bits[qb] == c.vstar && T < E);
-        counts[row] += (int)T + extra;
+      // counts holds the row's entries above the cut value (G) and eqrow its
+      // entries equal to it (E), or with a split run the exclusive scan of E
+      // in flat order.  The row takes G, the two forced entries (key blocks 0
+      // and qb) where they lie below the cut, and E, or with a split run the
+      // first T of its tied entries in flat order, T = clamp(take - (tied
+      // entries before the row), 0, E), plus a forced entry that is tied but
+      // not among them (key block 0 is the row's first tied entry, qb its last)
+      if (lane == 0) {
+        int add = (bits[0] < c.vstar) + (qb > 0 && bits[qb] < c.vstar);
+        if (split) {
+          const int32_t* e = eqrow + sp.rows + (int64_t)hl * nb;
+          const long long before = e[qb];
+          const long long E = (qb + 1 < nb ? (long long)e[qb + 1] : (long long)c.eq_cnt) - before;
+          const long long room = (long long)c.take - before;
+          const long long T = room < 0 ? 0 : (room > E ? E : room);
+          add += (int)T + (bits[0] == c.vstar && T == 0) + (qb > 0 && bits[qb] == c.vstar && T < E);
+        } else {
+          add += eqrow[row];
+        }
+        counts[row] += add;
       }
       return;
     }
@@ -1433,9 +1532,12 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
   pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
   pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_hist_kernel<2><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  const int cap = pe_cand_limit(nb_max);
+  pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
+                                                                  (uint2*)b.cand, cap, seqs, hq, hkv);
   pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_eq_count_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.eqrow, b.counts, seqs, hq, hkv);
+  pe_cand_kernel<<<dim3(8, vh), 256, 0, s>>>(cut, (const uint2*)b.cand, cap, b.eqrow, b.counts);
+  pe_eq_full_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, cut, cap, b.eqrow, b.counts, seqs, hq, hkv);
   pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
   const dim3 gl((nb_max + 3) / 4, vh);
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);

@@ -5,6 +5,8 @@ Llama / Qwen layers (32k, 128k, 512k) are compared on every routing and
 selection decision and on a seeded sample of query blocks, in the same launch
 configuration the bench times.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -265,6 +267,57 @@ def test_parameter_sweep_and_min_blocks():
                 if mb:
                     nv = sel.nv.cpu().numpy()[sel.route.cpu().numpy() == 1]
                     assert np.all(nv >= mb)
+
+
+@pytest.mark.parametrize("case", ["llama", "zero_q"])
+def test_pe_cut_candidates_equal_full_read(case):
+    """The last radix pass counts each Pooled-Estimation row's entries above and
+    at the cut value from the few entries that share the cut's top 22 bits; a
+    head with more of them than the buffer holds reads its rows in full
+    instead.  CRISP_PE_CAND_CAP=0 sends every head to the full read: the
+    selection must be bitwise the same.  With Q = 0 every pooled row is uniform
+    (p = 1/(qb+1)), so the cut falls inside a run of equal values and only part
+    of it is taken (the flat-order tie rule)."""
+    cfg = synth.custom_config("candcap", 8192, 8, 2, seed=51, conc_frac=0.5)
+    spec = synth.make_spec(cfg)
+    Q, K, V = synth.generate(spec)
+    if case == "zero_q":
+        Q[:] = 0
+    q, k = P.to_device(spec, Q), P.to_device(spec, K)
+    p = P.params_of(cfg, tau=2.0) if case == "zero_q" else P.params_of(cfg)   # tau 2: every head pooled
+    a = dsp.crisp_select(q, k, p, pe_prob=True)
+    torch.cuda.synchronize()
+    os.environ["CRISP_PE_CAND_CAP"] = "0"
+    try:
+        b = dsp.crisp_select(q, k, p, pe_prob=True)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["CRISP_PE_CAND_CAP"]
+    route = a.route.cpu().numpy()
+    P.log(f"[cand {case}] routes VS={int((route == 1).sum())} PE={int((route == 0).sum())}")
+    assert (route == 0).any()
+    if case == "zero_q":
+        assert (route == 0).all()
+    for f in ("route", "c_struct", "row_ptr", "nv", "ns"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    n = int(a.row_ptr[-1])
+    assert torch.equal(a.col_idx[:n], b.col_idx[:n])
+    rep = P.check_decisions(a, cfg.hq, cfg.nb, p, name=f"candcap {case}")
+    P.log(f"[cand {case}]", rep)
+    assert rep["heads_checked"] + rep["pe_exempt"] + rep["vs_exempt"] + rep["route_ties"] == cfg.hq
+    if case == "zero_q":
+        # uniform rows: entry (qb, kb) is 1/(qb+1); the kept set is every row
+        # above some qb*, part of row qb* in flat order, and the two anchors of
+        # the rows below it
+        rp = a.row_ptr.cpu().numpy()
+        cnt = np.diff(rp)
+        full = cnt == np.tile(np.arange(1, cfg.nb + 1), cfg.hq)
+        for h in range(cfg.hq):
+            c = cnt[h * cfg.nb:(h + 1) * cfg.nb]
+            f_ = full[h * cfg.nb:(h + 1) * cfg.nb]
+            part = np.nonzero(~f_)[0]
+            assert part.size and f_[:part[0]].all(), "rows before the cut are whole"
+            assert np.all(c[part[1:]] == np.minimum(2, part[1:] + 1)), "rows past the cut keep their anchors"
 
 
 def test_selection_is_deterministic():
