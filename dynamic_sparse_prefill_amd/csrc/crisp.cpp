@@ -88,7 +88,7 @@ int64_t tri(int64_t nb) { return nb * (nb + 1) / 2; }
 // Selection workspace layout (every region 256-byte aligned).
 struct SelectLayout {
   size_t tstat, stats, rowstat, tiles, pv, ps, sv, ss, nv, ns, kbar, qbar, P, hcnt, hmass, cut, eqrow, counts, jsd, abar,
-      cand, pepart, peq, rtsum, total;
+      cand, pnorm, pepart, peq, rtsum, total;
 };
 
 SeqList one_sequence(const crisp_shape* s) {
@@ -135,6 +135,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
   L.eqrow = take(rows * 4);
   L.counts = take(rows * 4);
   L.cand = take((size_t)vh * pe_cand_cap(nb_max) * 8);
+  L.pnorm = take(rows * 8);
   L.jsd = take(vh * 8);
   L.abar = take(rows * 4);
   L.pepart = take(rows * nseg * 8);
@@ -205,7 +206,9 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.pv = (float*)(w + L.pv);
   b.ps = (float*)(w + L.ps);
   b.qbar = (float*)(w + L.qbar);
-  b.P = out->pe_prob ? out->pe_prob : (float*)(w + L.P);
+  b.P = (float*)(w + L.P);
+  b.pnorm = w + L.pnorm;
+  b.pe_prob = out->pe_prob;
   b.sv = (int32_t*)(w + L.sv);
   b.nv = (int32_t*)(w + L.nv);
   b.ss = (int32_t*)(w + L.ss);

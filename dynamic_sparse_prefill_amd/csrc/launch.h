@@ -106,7 +106,10 @@ struct SelectBufs {
   const void* tiles;
   const float* kbar;
   // scratch
-  float *pv, *ps, *qbar, *P;
+  float *pv, *ps, *qbar;
+  float* P;                         // [hq * N_b (N_b + 1) / 2] pooled logits of the PE heads (causal triangles)
+  void* pnorm;                      // [hq * N_b] float2: (max, 1/sum) of each pooled row
+  float* pe_prob;                   // optional caller output: the pooled probabilities, same layout as P
   int32_t *sv, *nv, *ss, *ns;
   uint32_t* hcnt;  unsigned long long* hmass;  void* cut;
   int32_t *eqrow, *counts;

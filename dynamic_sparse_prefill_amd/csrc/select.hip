@@ -6,16 +6,19 @@
 //              S_d = {k : p_k > alpha mu_d} U {0, N_b - 1} per direction
 //              [CRISP §4], compacted in ascending order; optional min budget.
 //  pool_q      block means of Q for Pooled-Estimation heads.
-//  pe_logits   pooled logits Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb (fp32
-//              MFMA), with per-segment row max / sum;
-//  pe_norm_hist the causal row softmax [CRISP §2, PE path], in place, in
-//              the same sweep as the first radix pass of the cut;
-//  pe_hist/    global gamma-cut over the flattened causal matrix: a radix
-//  pe_scan     select on the float32 bit pattern (11+11+10 bits, three
-//              passes) with per-bucket mass in 2^-46 fixed point, so the sums
-//              are exact integers and order-independent.  Entries are taken in
-//              descending value, ties by ascending row-major flat index,
-//              until the mass reaches gamma * total.
+//  pe_logits   pooled logits Qbar[qb] . Kbar[kb] / sqrt(d), kb <= qb
+//              (float32 accuracy on the bf16 matrix unit), stored once, with
+//              per-segment row max / sum;
+//  pe_flat_pass/ the causal row softmax [CRISP §2, PE path], formed from the
+//  pe_last_pass  stored logits and each row's normaliser by every pass that
+//  pe_scan     reads the matrix, and the global gamma-cut over the flattened
+//              causal matrix: a radix select on the float32 bit pattern
+//              (11+11+10 bits, three passes) with per-bucket mass in 2^-46
+//              fixed point, so the sums are exact integers and
+//              order-independent.  Entries are taken in descending value, ties
+//              by ascending row-major flat index, until the mass reaches gamma
+//              * total.  The last pass also counts each row's entries above
+//              the cut.
 //  list_*      per (head, query block) ascending key-block lists in one CSR:
 //              VS rows = {S_v <= qb} U {qb - S_s} U {0, qb}, PE rows = the
 //              selected entries of the row plus (qb, 0) and (qb, qb), dense
@@ -52,8 +55,18 @@ struct PeCut {
 size_t pe_cut_state_bytes() { return sizeof(PeCut); }
 
 constexpr double FX_SCALE = 70368744177664.0;  // 2^46
+// floor(x * 2^46) of the float32 x with bit pattern bits.  For 0 <= x <= 1
+// (exponent field e <= 127) it is formed from the bits: x = m 2^(e - 150) with
+// the 24-bit significand m, so x 2^46 = m 2^(e - 104), a shift of m (floor on
+// a right shift); other values take the double product.  The two agree on
+// every float in [0, 1].
 __device__ __forceinline__ unsigned long long fx_mass(uint32_t bits) {
-  return (unsigned long long)((double)__uint_as_float(bits) * FX_SCALE);
+  const uint32_t e = bits >> 23;   // sign and exponent
+  if (e > 127) return (unsigned long long)((double)__uint_as_float(bits) * FX_SCALE);
+  const uint32_t m = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  if (e >= 104) return (unsigned long long)m << (e - 104);
+  const uint32_t sh = 104 - e;
+  return sh < 24 ? (unsigned long long)(m >> sh) : 0ull;
 }
 
 // ------------------------------------------------------------------ block helpers (256 threads)
@@ -794,28 +807,85 @@ constexpr int PE_SLICE = 32768;  // entries per histogram work-group
 __host__ __device__ constexpr int pe_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __host__ __device__ constexpr int pe_width(int pass) { return pass == 2 ? 10 : 11; }
 
+// Pooled probability of the stored logit x in a row whose normaliser is n =
+// (max M, 1/S).  Every pass forms the probabilities with this one function
+// from the logits the logits kernel wrote, so all of them see the same float32
+// bits (the matrix is never rewritten).
+__device__ __forceinline__ uint32_t pe_p(float x, float2 n) { return __float_as_uint(pe_exp(x - n.x) * n.y); }
+
+// Row normaliser of pooled row qb from its segments' (max, sum of exp(x - max)),
+// in segment order: M = the largest segment max, S = the sums rescaled to M.
+__device__ __forceinline__ float2 pe_row_norm(const float2* __restrict__ pp, int qb) {
+  const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;
+  float M = -INFINITY;
+  for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
+  float S = 0.f;
+  for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * pe_exp(pp[c].x - M);
+  return make_float2(M, 1.f / S);
+}
+
+// Offsets inside one head's triangle fit in 32 bits: tri(32768) < 2^31.
+__device__ __forceinline__ int tri32(int qb) { return qb * (qb + 1) / 2; }
+__device__ __forceinline__ int tri_row(int e) {   // the row qb with tri(qb) <= e < tri(qb + 1)
+  int r = (int)((sqrtf(8.f * (float)e + 1.f) - 1.f) * 0.5f);   // within one of the row; fixed below
+  while (tri32(r + 1) <= e) ++r;
+  while (tri32(r) > e) --r;
+  return r;
+}
+
+// First two radix passes over the flattened causal triangle of a
+// Pooled-Estimation head.  Work-group (s, vh) takes entries [s * slice,
+// +slice), slice = PE_SLICE or less where the grid would not fill the device
+// (at most 256 rows: rows 0..255 already hold more than PE_SLICE entries),
+// and forms each entry's probability from its logit and its row's normaliser.  Pass 0 builds the normalisers from the logits
+// kernel's segment partials (storing those of the rows that start in the
+// slice, for the later passes), writes the probabilities to pe_prob when the
+// caller asks for them, and histograms the top 11 bits of every entry; pass 1
+// histograms the next 11 bits of the entries under the pass-0 prefix.
 template <int PASS>
-__global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
-                                                      uint32_t* __restrict__ hcnt,
-                                                      unsigned long long* __restrict__ hmass, const SeqList seqs,
-                                                      int hq, int hkv) {
+__global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __restrict__ route,
+                                                           const float* __restrict__ P,
+                                                           const float2* __restrict__ part, float2* __restrict__ pnorm,
+                                                           float* __restrict__ pe_prob, const PeCut* __restrict__ cut,
+                                                           uint32_t* __restrict__ hcnt,
+                                                           unsigned long long* __restrict__ hmass, const SeqList seqs,
+                                                           int hq, int hkv, int nseg, int slice) {
   __shared__ uint32_t sc[PE_BUCKETS];
   __shared__ unsigned long long sm[PE_BUCKETS];
+  __shared__ float2 sN[256];
   const int h = blockIdx.y, tid = threadIdx.x;   // h: virtual head
-  if (!cut[h].active) return;
+  if (route[h] != 0) return;
+  const bool active = cut[h].active;
+  if (PASS > 0 && !active) return;
   const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
-  const int64_t total = tri(sp.nb);
-  if ((int64_t)blockIdx.x * PE_SLICE >= total) return;
-  P += sp.tri + (int64_t)(h % hq) * total;
+  const int nb = sp.nb;
+  const int total = tri32(nb);
+  const int a = blockIdx.x * slice;
+  if (a >= total) return;
+  const int b = min(total, a + slice);
+  const int64_t hrow = sp.rows + (int64_t)(h % hq) * nb;   // packed index of the head's row 0
+  const float* Ph = P + sp.tri + (int64_t)(h % hq) * total;
+  float* Oh = (PASS == 0 && pe_prob) ? pe_prob + sp.tri + (int64_t)(h % hq) * total : nullptr;
+  const int r0 = tri_row(a), r1 = tri_row(b - 1);
+  if (tid <= r1 - r0) {
+    const int qb = r0 + tid;
+    float2 nrm;
+    if (PASS == 0) {
+      nrm = pe_row_norm(part + (hrow + qb) * nseg, qb);
+      if (tri32(qb) >= a) pnorm[hrow + qb] = nrm;   // once: by the slice in which the row starts
+    } else {
+      nrm = pnorm[hrow + qb];
+    }
+    sN[tid] = nrm;
+  }
+  for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
+  __syncthreads();
   constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
   constexpr uint32_t mask = (1u << width) - 1;
   constexpr int hi = shift + width;
-  const uint32_t prefix = cut[h].prefix;
-  for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
-  __syncthreads();
-  const uint32_t* bits = (const uint32_t*)P;
-  const int64_t a = (int64_t)blockIdx.x * PE_SLICE, b = min(total, a + PE_SLICE);
-  // neighbouring entries of a softmax row mostly fall into the same bucket:
+  const uint32_t prefix = PASS > 0 ? cut[h].prefix : 0u;
+  const bool hist = PASS > 0 || active;
+  // neighbouring entries of a softmax row often fall into the same bucket:
   // each thread merges runs of equal buckets in registers (over its strided
   // entries) and commits a run with one pair of LDS atomics
   uint32_t run_b = 0xffffffffu, run_c = 0;
@@ -832,175 +902,82 @@ __global__ __launch_bounds__(256) void pe_hist_kernel(const float* __restrict__ 
     ++run_c;
     run_m += fx_mass(x);
   };
-  constexpr int U = 4;
-  if (((uintptr_t)bits & 15) == 0) {
-    // 16-byte loads of four consecutive entries, four loads in flight per
-    // thread; a ragged end of the slice is read entry by entry
-    for (int64_t e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
-      uint4 xs[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t e = e0 + 1024 * u;
-        if (e + 4 <= b) xs[u] = *(const uint4*)(bits + e);
-        else xs[u] = make_uint4(e < b ? bits[e] : 0u, e + 1 < b ? bits[e + 1] : 0u, e + 2 < b ? bits[e + 2] : 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t e = e0 + 1024 * u;
-        if (e >= b) break;
-        take(xs[u].x);
-        if (e + 1 < b) take(xs[u].y);
-        if (e + 2 < b) take(xs[u].z);
-        if (e + 3 < b) take(xs[u].w);
-      }
-    }
-  } else {
-    // four strided entries are loaded before any is used (memory-level
-    // parallelism); they are then taken in the same order as one at a time
-    for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
-      uint32_t xs[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? bits[e0 + 256 * u] : 0u;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (e0 + 256 * u >= b) break;
-        take(xs[u]);
-      }
-    }
-  }
-  if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
-  __syncthreads();
-  uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
-  unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
-  for (int i = tid; i < PE_BUCKETS; i += 256)
-    if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
-}
-
-// Row softmax and the first radix pass in one sweep.  Work-group (slice, vh)
-// takes entries [slice * PE_SLICE, +PE_SLICE) of Pooled-Estimation head vh's
-// flattened causal triangle (at most 256 rows: rows 0..255 already hold more
-// than PE_SLICE entries): it merges each of its rows' segment maxima and sums
-// into the row's max M and 1/S, then replaces every logit x in place by
-// P = exp(x - M) / S and, when the head's cut is active, adds P to the pass-0
-// histogram.  The same values as a separate normalising pass, one read of the
-// matrix fewer.
-__device__ __forceinline__ int tri_row(int64_t e) {   // the row qb with tri(qb) <= e < tri(qb + 1)
-  int r = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
-  while (tri(r + 1) <= e) ++r;
-  while (tri(r) > e) --r;
-  return r;
-}
-
-__global__ __launch_bounds__(256) void pe_norm_hist_kernel(const int32_t* __restrict__ route,
-                                                           const float2* __restrict__ part, float* __restrict__ P,
-                                                           const PeCut* __restrict__ cut,
-                                                           uint32_t* __restrict__ hcnt,
-                                                           unsigned long long* __restrict__ hmass, const SeqList seqs,
-                                                           int hq, int hkv, int nseg) {
-  __shared__ uint32_t sc[PE_BUCKETS];
-  __shared__ unsigned long long sm[PE_BUCKETS];
-  __shared__ float sM[256], sInv[256];
-  const int h = blockIdx.y, tid = threadIdx.x;   // h: virtual head
-  if (route[h] != 0) return;
-  const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
-  const int nb = sp.nb;
-  const int64_t total = tri(nb);
-  const int64_t a = (int64_t)blockIdx.x * PE_SLICE;
-  if (a >= total) return;
-  const int64_t b = min(total, a + PE_SLICE);
-  const bool active = cut[h].active;
-  float* Ph = P + sp.tri + (int64_t)(h % hq) * total;
-  const int r0 = tri_row(a), r1 = tri_row(b - 1);
-  if (tid <= r1 - r0) {   // this row's normaliser, as the separate softmax pass forms it
-    const int qb = r0 + tid;
-    const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;
-    const float2* pp = part + (sp.rows + (int64_t)(h % hq) * nb + qb) * nseg;
-    float M = -INFINITY;
-    for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
-    float S = 0.f;
-    for (int c = 0; c < ns; ++c) S += pp[c].x == -INFINITY ? 0.f : pp[c].y * pe_exp(pp[c].x - M);
-    sM[tid] = M;
-    sInv[tid] = 1.f / S;
-  }
-  for (int i = tid; i < PE_BUCKETS; i += 256) { sc[i] = 0; sm[i] = 0; }
-  __syncthreads();
-  constexpr uint32_t mask = (1u << pe_width(0)) - 1;
-  uint32_t run_b = 0xffffffffu, run_c = 0;
-  unsigned long long run_m = 0;
-  auto take = [&](uint32_t x) {
-    const uint32_t bk = (x >> pe_shift(0)) & mask;
-    if (bk != run_b) {
-      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
-      run_b = bk;
-      run_c = 0;
-      run_m = 0;
-    }
-    ++run_c;
-    run_m += fx_mass(x);
+  // probability of entry e of row r; r, the start of row r + 1 (rend) and the
+  // row's normaliser are carried from one entry of a thread to the next
+  int r = 0, rend = 0;
+  float2 nrm = make_float2(0.f, 0.f);
+  auto at_row = [&](int e) {   // start tracking at entry e
+    r = tri_row(e);
+    rend = tri32(r + 1);
+    nrm = sN[r - r0];
   };
-  // normalise entry e (row r, tracked forward from the previous entry of the thread)
-  auto norm = [&](int64_t e, int& r, float x) -> float {
-    while (tri(r + 1) <= e) ++r;
-    return pe_exp(x - sM[r - r0]) * sInv[r - r0];
+  auto prob = [&](int e, float x) -> uint32_t {
+    if (e >= rend) {
+      do { ++r; rend += r + 1; } while (e >= rend);
+      nrm = sN[r - r0];
+    }
+    return pe_p(x, nrm);
   };
   constexpr int U = 4;
-  if (((uintptr_t)Ph & 15) == 0) {
+  if (((uintptr_t)Ph & 15) == 0 && (!Oh || ((uintptr_t)Oh & 15) == 0)) {
     // 16-byte loads of four consecutive entries, four loads in flight per thread
-    for (int64_t e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
+    for (int e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
       float4 xs[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t e = e0 + 1024 * u;
+        const int e = e0 + 1024 * u;
         if (e + 4 <= b) xs[u] = *(const float4*)(Ph + e);
         else xs[u] = make_float4(e < b ? Ph[e] : 0.f, e + 1 < b ? Ph[e + 1] : 0.f, e + 2 < b ? Ph[e + 2] : 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t e = e0 + 1024 * u;
+        const int e = e0 + 1024 * u;
         if (e >= b) break;
-        int r = tri_row(e);
-        float4 y;
-        y.x = norm(e, r, xs[u].x);
-        y.y = e + 1 < b ? norm(e + 1, r, xs[u].y) : 0.f;
-        y.z = e + 2 < b ? norm(e + 2, r, xs[u].z) : 0.f;
-        y.w = e + 3 < b ? norm(e + 3, r, xs[u].w) : 0.f;
-        if (e + 4 <= b) {
-          *(float4*)(Ph + e) = y;
-        } else {
-          Ph[e] = y.x;
-          if (e + 1 < b) Ph[e + 1] = y.y;
-          if (e + 2 < b) Ph[e + 2] = y.z;
+        at_row(e);
+        uint4 y;
+        y.x = prob(e, xs[u].x);
+        y.y = e + 1 < b ? prob(e + 1, xs[u].y) : 0u;
+        y.z = e + 2 < b ? prob(e + 2, xs[u].z) : 0u;
+        y.w = e + 3 < b ? prob(e + 3, xs[u].w) : 0u;
+        if (Oh) {
+          if (e + 4 <= b) {
+            *(uint4*)(Oh + e) = y;
+          } else {
+            Oh[e] = __uint_as_float(y.x);
+            if (e + 1 < b) Oh[e + 1] = __uint_as_float(y.y);
+            if (e + 2 < b) Oh[e + 2] = __uint_as_float(y.z);
+          }
         }
-        if (active) {
-          take(__float_as_uint(y.x));
-          if (e + 1 < b) take(__float_as_uint(y.y));
-          if (e + 2 < b) take(__float_as_uint(y.z));
-          if (e + 3 < b) take(__float_as_uint(y.w));
+        if (hist) {
+          take(y.x);
+          if (e + 1 < b) take(y.y);
+          if (e + 2 < b) take(y.z);
+          if (e + 3 < b) take(y.w);
         }
       }
     }
   } else {
     // four strided entries are loaded before any is used
-    for (int64_t e0 = a + tid; e0 < b; e0 += U * 256) {
+    for (int e0 = a + tid; e0 < b; e0 += U * 256) {
       float xs[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) xs[u] = e0 + 256 * u < b ? Ph[e0 + 256 * u] : 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t e = e0 + 256 * u;
+        const int e = e0 + 256 * u;
         if (e >= b) break;
-        int r = tri_row(e);
-        const float y = norm(e, r, xs[u]);
-        Ph[e] = y;
-        if (active) take(__float_as_uint(y));
+        at_row(e);
+        const uint32_t y = prob(e, xs[u]);
+        if (Oh) Oh[e] = __uint_as_float(y);
+        if (hist) take(y);
       }
     }
   }
-  if (!active) return;
+  if (!hist) return;
   if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
   __syncthreads();
-  uint32_t* gc = hcnt + (int64_t)h * 3 * PE_BUCKETS;
-  unsigned long long* gm = hmass + (int64_t)h * 3 * PE_BUCKETS;
+  uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
+  unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   for (int i = tid; i < PE_BUCKETS; i += 256)
     if (sc[i]) { atomicAdd(&gc[i], sc[i]); atomicAdd(&gm[i], sm[i]); }
 }
@@ -1085,7 +1062,8 @@ int pe_cand_limit(int64_t nb_max) {
 }
 
 static_assert(pe_shift(2) == 0 && pe_shift(1) == pe_width(2), "the last pass buckets the low bits under a 22-bit prefix");
-__global__ __launch_bounds__(256) void pe_last_pass_kernel(const float* __restrict__ P, PeCut* __restrict__ cut,
+__global__ __launch_bounds__(256) void pe_last_pass_kernel(const float* __restrict__ P,
+                                                           const float2* __restrict__ pnorm, PeCut* __restrict__ cut,
                                                            uint32_t* __restrict__ hcnt,
                                                            unsigned long long* __restrict__ hmass,
                                                            int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
@@ -1099,19 +1077,20 @@ __global__ __launch_bounds__(256) void pe_last_pass_kernel(const float* __restri
   const int nb = sp.nb;
   if (qb >= nb) return;
   const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
-  const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
+  const float* row = P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb);
+  const float2 nrm = pnorm[r];
   uint32_t* gc = hcnt + ((int64_t)h * 3 + 2) * PE_BUCKETS;
   unsigned long long* gm = hmass + ((int64_t)h * 3 + 2) * PE_BUCKETS;
   uint2* ch = cand + (int64_t)h * cap;
   int above = 0;
-  for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
-    uint32_t xs[4];
+  for (int k0 = lane; k0 <= qb; k0 += 512) {   // eight loads in flight per lane
+    float xs[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0u;
+    for (int u = 0; u < 8; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const bool valid = k0 + 64 * u <= qb;
-      const uint32_t x = xs[u], t = x >> 10;
+      const uint32_t x = pe_p(xs[u], nrm), t = x >> 10;
       above += valid && t > p22;
       const bool match = valid && t == p22;
       const unsigned long long mm = __ballot(match);
@@ -1165,7 +1144,8 @@ __global__ __launch_bounds__(256) void pe_cand_kernel(const PeCut* __restrict__ 
 // candidates did not fit (many entries sharing the cut's top 22 bits): count
 // of entries above vstar to counts, equal to it to eqrow.  Work-groups stride
 // over the rows; every other head returns at once.
-__global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict__ P, const PeCut* __restrict__ cut,
+__global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict__ P,
+                                                         const float2* __restrict__ pnorm, const PeCut* __restrict__ cut,
                                                          int cap, int32_t* __restrict__ eqrow,
                                                          int32_t* __restrict__ counts, const SeqList seqs, int hq,
                                                          int hkv) {
@@ -1175,17 +1155,20 @@ __global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict
   const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
   const int nb = sp.nb;
   for (int qb = blockIdx.x * 4 + w; qb < nb; qb += gridDim.x * 4) {
-    const uint32_t* row = (const uint32_t*)(P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb));
+    const float* row = P + sp.tri + (int64_t)(h % hq) * tri(nb) + tri(qb);
+    const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
+    const float2 nrm = pnorm[r];
     int eq = 0, gt = 0;
     for (int k0 = lane; k0 <= qb; k0 += 256) {   // four loads in flight per lane
-      uint32_t xs[4];
+      float xs[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0u;
+      for (int u = 0; u < 4; ++u) xs[u] = k0 + 64 * u <= qb ? row[k0 + 64 * u] : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool valid = k0 + 64 * u <= qb;
-        eq += valid && xs[u] == c.vstar;
-        gt += valid && xs[u] > c.vstar;
+        const uint32_t x = pe_p(xs[u], nrm);
+        eq += valid && x == c.vstar;
+        gt += valid && x > c.vstar;
       }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -1193,7 +1176,6 @@ __global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict
       gt += __shfl_xor(gt, o, 64);
     }
     if (lane == 0) {
-      const int64_t r = sp.rows + (int64_t)(h % hq) * nb + qb;
       counts[r] = gt;
       eqrow[r] = eq;
     }
@@ -1229,7 +1211,8 @@ template <bool FILL>
 __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ route,
                                                    const int32_t* __restrict__ sv, const int32_t* __restrict__ nv,
                                                    const int32_t* __restrict__ ss, const int32_t* __restrict__ ns,
-                                                   const float* __restrict__ P, const PeCut* __restrict__ cut,
+                                                   const float* __restrict__ P, const float2* __restrict__ pnorm,
+                                                   const PeCut* __restrict__ cut,
                                                    const int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
                                                    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
                                                    const SeqList seqs, int hq, int hkv, int nb_max, int pe_all) {
@@ -1251,7 +1234,8 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
   }
   if (r == 0) {
     const PeCut c = cut[h];
-    const uint32_t* bits = (const uint32_t*)(P + sp.tri + (int64_t)hl * tri(nb) + tri(qb));
+    const float* lg = P + sp.tri + (int64_t)hl * tri(nb) + tri(qb);   // the row's logits
+    const float2 nrm = pnorm[row];
     const bool split = c.take < c.eq_cnt;
     if (!FILL) {
       // counts holds the row's entries above the cut value (G) and eqrow its
@@ -1262,14 +1246,15 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
       // entries before the row), 0, E), plus a forced entry that is tied but
       // not among them (key block 0 is the row's first tied entry, qb its last)
       if (lane == 0) {
-        int add = (bits[0] < c.vstar) + (qb > 0 && bits[qb] < c.vstar);
+        const uint32_t p0 = pe_p(lg[0], nrm), pd = pe_p(lg[qb], nrm);   // the two anchors
+        int add = (p0 < c.vstar) + (qb > 0 && pd < c.vstar);
         if (split) {
           const int32_t* e = eqrow + sp.rows + (int64_t)hl * nb;
           const long long before = e[qb];
           const long long E = (qb + 1 < nb ? (long long)e[qb + 1] : (long long)c.eq_cnt) - before;
           const long long room = (long long)c.take - before;
           const long long T = room < 0 ? 0 : (room > E ? E : room);
-          add += (int)T + (bits[0] == c.vstar && T == 0) + (qb > 0 && bits[qb] == c.vstar && T < E);
+          add += (int)T + (p0 == c.vstar && T == 0) + (qb > 0 && pd == c.vstar && T < E);
         } else {
           add += eqrow[row];
         }
@@ -1281,11 +1266,11 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
     long long eqb = split ? eqrow[row] : 0;
     // eight 64-entry pieces are loaded before any is used, then taken in order
     for (int k00 = 0; k00 <= qb; k00 += 512) {
-      uint32_t xs[8];
+      float xs[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = k00 + 64 * u + lane;
-        xs[u] = k <= qb ? bits[k] : 0u;
+        xs[u] = k <= qb ? lg[k] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1293,7 +1278,7 @@ __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ r
         if (k0 > qb) break;
         const int k = k0 + lane;
         const bool valid = k <= qb;
-        const uint32_t x = xs[u];
+        const uint32_t x = pe_p(xs[u], nrm);
         bool sel = valid && ((x > c.vstar) || k == 0 || k == qb || (!split && x == c.vstar));
         if (split) {  // the cut splits a run of equal values: take them in flat order
           const bool eq = valid && x == c.vstar;
@@ -1526,28 +1511,32 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
       pe_items);
-  const dim3 gh((unsigned)((total_max + PE_SLICE - 1) / PE_SLICE), vh);
-  pe_norm_hist_kernel<<<gh, 256, 0, s>>>(b.route, (const float2*)b.pepart, b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv,
-                                         nseg);
+  // slice of the flat passes: PE_SLICE entries, fewer where the grid would not fill the device
+  int slice = PE_SLICE;
+  while (slice > 1024 && ((total_max + slice - 1) / slice) * vh < 2 * device_cu_count()) slice /= 2;
+  const dim3 gh((unsigned)((total_max + slice - 1) / slice), vh);
+  pe_flat_pass_kernel<0><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, b.pe_prob, cut,
+                                            b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
   pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_hist_kernel<1><<<gh, 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, seqs, hq, hkv);
+  pe_flat_pass_kernel<1><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, nullptr, cut,
+                                            b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
   pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
   const int cap = pe_cand_limit(nb_max);
-  pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
+  pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
                                                                   (uint2*)b.cand, cap, seqs, hq, hkv);
   pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
   pe_cand_kernel<<<dim3(8, vh), 256, 0, s>>>(cut, (const uint2*)b.cand, cap, b.eqrow, b.counts);
-  pe_eq_full_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, cut, cap, b.eqrow, b.counts, seqs, hq, hkv);
+  pe_eq_full_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, cap, b.eqrow, b.counts, seqs, hq, hkv);
   pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
   const dim3 gl((nb_max + 3) / 4, vh);
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);
-  list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
-                                               b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
+  list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, (const float2*)b.pnorm, cut,
+                                               b.eqrow, b.counts, b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
   const int ntile = row_tiles((int64_t)hq * nb_max);
   row_tile_sum_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, seqs, hq, hkv, ntile);
   scan_rows_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, b.row_ptr, seqs, hq, hkv, ntile);
-  list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, cut, b.eqrow, b.counts,
-                                              b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
+  list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, (const float2*)b.pnorm, cut,
+                                              b.eqrow, b.counts, b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
   if (b.sv_out || b.nv_out || b.ss_out || b.ns_out)
     copy_sets_kernel<<<vh, 256, 0, s>>>(b.sv, b.nv, b.ss, b.ns, b.sv_out, b.nv_out, b.ss_out, b.ns_out, seqs, hq,
                                         hkv);

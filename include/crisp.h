@@ -175,7 +175,7 @@ int crisp_prefill(const crisp_shape *shape, const void *q, const void *k, const 
  * selection buffers.  It allocates nothing and calls no allocating routine.
  *   - A problem whose workspace (crisp_workspace_bytes) exceeds the scratch is
  *     rejected with CRISP_E_TOO_LARGE before anything is enqueued (128 MiB holds
- *     a bf16 Llama-shaped layer of 32 query / 8 KV heads up to 45,184 tokens).
+ *     a bf16 Llama-shaped layer of 32 query / 8 KV heads up to 44,800 tokens).
  *   - The first call on a device looks up the array's device address on that
  *     device (hipGetSymbolAddress); CRISP_E_HIP if that fails.
  *   - Every call on one GPU uses the same array, so calls that overlap in time
