@@ -885,32 +885,38 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
   constexpr int hi = shift + width;
   const uint32_t prefix = PASS > 0 ? cut[h].prefix : 0u;
   const bool hist = PASS > 0 || active;
-  // neighbouring entries of a softmax row often fall into the same bucket:
+  // Neighbouring entries of a softmax row often fall into the same bucket:
   // each thread merges runs of equal buckets in registers (over its strided
-  // entries) and commits a run with one pair of LDS atomics
+  // entries) and commits a run with one pair of LDS atomics.  All entries of a
+  // bucket share one exponent field e, so a run sums the 24-bit significands
+  // m (shifted right by 104 - e per entry where e < 104) and the commit shifts
+  // the sum left by e - 104 where e >= 104: exactly the sum of the entries'
+  // fx_mass (floor(p 2^46) = m 2^(e - 104); p <= 1, so e <= 127).
   uint32_t run_b = 0xffffffffu, run_c = 0;
-  unsigned long long run_m = 0;
+  unsigned long long run_s = 0;
+  auto commit = [&]() {
+    const int e = PASS == 0 ? (int)(run_b >> 2) : (int)(prefix >> 23);   // the bucket's exponent field
+    atomicAdd(&sc[run_b], run_c);
+    atomicAdd(&sm[run_b], run_s << max(e - 104, 0));
+  };
   auto take = [&](uint32_t x) {
     if (PASS > 0 && (x >> hi) != (prefix >> hi)) return;
     const uint32_t bk = (x >> shift) & mask;
     if (bk != run_b) {
-      if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+      if (run_c) commit();
       run_b = bk;
       run_c = 0;
-      run_m = 0;
+      run_s = 0;
     }
     ++run_c;
-    run_m += fx_mass(x);
+    const int sh = min(max(104 - (int)(x >> 23), 0), 31);
+    run_s += ((x & 0x7FFFFFu) | 0x800000u) >> sh;
   };
   // probability of entry e of row r; r, the start of row r + 1 (rend) and the
-  // row's normaliser are carried from one entry of a thread to the next
-  int r = 0, rend = 0;
-  float2 nrm = make_float2(0.f, 0.f);
-  auto at_row = [&](int e) {   // start tracking at entry e
-    r = tri_row(e);
-    rend = tri32(r + 1);
-    nrm = sN[r - r0];
-  };
+  // row's normaliser are carried forward over a thread's entries, which only
+  // move ahead
+  int r = r0, rend = tri32(r0 + 1);
+  float2 nrm = sN[0];
   auto prob = [&](int e, float x) -> uint32_t {
     if (e >= rend) {
       do { ++r; rend += r + 1; } while (e >= rend);
@@ -933,7 +939,6 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
       for (int u = 0; u < U; ++u) {
         const int e = e0 + 1024 * u;
         if (e >= b) break;
-        at_row(e);
         uint4 y;
         y.x = prob(e, xs[u].x);
         y.y = e + 1 < b ? prob(e + 1, xs[u].y) : 0u;
@@ -966,7 +971,6 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
       for (int u = 0; u < U; ++u) {
         const int e = e0 + 256 * u;
         if (e >= b) break;
-        at_row(e);
         const uint32_t y = prob(e, xs[u]);
         if (Oh) Oh[e] = __uint_as_float(y);
         if (hist) take(y);
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
     }
   }
   if (!hist) return;
-  if (run_c) { atomicAdd(&sc[run_b], run_c); atomicAdd(&sm[run_b], run_m); }
+  if (run_c) commit();
   __syncthreads();
   uint32_t* gc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   unsigned long long* gm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
