@@ -553,10 +553,14 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const T* __restrict__ Q, co
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int r = rg; r < BLK; r += RG) {
-    const T* p = base + (int64_t)r * sq_n;
-    const uint4 raw = *(const uint4*)p;
-    const T* v = (const T*)&raw;
+  // all BLK / RG loads of a thread are in flight before the first is used
+  constexpr int NL = BLK / RG;
+  uint4 raw[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) raw[i] = *(const uint4*)(base + (int64_t)(rg + RG * i) * sq_n);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const T* v = (const T*)&raw[i];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += to_f32(v[e]);
   }
