@@ -112,7 +112,7 @@ SelectLayout select_layout(const crisp_shape* s, const SeqList& seqs) {
     if (nb > nb_max) nb_max = nb;
   }
   const int64_t nch = proxy_chunks(s->dtype == CRISP_FP32, seqs, (int)hq, (int)hkv);
-  const int64_t nseg = pe_segments(nb_max);
+  const int64_t nseg = pe_segments_max(seqs);
   SelectLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };

@@ -18,10 +18,13 @@ hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv
 // nb[i]) of Q, K, V^T and O, and its lists live at row_ptr + rp[i] (hq * nb[i]
 // + 1 entries, offsets relative to col_idx + col[i]).
 constexpr int MAX_SEQ = 64;
-// Pooled-estimation logits are produced in segments of PE_SEG tiles of 32 key
-// blocks (one work-group each); every row keeps one (max, sum) pair per segment.
-constexpr int PE_SEG = 8;
-inline int pe_segments(int nb) { return ((nb + 31) / 32 + PE_SEG - 1) / PE_SEG; }
+// Pooled-estimation logits are produced in segments of pe_seg(N_b) tiles of 32
+// key blocks (one work item each); every row keeps one (max, sum) pair per
+// segment.  Long sequences take longer segments (fewer item start-ups); the
+// size depends on the sequence's own N_b only, so a sequence is cut the same
+// way alone and in a packed batch.
+__host__ __device__ inline int pe_seg(int nb) { return nb >= 4096 ? 16 : 8; }
+__host__ __device__ inline int pe_segments(int nb) { return ((nb + 31) / 32 + pe_seg(nb) - 1) / pe_seg(nb); }
 struct SeqTable {
   int nseq;
   int unit_off[MAX_SEQ + 1];   // work units (query-block pairs x KV heads) before sequence i
@@ -50,6 +53,11 @@ struct SeqPos {
   int64_t rp;      // row pointers of the earlier sequences (hq * N_b + 1 each)
   int64_t kvrows;  // hkv * N_b of the earlier sequences (K-bar rows)
 };
+inline int pe_segments_max(const SeqList& L) {   // row stride of the per-segment partials
+  int m = 1;
+  for (int i = 0; i < L.nseq; ++i) m = pe_segments(L.nb[i]) > m ? pe_segments(L.nb[i]) : m;
+  return m;
+}
 __host__ __device__ inline SeqPos seq_pos(const SeqList& L, int s, int hq, int hkv) {
   SeqPos p{L.nb[s], 0, 0, 0, 0, 0};
   for (int i = 0; i < s; ++i) {

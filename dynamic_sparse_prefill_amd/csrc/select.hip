@@ -601,7 +601,7 @@ __device__ __forceinline__ Split3 split3(float x) {
 }
 
 // Logits: one item per (PE_RB row blocks of 32 query blocks, segment cs of
-// PE_SEG key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
+// pe_seg(N_b) key tiles, Pooled-Estimation head); wave w owns row block rb0 + w.
 // L[qb][kb] = scale * Qbar[qb] . Kbar[kb] for kb <= qb is formed 32 key blocks
 // at a time in the transposed form L^T = Kbar Qbar^T on the bf16 matrix unit
 // (v_mfma_f32_32x32x16_bf16) with both operands split in three bf16 parts
@@ -631,7 +631,8 @@ __device__ __forceinline__ void pe_logits_item(bf16 (&kt)[2][3][32 * KT_PITCH], 
   const int ntile = rb < nrb ? min(nb - 1, rb * 32 + 31) / 32 + 1 : 0;
   const int rb_top = min(nrb - 1, rg * PE_RB + PE_RB - 1);
   const int ntile_top = min(nb - 1, rb_top * 32 + 31) / 32 + 1;
-  const int ct0 = cs * PE_SEG, ct1 = min(ntile_top, ct0 + PE_SEG);
+  const int seg = pe_seg(nb);
+  const int ct0 = cs * seg, ct1 = min(ntile_top, ct0 + seg);
   if (ct0 >= ct1) return;
   qbar += sp.rows * HD;
   kbar += sp.kvrows * HD;
@@ -819,8 +820,8 @@ __device__ __forceinline__ uint32_t pe_p(float x, float2 n) { return __float_as_
 
 // Row normaliser of pooled row qb from its segments' (max, sum of exp(x - max)),
 // in segment order: M = the largest segment max, S = the sums rescaled to M.
-__device__ __forceinline__ float2 pe_row_norm(const float2* __restrict__ pp, int qb) {
-  const int ns = ((qb / 32) + 1 + PE_SEG - 1) / PE_SEG;
+__device__ __forceinline__ float2 pe_row_norm(const float2* __restrict__ pp, int qb, int seg) {
+  const int ns = ((qb / 32) + 1 + seg - 1) / seg;
   float M = -INFINITY;
   for (int c = 0; c < ns; ++c) M = fmaxf(M, pp[c].x);
   float S = 0.f;
@@ -875,7 +876,7 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
     const int qb = r0 + tid;
     float2 nrm;
     if (PASS == 0) {
-      nrm = pe_row_norm(part + (hrow + qb) * nseg, qb);
+      nrm = pe_row_norm(part + (hrow + qb) * nseg, qb, pe_seg(nb));
       if (tri32(qb) >= a) pnorm[hrow + qb] = nrm;   // once: by the slice in which the row starts
     } else {
       nrm = pnorm[hrow + qb];
@@ -1514,7 +1515,7 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   else
     pool_q_kernel<bf16><<<gq, 256, 0, s>>>((const bf16*)Q, b.route, b.qbar, seqs, hq, hkv, st.q_h, st.q_n, b.peq,
                                            cut, b.hcnt, b.hmass, gamma);
-  const int nrb = (nb_max + 31) / 32, nseg = pe_segments(nb_max);
+  const int nrb = (nb_max + 31) / 32, nseg = pe_segments_max(seqs);
   const int pe_items = ((nrb + PE_RB - 1) / PE_RB) * nseg * vh;
   pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
