@@ -931,8 +931,46 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
   };
   constexpr int U = 4;
   if (((uintptr_t)Ph & 15) == 0 && (!Oh || ((uintptr_t)Oh & 15) == 0)) {
-    // 16-byte loads of four consecutive entries, four loads in flight per thread
-    for (int e0 = a + 4 * tid; e0 < b; e0 += 4 * 256 * U) {
+    // 16-byte loads of four consecutive entries.  The slice's whole steps of
+    // 4 * 256 * U entries (a trip count uniform over the work-group, no bounds
+    // tests) keep U loads in flight per thread, the next step's issued before
+    // the current one is used; the rest of the slice takes the tested form.
+    constexpr int STEP = 4 * 256 * U;
+    const int nfull = (b - a) / STEP;
+    int e0 = a + 4 * tid;
+    float4 nx[U];
+    if (nfull > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) nx[u] = *(const float4*)(Ph + e0 + 1024 * u);
+    }
+    for (int it = 0; it < nfull; ++it, e0 += STEP) {
+      // the next step's loads go out before this step's entries are used; on
+      // the last step they re-read this step's entries (unused), so that every
+      // path into the loop has the same loads in flight
+      const int en = it + 1 < nfull ? e0 + STEP : e0;
+      float4 nn[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) nn[u] = *(const float4*)(Ph + en + 1024 * u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + 1024 * u;
+        uint4 y;
+        y.x = prob(e, nx[u].x);
+        y.y = prob(e + 1, nx[u].y);
+        y.z = prob(e + 2, nx[u].z);
+        y.w = prob(e + 3, nx[u].w);
+        if (Oh) *(uint4*)(Oh + e) = y;
+        if (hist) {
+          take(y.x);
+          take(y.y);
+          take(y.z);
+          take(y.w);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) nx[u] = nn[u];
+    }
+    for (; e0 < b; e0 += STEP) {
       float4 xs[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
