@@ -469,12 +469,20 @@ __global__ __launch_bounds__(BLK * CMB_GROUPS) void proxy_combine_kernel(const f
   const int kpc = seq_kpc(nb, chunks1);
   const int nc = (nb + kpc - 1) / kpc;   // the score pass's chunks of this sequence
   const float2* p = stats + (int64_t)h * nchunk * BLK + r;
-  float M = -1e30f;
-  for (int c = grp; c < nc; c += CMB_GROUPS) M = fmaxf(M, p[(int64_t)c * BLK].x);
-  float L = 0.f;
-  for (int c = grp; c < nc; c += CMB_GROUPS) {
-    const float2 v = p[(int64_t)c * BLK];
-    L += v.y * fast_exp2((v.x - M) * sl2);
+  float M = -1e30f, L = 0.f;
+  for (int c0 = grp; c0 < nc; c0 += 4 * CMB_GROUPS) {   // four chunks' loads in flight, then merged in chunk order
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[(int64_t)min(c0 + CMB_GROUPS * u, nc - 1) * BLK];
+    float m4 = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c0 + CMB_GROUPS * u < nc) m4 = fmaxf(m4, v[u].x);
+    L *= fast_exp2((M - m4) * sl2);
+    M = m4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c0 + CMB_GROUPS * u < nc) L += v[u].y * fast_exp2((v[u].x - M) * sl2);
   }
   part[grp][r] = make_float2(M, L);
   __syncthreads();

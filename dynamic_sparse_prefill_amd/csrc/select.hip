@@ -160,16 +160,28 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
   float* PV = pv + rowb;
   float* PS = ps + rowb;
   const float inv_b = 1.f / BLK;  // exact power of two
-  for (int k = tid; k < nb; k += 256) {
-    const float4 t = T[k];
-    const float v = __fmul_rn(__fadd_rn(t.x, t.y), inv_b);
-    const float lo = T[nb - 1 - k].x;
-    const float up = (k <= nb - 2) ? T[nb - 2 - k].y : 0.f;
-    const float sl = __fmul_rn(__fadd_rn(lo, up), inv_b);
-    PV[k] = v;
-    PS[k] = sl;
-    if (pv_out) pv_out[rowb + k] = v;
-    if (ps_out) ps_out[rowb + k] = sl;
+  // four tiles per thread at a time, their loads issued before any is used
+  for (int k0 = tid; k0 < nb; k0 += 4 * 256) {
+    float4 t[4];
+    float lo[4], up[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = min(k0 + 256 * u, nb - 1);   // clamped: every load is issued
+      t[u] = T[k];
+      lo[u] = T[nb - 1 - k].x;
+      up[u] = T[max(nb - 2 - k, 0)].y;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 256 * u;
+      if (k >= nb) break;
+      const float v = __fmul_rn(__fadd_rn(t[u].x, t[u].y), inv_b);
+      const float sl = __fmul_rn(__fadd_rn(lo[u], k <= nb - 2 ? up[u] : 0.f), inv_b);
+      PV[k] = v;
+      PS[k] = sl;
+      if (pv_out) pv_out[rowb + k] = v;
+      if (ps_out) ps_out[rowb + k] = sl;
+    }
   }
   if (tid == 0) {
     // tiles touching [0, w_sink) or [n - w_local, n), ascending: the sink tiles,
@@ -202,7 +214,16 @@ __global__ __launch_bounds__(256) void vs_select_kernel(
     t = fmaxf(t, 0.f);
     const float mu = __fdiv_rn(t, denom);
     const float thr = __fmul_rn(alpha, mu);
-    for (int k = tid; k < nb; k += 256) flag[k] = (p[k] > thr) || k == 0 || k == nb - 1;
+    for (int k0 = tid; k0 < nb; k0 += 4 * 256) {   // loads first, as above
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = p[min(k0 + 256 * u, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + 256 * u;
+        if (k < nb) flag[k] = (x[u] > thr) || k == 0 || k == nb - 1;
+      }
+    }
     __syncthreads();
     if (min_blocks > 0) top_up(flag, p, nb, min(min_blocks, nb), shv, shi);
     compact_flags(flag, nb, (dir == 0 ? sv : ss) + rowb, (dir == 0 ? nv : ns) + h, shi);
