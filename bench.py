@@ -352,16 +352,20 @@ def measured_peaks(torch):
     stream = torch.cuda.current_stream().cuda_stream
     iters = 3_000_000
     flops = ncu * 8 * iters * 4 * 32768
-    rates = []
-    for _ in range(2):                      # the first launch brings the clocks to their loaded state
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        st = L.crisp_probe_mfma_bf16(out.data_ptr(), ncu, iters, stream)
-        e1.record()
-        e1.synchronize()
-        if st != 0:
-            raise RuntimeError(f"crisp_probe_mfma_bf16 failed: {st}")
-        rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    def loop(fn, name):
+        rates = []
+        for _ in range(2):                  # the first launch brings the clocks to their loaded state
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = fn(out.data_ptr(), ncu, iters, stream)
+            e1.record()
+            e1.synchronize()
+            if st != 0:
+                raise RuntimeError(f"{name} failed: {st}")
+            rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        return rates[-1]
+    const_rate = loop(L.crisp_probe_mfma_bf16, "crisp_probe_mfma_bf16")
+    data_rate = loop(L.crisp_probe_mfma_bf16_data, "crisp_probe_mfma_bf16_data")
     a = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
@@ -374,9 +378,12 @@ def measured_peaks(torch):
     e1.synchronize()
     gbs = 5 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
-    return {"mfma_bf16_tflops": round(rates[-1], 1), "copy_gbs": round(gbs, 1),
+    return {"mfma_bf16_tflops": round(const_rate, 1), "mfma_bf16_random_operands_tflops": round(data_rate, 1),
+            "copy_gbs": round(gbs, 1),
             "how": "bf16 MFMA loop, 4 independent 32x32x16 accumulators per wave, 2 waves/SIMD, "
-                   "second of two ~0.4 s launches; HBM: 2 GiB device copy, read + write bytes"}
+                   "second of two ~0.4 s launches, operands constant (mfma_bf16_tflops) or cycling over "
+                   "8 pseudo-random fragment pairs (..._random_operands_tflops); "
+                   "HBM: 2 GiB device copy, read + write bytes"}
 
 
 def run_layer(layer, steps, warmup, torch, dsp, synth, with_dense=True, compare=False, compensate=True):
@@ -591,6 +598,8 @@ def main():
                      "useful_frac": round(main_res["useful_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "useful_flops_per_launch": int(main_res["useful_flops"]),
                      "frac_of_measured": round(ach / peaks["mfma_bf16_tflops"], 4) if peaks else None,
+                     "frac_of_measured_random_operands":
+                         round(ach / peaks["mfma_bf16_random_operands_tflops"], 4) if peaks else None,
                      "traffic": profiled_traffic() if args.workload == "llama3.1-8b-512k" else None,
                      "kernel": "fa_bf16_kernel<false> (sparse attention; event time includes the V re-layout)",
                      "flops_per_launch": main_res["tiles"] * TILE_FLOPS},

@@ -72,6 +72,8 @@ def probe_lib() -> C.CDLL:
         L = C.CDLL(PROBE_LIB_PATH)
         L.crisp_probe_mfma_bf16.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         L.crisp_probe_mfma_bf16.restype = C.c_int
+        L.crisp_probe_mfma_bf16_data.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+        L.crisp_probe_mfma_bf16_data.restype = C.c_int
         _PROBE = L
     return _PROBE
 

@@ -26,6 +26,15 @@ extern "C" {
  */
 int crisp_probe_mfma_bf16(float *out, int blocks, int iters, void *stream);
 
+/*
+ * The same loop, same work per iteration, but each wave's operands cycle over
+ * eight pseudo-random bf16 fragment pairs instead of staying constant, so the
+ * multipliers switch as they do on real tiles.  `iters` must be even
+ * (2 .. 2^26); total work = blocks * 8 * iters * 4 * 32768 flop, as above.
+ * Same returns, same guarantees.
+ */
+int crisp_probe_mfma_bf16_data(float *out, int blocks, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def test_header_and_exports_agree():
 
 def test_probe_header_and_exports_agree():
     names = declared_functions("crisp_probe.h")
-    assert names == ["crisp_probe_mfma_bf16"]
+    assert names == ["crisp_probe_mfma_bf16", "crisp_probe_mfma_bf16_data"]
     L = api.probe_lib()
     for n in names:
         assert hasattr(L, n), n
@@ -37,6 +37,9 @@ def test_probe_header_and_exports_agree():
     assert L.crisp_probe_mfma_bf16(None, 1, 1, None) == -1
     assert L.crisp_probe_mfma_bf16(C.c_void_p(16), 0, 1, None) == -1
     assert L.crisp_probe_mfma_bf16(C.c_void_p(16), 1, 0, None) == -1
+    assert L.crisp_probe_mfma_bf16_data(None, 1, 2, None) == -1
+    assert L.crisp_probe_mfma_bf16_data(C.c_void_p(16), 1, 3, None) == -1   # odd iteration count
+    assert L.crisp_probe_mfma_bf16_data(C.c_void_p(16), 0, 2, None) == -1
 
 
 def _shape(n=4096, hq=4, hkv=2, d=128, dtype=0):
