@@ -38,6 +38,7 @@
 #include "lanes.h"
 #include "launch.h"
 #include "tile.h"
+#include "vt.h"
 
 namespace crisp {
 
@@ -55,38 +56,40 @@ constexpr int NQUEUE = 8;  // work queues of the persistent attention kernel (on
 // one pass over all items, as dense attention always does.
 constexpr int NPHASE = 2;
 constexpr int TWO_PASS_NB = 256;
+static_assert(NQUEUE * NPHASE == ATTN_QUEUE_INTS, "the V re-layout clears ATTN_QUEUE_INTS counters");
 
 // ------------------------------------------------------------------ V re-layout
 
-// Position of key e (0..127) inside a re-laid-out V^T row (bf16 only).  Within
-// each group of 16 keys, positions 8g..8g+7 hold keys {4g..4g+3, 8+4g..8+4g+3}:
-// exactly the eight keys that lane half g contributes to one 32x32x16 MFMA of
-// O^T += V^T P^T, so each A operand is a single 16-byte LDS read.
-__host__ __device__ __forceinline__ int vt_pos(int e) {
-  const int grp = e >> 4, k = e & 15, h = k >> 3, g = (k >> 2) & 1, j = k & 3;
-  return 16 * grp + 8 * g + 4 * h + j;
-}
-
-// V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128]; bf16 rows use vt_pos order.
-// Also clears the attention kernels' work-queue counters (they run right after).
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, T* __restrict__ Vt,
-                                                          int nb, int64_t sv_h, int64_t sv_n, int* queue) {
-  __shared__ T tile[BLK][HD + 2];
+// V [hkv][n][d] (token stride sv_n) -> Vt [hkv][nb][d][128] (the layout of
+// vt.h).  Also clears the attention kernels' work-queue counters (they run
+// right after).  fp32: one tile per work-group through LDS; bf16: two tiles per
+// 512-thread work-group in registers (vt_tile_bf16).
+__global__ __launch_bounds__(256) void transpose_v_f32_kernel(const float* __restrict__ V, float* __restrict__ Vt,
+                                                              int nb, int64_t sv_h, int64_t sv_n, int* queue) {
+  __shared__ float tile[BLK][HD + 2];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  if (kb == 0 && g == 0 && tid < NQUEUE * NPHASE && queue) queue[tid] = 0;
-  const T* src = V + (int64_t)g * sv_h + (int64_t)kb * BLK * sv_n;
+  if (kb == 0 && g == 0 && tid < ATTN_QUEUE_INTS && queue) queue[tid] = 0;
+  const float* src = V + (int64_t)g * sv_h + (int64_t)kb * BLK * sv_n;
   for (int e = tid; e < BLK * HD; e += 256) {
     const int r = e / HD, d = e % HD;
     tile[r][d] = src[(int64_t)r * sv_n + d];
   }
   __syncthreads();
-  T* dst = Vt + ((int64_t)g * nb + kb) * (BLK * HD);
+  float* dst = Vt + ((int64_t)g * nb + kb) * (BLK * HD);
   for (int e = tid; e < BLK * HD; e += 256) {
     const int d = e / BLK, r = e % BLK;
-    const int pos = sizeof(T) == 2 ? vt_pos(r) : r;
-    dst[d * BLK + pos] = tile[r][d];
+    dst[d * BLK + r] = tile[r][d];
   }
+}
+
+__global__ __launch_bounds__(512) void transpose_v_bf16_kernel(const bf16* __restrict__ V, bf16* __restrict__ Vt,
+                                                               int nb, int hkv, int64_t sv_h, int64_t sv_n,
+                                                               int* queue) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid < ATTN_QUEUE_INTS && queue) queue[tid] = 0;
+  const int64_t tile = 2 * (int64_t)blockIdx.x + (tid >> 8);   // tile = g * nb + kb
+  if (tile >= (int64_t)hkv * nb) return;
+  vt_tile_bf16(V, Vt, sv_h, sv_n, nb, (int)(tile % nb), (int)(tile / nb), tid & 255);
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -603,11 +606,13 @@ __global__ __launch_bounds__(256, 1) void fa_f32_kernel(
 
 hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv, int64_t sv_h, int64_t sv_n,
                               int* queue, hipStream_t s) {
-  dim3 grid(nb, hkv);
-  if (fp32)
-    transpose_v_kernel<float><<<grid, 256, 0, s>>>((const float*)V, (float*)Vt, nb, sv_h, sv_n, queue);
-  else
-    transpose_v_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)V, (bf16*)Vt, nb, sv_h, sv_n, queue);
+  if (fp32) {
+    transpose_v_f32_kernel<<<dim3(nb, hkv), 256, 0, s>>>((const float*)V, (float*)Vt, nb, sv_h, sv_n, queue);
+  } else {
+    const int64_t tiles = (int64_t)nb * hkv;
+    transpose_v_bf16_kernel<<<(unsigned)((tiles + 1) / 2), 512, 0, s>>>((const bf16*)V, (bf16*)Vt, nb, hkv, sv_h,
+                                                                          sv_n, queue);
+  }
   return hipGetLastError();
 }
 

@@ -190,7 +190,7 @@ int validate_attn(const crisp_shape* s, const void* q, const void* k, const void
 
 // Selection of every sequence in `seqs` (one prefill: one sequence), all at once.
 int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
-               void* ws, hipStream_t stream, const SeqList& seqs) {
+               void* ws, hipStream_t stream, const SeqList& seqs, const VtJob& vt = VtJob{}) {
   const SelectLayout L = select_layout(s, seqs);
   char* w = (char*)ws;
   int nb_max = 0;
@@ -198,7 +198,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   const int fp32 = s->dtype == CRISP_FP32;
   const Strides st = strides(s);
   hipError_t e = launch_proxy(fp32, q, k, seqs, nb_max, s->hq, s->hkv, st, p->sink, p->local, p->dense_below_n,
-                              w + L.tstat, w + L.stats, w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), stream);
+                              w + L.tstat, w + L.stats, w + L.rowstat, w + L.tiles, (float*)(w + L.kbar), vt, stream);
   if (e != hipSuccess) return CRISP_E_HIP;
   SelectBufs b;
   b.tiles = w + L.tiles;
@@ -240,8 +240,23 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
                                  p->gamma, p->min_blocks, p->dense_below_n, b, stream));
 }
 int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
-               void* ws, hipStream_t stream) {
-  return run_select(s, q, k, p, out, ws, stream, one_sequence(s));
+               void* ws, hipStream_t stream, const VtJob& vt = VtJob{}) {
+  return run_select(s, q, k, p, out, ws, stream, one_sequence(s), vt);
+}
+
+// The V re-layout of a bf16 prefill, done by the proxy launch (the fp32 path
+// keeps its own re-layout launch): V^T at the start of the attention
+// workspace, the attention's work counters right after it.
+VtJob prefill_vt_job(const crisp_shape* s, const void* v, void* attn_ws) {
+  VtJob j;
+  if (s->dtype != CRISP_BF16) return j;
+  j.V = v;
+  j.Vt = attn_ws;
+  j.sv_h = s->sv_h;
+  j.sv_n = s->sv_n;
+  j.nb = (int)(s->n / BLK);
+  j.queue = (int*)((char*)attn_ws + vt_bytes(s));
+  return j;
 }
 
 SeqTable single_sequence(int nb, int hkv) {
@@ -257,13 +272,18 @@ SeqTable single_sequence(int nb, int hkv) {
   return t;
 }
 
+// vt_ready: the proxy launch of the same prefill has already re-laid out V
+// (prefill_vt_job) and cleared the work counters.
 int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
-             const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream, const SeqTable* seqs = nullptr) {
+             const int32_t* col_idx, bool dense, void* o, void* ws, hipStream_t stream, const SeqTable* seqs = nullptr,
+             bool vt_ready = false) {
   const int nb = (int)(s->n / BLK);
   const int fp32 = s->dtype == CRISP_FP32;
   int* queue = (int*)((char*)ws + vt_bytes(s));
-  hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, queue, stream);
-  if (e != hipSuccess) return CRISP_E_HIP;
+  if (!vt_ready) {
+    const hipError_t e = launch_transpose_v(fp32, v, ws, nb, s->hkv, s->sv_h, s->sv_n, queue, stream);
+    if (e != hipSuccess) return CRISP_E_HIP;
+  }
   const SeqTable one = single_sequence(nb, s->hkv);
   return status_of(launch_attention(fp32, dense, q, k, ws, o, row_ptr, col_idx, queue, seqs ? *seqs : one, nb,
                                     s->hq, s->hkv, strides(s), stream));
@@ -399,9 +419,10 @@ int crisp_prefill(const crisp_shape* shape, const void* q, const void* k, const 
   char* attn_ws_ptr = (char*)workspace + sel_bytes;
   st = validate_attn(shape, q, k, v, o, attn_ws_ptr, workspace_bytes - sel_bytes);
   if (st) return st;
-  st = run_select(shape, q, k, params, sel, workspace, stream);
+  const VtJob vt = prefill_vt_job(shape, v, attn_ws_ptr);
+  st = run_select(shape, q, k, params, sel, workspace, stream, vt);
   if (st) return st;
-  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream);
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream, nullptr, vt.V != nullptr);
 }
 
 size_t crisp_noalloc_scratch_bytes(void) { return CRISP_NOALLOC_SCRATCH_BYTES; }
@@ -420,9 +441,11 @@ int crisp_prefill_noalloc(const crisp_shape* shape, const void* q, const void* k
   if (sel->col_capacity < crisp_col_capacity(shape)) return CRISP_E_WORKSPACE;
   void* ws = nullptr;
   if ((st = scratch_address(&ws))) return st;
-  st = run_select(shape, q, k, params, sel, ws, stream);
+  const VtJob vt = prefill_vt_job(shape, v, (char*)ws + sel_bytes);
+  st = run_select(shape, q, k, params, sel, ws, stream, vt);
   if (st) return st;
-  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)ws + sel_bytes, stream);
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)ws + sel_bytes, stream, nullptr,
+                  vt.V != nullptr);
 }
 
 int64_t crisp_varlen_col_capacity(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens) {
@@ -452,7 +475,8 @@ int crisp_prefill_varlen(const crisp_shape* shape, int32_t nseq, const int64_t* 
   const size_t sel_bytes = align256(P.sel_ws);
   if (workspace_bytes < sel_bytes + attn_ws(shape)) return CRISP_E_WORKSPACE;
   // selection of every sequence at once (virtual heads = sequence x query head)
-  st = run_select(shape, q, k, params, sel, workspace, stream, P.seqs);
+  const VtJob vt = prefill_vt_job(shape, v, (char*)workspace + sel_bytes);
+  st = run_select(shape, q, k, params, sel, workspace, stream, P.seqs, vt);
   if (st) return st;
   SeqTable seqs;
   seqs.nseq = nseq;
@@ -467,7 +491,7 @@ int crisp_prefill_varlen(const crisp_shape* shape, int32_t nseq, const int64_t* 
     seqs.unit_off[i + 1] = seqs.unit_off[i] + (int)((nb + 1) / 2) * shape->hkv;
   }
   return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)workspace + sel_bytes, stream,
-                  &seqs);
+                  &seqs, vt.V != nullptr);
 }
 
 const char* crisp_status_string(int status) {

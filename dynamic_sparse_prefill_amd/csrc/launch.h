@@ -12,6 +12,18 @@ struct Strides { int64_t q_h, q_n, k_h, k_n, v_h, v_n, o_h, o_n; };
 // V [hkv][n][d] -> per-block transposed V^T; also zeroes *queue (may be NULL)
 hipError_t launch_transpose_v(int fp32, const void* V, void* Vt, int nb, int hkv,
                               int64_t sv_h, int64_t sv_n, int* queue, hipStream_t s);
+constexpr int ATTN_QUEUE_INTS = 16;   // work counters of the persistent attention kernel
+
+// The bf16 V re-layout of a prefill, handed to the proxy launch so that it runs
+// in the same grid as the proxy scores (extra work-groups) instead of as a
+// launch of its own between selection and attention.  V == nullptr: none.
+struct VtJob {
+  const void* V = nullptr;
+  void* Vt = nullptr;
+  int64_t sv_h = 0, sv_n = 0;
+  int nb = 0;                 // blocks of the whole packed V (V^T head stride)
+  int* queue = nullptr;       // ATTN_QUEUE_INTS counters, zeroed with the re-layout
+};
 
 // Sequences of a packed batch (a single prefill is one sequence).  Passed by
 // value to the attention kernel.  Sequence i owns tokens [tok[i], tok[i] + 128
@@ -75,7 +87,7 @@ __host__ __device__ inline bool seq_dense(int nb, int dense_below_n) {
   return nb <= 2 || (dense_below_n > 0 && (int64_t)nb * 128 < dense_below_n);
 }
 
-// queue: the persistent kernel's work counter, zero at launch (set by launch_transpose_v).
+// queue: the persistent kernel's work counters, zero at launch (set by the V re-layout).
 // nb_total: blocks of the whole packed V^T (its head stride).
 hipError_t launch_attention(int fp32, bool dense, const void* Q, const void* K, const void* Vt, void* O,
                             const int32_t* row_ptr, const int32_t* col_idx, int* queue, const SeqTable& seqs,
@@ -89,7 +101,7 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
                         const Strides& st, int w_sink, int w_local, int dense_below_n,
                         void* tstat /*[rows*128] float4*/, void* stats /*[nseq*hq*nchunk*128] float2*/,
                         void* rowstat /*[nseq*hq*128] float2*/, void* tiles /*[rows] float4*/,
-                        float* kbar /*[kvrows*128]*/, hipStream_t s);
+                        float* kbar /*[kvrows*128]*/, const VtJob& vt, hipStream_t s);
 
 // compute units of the current device (cached per device)
 int device_cu_count();

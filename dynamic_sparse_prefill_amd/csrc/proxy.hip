@@ -28,6 +28,7 @@
 #include "lanes.h"
 #include "launch.h"
 #include "tile.h"
+#include "vt.h"
 
 namespace crisp {
 
@@ -149,7 +150,18 @@ struct PxCopy {   // the offsets are formed at each issue: a few ALU ops per til
 __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void proxy_scores_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, float4* __restrict__ tstat, float* __restrict__ kbar,
     float2* __restrict__ stats, const SeqList seqs, int hq, int hkv, int64_t sq_h, int64_t sq_n, int64_t sk_h,
-    int64_t sk_n, int w_sink, int w_local, int dense_below_n, float sl2, int chunks1, int nchunk) {
+    int64_t sk_n, int w_sink, int w_local, int dense_below_n, float sl2, int chunks1, int nchunk, int nscore,
+    VtJob vt) {
+  if ((int)blockIdx.x >= nscore) {   // the V re-layout of a prefill: two tiles per work-group
+    if (blockIdx.y != 0) return;
+    const int tid = threadIdx.x;
+    const int64_t tile = 2 * (int64_t)(blockIdx.x - nscore) + (tid >> 8);   // tile = g * nb + kb
+    if (blockIdx.x == nscore && tid < ATTN_QUEUE_INTS) vt.queue[tid] = 0;
+    if (tile < (int64_t)hkv * vt.nb)
+      vt_tile_bf16((const bf16*)vt.V, (bf16*)vt.Vt, vt.sv_h, vt.sv_n, vt.nb, (int)(tile % vt.nb), (int)(tile / vt.nb),
+                   tid & 255);
+    return;
+  }
   __shared__ __attribute__((aligned(1024))) char sK0[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char sK1[BLK * 256];
   __shared__ __attribute__((aligned(16))) float red[2][PX_WAVES][HD];   // K-bar partials per (tile parity, wave)
@@ -526,7 +538,7 @@ __global__ __launch_bounds__(256) void proxy_tilesum_kernel(const float4* __rest
 
 hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& seqs, int nb_max, int hq, int hkv,
                         const Strides& st, int w_sink, int w_local, int dense_below_n, void* tstat, void* stats,
-                        void* rowstat, void* tiles, float* kbar, hipStream_t s) {
+                        void* rowstat, void* tiles, float* kbar, const VtJob& vt, hipStream_t s) {
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int nseq = seqs.nseq;
   const int G = hq / hkv;
@@ -534,16 +546,20 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const int groups = hkv * ((G + hpw - 1) / hpw);
   const int chunks1 = proxy_chunks1(fp32, hq, hkv);
   const int nchunk = proxy_chunks(fp32, seqs, hq, hkv);
-  const dim3 grid((unsigned)(nchunk * groups), (unsigned)nseq);
+  const int nscore = nchunk * groups;
+  const dim3 grid((unsigned)nscore, (unsigned)nseq);
   if (fp32) {
     proxy_tiles_f32_kernel<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar,
                                                  (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink,
                                                  w_local, dense_below_n, sl2, chunks1, nchunk);
   } else {
-    proxy_scores_bf16_kernel<<<grid, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
-                                                            (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
-                                                            st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
-                                                            nchunk);
+    static_assert(PX_WAVES * 64 == 512, "the fused V re-layout takes two 256-thread tiles per work-group");
+    const int64_t vt_tiles = vt.V ? (int64_t)vt.nb * hkv : 0;
+    const dim3 g2((unsigned)(nscore + (vt_tiles + 1) / 2), (unsigned)nseq);
+    proxy_scores_bf16_kernel<<<g2, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
+                                                          (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
+                                                          st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
+                                                          nchunk, nscore, vt);
   }
   const unsigned vheads = (unsigned)(nseq * hq);
   proxy_combine_kernel<<<vheads, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, seqs, hq, nchunk,

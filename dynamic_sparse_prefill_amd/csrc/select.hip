@@ -1051,9 +1051,19 @@ __global__ __launch_bounds__(256) void pe_flat_pass_kernel(const int32_t* __rest
 }
 
 // One wave per head: lane L owns the buckets nbk-1-32L down to nbk-32-32L (from
-// the top); the lane sums are scanned across the wave and the lane in which the
-// running mass first reaches `need` walks its own buckets.  Integer sums, so
-// the result equals a sequential walk from the top bucket.
+// the top); the lane sums are scanned across the wave, and the buckets of the
+// lane in which the running mass first reaches `need` are scanned across the
+// wave in turn (one bucket per lane), so no lane walks a chain of dependent
+// loads.  Integer sums, so the result equals a sequential walk from the top
+// bucket.
+__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 template <int PASS>
 __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
                                                      const unsigned long long* __restrict__ hmass, float gamma) {
@@ -1065,14 +1075,16 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
   const unsigned long long* hm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   constexpr int nbk = 1 << width;
   constexpr int per = nbk / 64;
-  const int top = nbk - 1 - per * lane;
+  static_assert(per % 2 == 0 && per <= 64, "a lane's buckets are read in pairs and scanned one per lane");
+  // the lane's buckets are contiguous (top - per + 1 .. top), 16-byte aligned
+  const ulonglong2* mb = (const ulonglong2*)(hm + nbk - per * (lane + 1));
   unsigned long long mine = 0;
-  for (int i = 0; i < per; ++i) mine += hm[top - i];
-  unsigned long long incl = mine;
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+#pragma unroll
+  for (int i = 0; i < per / 2; ++i) {
+    const ulonglong2 v = mb[i];
+    mine += v.x + v.y;
   }
+  const unsigned long long incl = wave_incl_scan(mine, lane);
   if (PASS == 0) {
     const unsigned long long t = __shfl(incl, 63, 64);
     c.total = t;
@@ -1083,14 +1095,23 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
   // first lane whose inclusive mass reaches need (the last lane if none does)
   const unsigned long long hit = __ballot(incl >= c.need);
   const int L = hit ? __builtin_ctzll(hit) : 63;
-  if (lane != L) return;
-  unsigned long long acc = incl - mine;
-  int sel = top - per + 1;
-  for (int i = top; i > top - per; --i) {
-    if (acc + hm[i] >= c.need) { sel = i; break; }
-    acc += hm[i];
-    sel = i;
+  const unsigned long long before = __shfl(incl - mine, L, 64);   // mass above the buckets of lane L
+  // lane j < per takes L's j-th bucket from the top
+  const int topL = nbk - 1 - per * L;
+  const unsigned long long v = lane < per ? hm[topL - lane] : 0ull;
+  const unsigned long long run = wave_incl_scan(v, lane);
+  const unsigned long long hit2 = __ballot(lane < per && before + run >= c.need);
+  unsigned long long acc;
+  int sel;
+  if (hit2) {
+    const int j = __builtin_ctzll(hit2);
+    sel = topL - j;
+    acc = before + __shfl(run - v, j, 64);        // mass above bucket sel
+  } else {
+    sel = topL - per + 1;                          // none reaches: the lowest bucket, all of L's mass above
+    acc = before + __shfl(run, per - 1, 64);
   }
+  if (lane != 0) return;
   c.need -= acc;
   c.above_mass += acc;
   c.prefix |= (uint32_t)sel << shift;
