@@ -1622,7 +1622,8 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, (const float2*)b.pnorm, cut,
                                                b.eqrow, b.counts, b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
   const int ntile = row_tiles((int64_t)hq * nb_max);
-  row_tile_sum_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, seqs, hq, hkv, ntile);
+  if (ntile > 1)   // one tile: its scan adds no earlier tile sums
+    row_tile_sum_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, seqs, hq, hkv, ntile);
   scan_rows_kernel<<<dim3(ntile, seqs.nseq), 1024, 0, s>>>(b.counts, b.rtsum, b.row_ptr, seqs, hq, hkv, ntile);
   list_kernel<true><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, (const float2*)b.pnorm, cut,
                                               b.eqrow, b.counts, b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max, pe_all);
