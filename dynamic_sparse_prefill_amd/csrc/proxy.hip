@@ -153,10 +153,11 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     int64_t sk_n, int w_sink, int w_local, int dense_below_n, float sl2, int chunks1, int nchunk, int nscore,
     VtJob vt) {
   if ((int)blockIdx.x >= nscore) {   // the V re-layout of a prefill: two tiles per work-group
-    if (blockIdx.y != 0) return;
     const int tid = threadIdx.x;
-    const int64_t tile = 2 * (int64_t)(blockIdx.x - nscore) + (tid >> 8);   // tile = g * nb + kb
-    if (blockIdx.x == nscore && tid < ATTN_QUEUE_INTS) vt.queue[tid] = 0;
+    // the re-layout work-groups of every grid row (sequence), numbered row after row
+    const int64_t wg = (int64_t)blockIdx.y * (gridDim.x - nscore) + (blockIdx.x - nscore);
+    const int64_t tile = 2 * wg + (tid >> 8);   // tile = g * nb + kb
+    if (wg == 0 && tid < ATTN_QUEUE_INTS) vt.queue[tid] = 0;
     if (tile < (int64_t)hkv * vt.nb)
       vt_tile_bf16((const bf16*)vt.V, (bf16*)vt.Vt, vt.sv_h, vt.sv_n, vt.nb, (int)(tile % vt.nb), (int)(tile / vt.nb),
                    tid & 255);
@@ -554,8 +555,9 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
                                                  w_local, dense_below_n, sl2, chunks1, nchunk);
   } else {
     static_assert(PX_WAVES * 64 == 512, "the fused V re-layout takes two 256-thread tiles per work-group");
-    const int64_t vt_tiles = vt.V ? (int64_t)vt.nb * hkv : 0;
-    const dim3 g2((unsigned)(nscore + (vt_tiles + 1) / 2), (unsigned)nseq);
+    // the V re-layout's work-groups (two tiles each) spread over the grid's rows
+    const int64_t vt_wgs = vt.V ? ((int64_t)vt.nb * hkv + 1) / 2 : 0;
+    const dim3 g2((unsigned)(nscore + (vt_wgs + nseq - 1) / nseq), (unsigned)nseq);
     proxy_scores_bf16_kernel<<<g2, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
                                                           (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
                                                           st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
