@@ -1212,35 +1212,29 @@ __global__ __launch_bounds__(256) void pe_last_pass_kernel(const float* __restri
   }
 }
 
-// After the last scan (cut value vstar): each candidate above vstar adds one
-// to its row's count, each equal to it one to the row's eqrow.  Heads whose
-// candidates overflowed the buffer are left to pe_eq_full_kernel.
-__global__ __launch_bounds__(256) void pe_cand_kernel(const PeCut* __restrict__ cut, const uint2* __restrict__ cand,
-                                                      int cap, int32_t* __restrict__ eqrow,
-                                                      int32_t* __restrict__ counts) {
-  const int h = blockIdx.y;
-  const PeCut c = cut[h];
-  if (!c.active || c.ncand > cap) return;
-  const uint2* ch = cand + (int64_t)h * cap;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < c.ncand; i += gridDim.x * 256) {
-    const uint2 e = ch[i];
-    if (e.y > c.vstar) atomicAdd(&counts[e.x], 1);
-    else if (e.y == c.vstar) atomicAdd(&eqrow[e.x], 1);
-  }
-}
-
-// The same per-row counts from a full read of every row, for a head whose
-// candidates did not fit (many entries sharing the cut's top 22 bits): count
-// of entries above vstar to counts, equal to it to eqrow.  Work-groups stride
-// over the rows; every other head returns at once.
-__global__ __launch_bounds__(256) void pe_eq_full_kernel(const float* __restrict__ P,
-                                                         const float2* __restrict__ pnorm, const PeCut* __restrict__ cut,
-                                                         int cap, int32_t* __restrict__ eqrow,
-                                                         int32_t* __restrict__ counts, const SeqList seqs, int hq,
-                                                         int hkv) {
+// After the last scan (cut value vstar), per active Pooled-Estimation head:
+// each candidate above vstar adds one to its row's count, each equal to it one
+// to the row's eqrow.  A head whose candidates overflowed the buffer (many
+// entries sharing the cut's top 22 bits) takes the same per-row counts from a
+// full read of every row instead: the count of entries above vstar to counts,
+// equal to it to eqrow.  Work-groups stride over the candidates or the rows.
+__global__ __launch_bounds__(256) void pe_count_kernel(const float* __restrict__ P, const float2* __restrict__ pnorm,
+                                                       const PeCut* __restrict__ cut, const uint2* __restrict__ cand,
+                                                       int cap, int32_t* __restrict__ eqrow,
+                                                       int32_t* __restrict__ counts, const SeqList seqs, int hq,
+                                                       int hkv) {
   const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;   // h: virtual head
   const PeCut c = cut[h];
-  if (!c.active || c.ncand <= cap) return;
+  if (!c.active) return;
+  if (c.ncand <= cap) {
+    const uint2* ch = cand + (int64_t)h * cap;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < c.ncand; i += gridDim.x * 256) {
+      const uint2 e = ch[i];
+      if (e.y > c.vstar) atomicAdd(&counts[e.x], 1);
+      else if (e.y == c.vstar) atomicAdd(&eqrow[e.x], 1);
+    }
+    return;
+  }
   const SeqPos sp = seq_pos(seqs, h / hq, hq, hkv);
   const int nb = sp.nb;
   for (int qb = blockIdx.x * 4 + w; qb < nb; qb += gridDim.x * 4) {
@@ -1294,7 +1288,8 @@ __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict
 // ------------------------------------------------------------------ lists
 
 // One wave per (head, query block).  FILL = false writes the row's count
-// (Pooled-Estimation rows: completes what pe_eq_count wrote, without reading
+// (Pooled-Estimation rows: completes the counts of entries above and at the
+// cut that the last radix pass and pe_count_kernel wrote, without reading
 // the matrix), FILL = true writes its ascending key blocks at row_ptr[row].
 template <bool FILL>
 __global__ __launch_bounds__(256) void list_kernel(const int32_t* __restrict__ route,
@@ -1614,8 +1609,8 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
                                                                   (uint2*)b.cand, cap, seqs, hq, hkv);
   pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_cand_kernel<<<dim3(8, vh), 256, 0, s>>>(cut, (const uint2*)b.cand, cap, b.eqrow, b.counts);
-  pe_eq_full_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, cap, b.eqrow, b.counts, seqs, hq, hkv);
+  pe_count_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, (const uint2*)b.cand, cap, b.eqrow,
+                                               b.counts, seqs, hq, hkv);
   pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
   const dim3 gl((nb_max + 3) / 4, vh);
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);
