@@ -237,10 +237,16 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     }
   };
 
+  float4 pend = make_float4(0.f, 0.f, 0.f, 0.f);   // the last tile's row statistics, not yet stored
+  int pend_kb = -1;
   auto tile = [&](int kb, const char* cur, char* nxt, int par) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(PX_WAIT_VM0);   // this wave's share of tile kb has landed
     px_barrier();                              // all of it has; every wave left the other stage
     if (kb + 1 < kb1) kc.issue(Kh + (int64_t)(kb + 1) * BLK * sk_n, kspan, nxt);
+    // the previous tile's row statistics are stored only now, after this
+    // tile's copy is issued: the wait at the start of the next tile (which
+    // counts stores too) then finds the store long completed
+    if (pend_kb >= 0 && g == 0) ts[(int64_t)pend_kb * BLK + qrow] = pend;
     if (kbar_wg) {
       if (kb > kb0) kbar_final(kb - 1, par ^ 1);   // the last tile's partials were written before the barrier
       kbar_partials(cur, par);
@@ -347,7 +353,8 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     lo = pair_sum(lo);
     up = pair_sum(up);
     an = pair_sum(an);
-    if (g == 0) ts[(int64_t)kb * BLK + qrow] = make_float4(m, lo, up, an);
+    pend = make_float4(m, lo, up, an);
+    pend_kb = kb;
     merge_row(rM, rL, m, lo + up, sl2);
   };
 
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     tile(kb, sK0, sK1, 0);
     if (kb + 1 < kb1) tile(kb + 1, sK1, sK0, 1);
   }
+  if (pend_kb >= 0 && g == 0) ts[(int64_t)pend_kb * BLK + qrow] = pend;
   if (scores && g == 0)
     stats[(((int64_t)blockIdx.y * hq + h0 + hg) * nchunk + chunk) * BLK + qrow] = make_float2(rM, rL);
   if (kbar_wg) {
