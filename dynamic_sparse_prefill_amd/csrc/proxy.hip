@@ -19,9 +19,12 @@
 // rescales the stored sums by exp(m - M) / L and adds them over the rows.
 // Every reduction has a fixed order (no float atomics), so the scores are
 // bit-reproducible.  The score pass also writes the block means of K (K-bar)
-// used by Pooled Estimation.  Grid: blockIdx -> (key chunk, group of query
-// heads of a KV group, KV head) so the work-groups sharing a K chunk run on
-// one XCD and share its L2; the heads of a group share each K tile in LDS.
+// used by Pooled Estimation, and in a bf16 prefill extra work-groups of the
+// same launch re-lay V out for the attention that follows (vt.h), beside the
+// selection instead of in a launch of their own.  Grid: blockIdx -> (key
+// chunk, group of query heads of a KV group, KV head) so the work-groups
+// sharing a K chunk run on one XCD and share its L2; the heads of a group
+// share each K tile in LDS.
 #include <algorithm>
 
 #include "common.h"
