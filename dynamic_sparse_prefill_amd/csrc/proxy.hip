@@ -199,10 +199,14 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   uint32_t kx[8];   // S^T A operand: key row 32t + l32, d chunk 2c + g (t adds 8192 bytes)
 #pragma unroll
   for (int c = 0; c < 8; ++c) kx[c] = l32 * 256 + (((2 * c + g) ^ (l32 & 15)) << 4);
-  // K-bar partials: lane L of wave w sums rows PX_ROWS w + 4i + L/16 of columns 8(L%16) .. +7
-  const int kb_r0 = PX_ROWS * w + (lane >> 4), kb_c = lane & 15;
+  // K-bar partials, taken by the second head's four waves only (each for two
+  // row groups vw = 2 wq, 2 wq + 1), so that the first head's waves sharing
+  // their SIMDs start on the scores while they sum: lane L of row group vw sums
+  // rows PX_ROWS vw + 4i + L/16 of columns 8(L%16) .. +7
+  const int kb_c = lane & 15;
   const bf16x2 px_ones = {(bf16)1.f, (bf16)1.f};
-  auto kbar_partials = [&](const char* cur, int par) __attribute__((always_inline)) {
+  auto kbar_partials = [&](const char* cur, int par, int vw) __attribute__((always_inline)) {
+    const int kb_r0 = PX_ROWS * vw + (lane >> 4);
     float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // rows r and r + 4 at a time: the same column of both side by side
     // (v_perm), then both added with one v_dot2 against (1, 1), two
@@ -227,8 +231,8 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
       cs[j] += __shfl_xor(cs[j], 32, 64);
     }
     if (lane < 16) {
-      *(f32x4*)&red[par][w][8 * lane] = f32x4{cs[0], cs[1], cs[2], cs[3]};
-      *(f32x4*)&red[par][w][8 * lane + 4] = f32x4{cs[4], cs[5], cs[6], cs[7]};
+      *(f32x4*)&red[par][vw][8 * lane] = f32x4{cs[0], cs[1], cs[2], cs[3]};
+      *(f32x4*)&red[par][vw][8 * lane + 4] = f32x4{cs[4], cs[5], cs[6], cs[7]};
     }
   };
   auto kbar_final = [&](int kb, int par) __attribute__((always_inline)) {
@@ -252,7 +256,10 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     if (pend_kb >= 0 && g == 0) ts[(int64_t)pend_kb * BLK + qrow] = pend;
     if (kbar_wg) {
       if (kb > kb0) kbar_final(kb - 1, par ^ 1);   // the last tile's partials were written before the barrier
-      kbar_partials(cur, par);
+      if (hg == 1) {
+        kbar_partials(cur, par, 2 * wq);
+        kbar_partials(cur, par, 2 * wq + 1);
+      }
     }
     if (!scores) return;
     const bool last = kb == nb - 1;
