@@ -168,7 +168,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   }
   __shared__ __attribute__((aligned(1024))) char sK0[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char sK1[BLK * 256];
-  __shared__ __attribute__((aligned(16))) float red[2][PX_WAVES][HD];   // K-bar partials per (tile parity, wave)
+  __shared__ __attribute__((aligned(16))) float red[2][PX_WAVES][HD];   // K-bar partials per (tile parity, 16-row group)
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = w >> 2, wq = w & 3;   // head of the group, row group (wave-uniform)
