@@ -1064,15 +1064,12 @@ __device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long 
   return v;
 }
 
+// The bucket walk of one radix pass, by one whole wave on histograms hc / hm
+// (global or LDS): updates the cut state c identically on every lane.
 template <int PASS>
-__global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
-                                                     const unsigned long long* __restrict__ hmass, float gamma) {
-  const int h = blockIdx.x, lane = threadIdx.x;
-  PeCut c = cut[h];
-  if (!c.active) return;
+__device__ __forceinline__ void pe_scan_wave(PeCut& c, const uint32_t* hc, const unsigned long long* hm, float gamma,
+                                             int lane) {
   constexpr int shift = pe_shift(PASS), width = pe_width(PASS);
-  const uint32_t* hc = hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
-  const unsigned long long* hm = hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS;
   constexpr int nbk = 1 << width;
   constexpr int per = nbk / 64;
   static_assert(per % 2 == 0 && per <= 64, "a lane's buckets are read in pairs and scanned one per lane");
@@ -1111,7 +1108,6 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
     sel = topL - per + 1;                          // none reaches: the lowest bucket, all of L's mass above
     acc = before + __shfl(run, per - 1, 64);
   }
-  if (lane != 0) return;
   c.need -= acc;
   c.above_mass += acc;
   c.prefix |= (uint32_t)sel << shift;
@@ -1122,7 +1118,17 @@ __global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, co
     unsigned long long take = fv ? (c.need + fv - 1) / fv : c.eq_cnt;
     c.take = take < c.eq_cnt ? take : c.eq_cnt;
   }
-  cut[h] = c;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(64) void pe_scan_kernel(PeCut* __restrict__ cut, const uint32_t* __restrict__ hcnt,
+                                                     const unsigned long long* __restrict__ hmass, float gamma) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  PeCut c = cut[h];
+  if (!c.active) return;
+  pe_scan_wave<PASS>(c, hcnt + ((int64_t)h * 3 + PASS) * PE_BUCKETS, hmass + ((int64_t)h * 3 + PASS) * PE_BUCKETS,
+                     gamma, lane);
+  if (lane == 0) cut[h] = c;
 }
 
 __device__ __forceinline__ int lane_prefix(unsigned long long m) {
@@ -1148,6 +1154,13 @@ int pe_cand_limit(int64_t nb_max) {
     if (v >= 0 && v < cap) cap = (int)v;
   }
   return cap;
+}
+
+// The one-launch cut of short heads (pe_cut_small_kernel) is used unless
+// CRISP_PE_SMALL=0 asks for the general passes (both give the same results).
+bool pe_small_enabled() {
+  const char* e = std::getenv("CRISP_PE_SMALL");
+  return !(e && e[0] == '0');
 }
 
 static_assert(pe_shift(2) == 0 && pe_shift(1) == pe_width(2), "the last pass buckets the low bits under a 22-bit prefix");
@@ -1283,6 +1296,112 @@ __global__ __launch_bounds__(256) void pe_eq_scan_kernel(const PeCut* __restrict
   int tot;
   int base = block_excl_scan(s, sh, &tot);
   for (int k = a; k < b; ++k) { const int v = e[k]; e[k] = base; base += v; }
+}
+
+// The whole gamma cut of one short Pooled-Estimation head in one work-group
+// (N_b <= PE_SMALL_NB, so at most PE_SMALL_ENT entries): the row normalisers,
+// the probabilities (kept in LDS), the three radix passes with their
+// histograms in LDS and the same bucket walks (pe_scan_wave), then each row's
+// count of entries above the cut value and of entries equal to it, and the
+// flat-order scan of the latter when the cut splits a run of equal values.
+// Every histogram is an integer sum and every other step the same code as the
+// flat passes, the last pass, pe_count and pe_eq_scan use, so the cut state,
+// counts, eqrow, pnorm and pe_prob are bitwise those of that path; it replaces
+// eight launches that are mostly start-up at these sizes.
+constexpr int PE_SMALL_NB = 64;
+constexpr int PE_SMALL_ENT = PE_SMALL_NB * (PE_SMALL_NB + 1) / 2;
+__global__ __launch_bounds__(1024) void pe_cut_small_kernel(const int32_t* __restrict__ route,
+                                                            const float* __restrict__ P,
+                                                            const float2* __restrict__ part, float2* __restrict__ pnorm,
+                                                            float* __restrict__ pe_prob, PeCut* __restrict__ cut,
+                                                            int32_t* __restrict__ eqrow, int32_t* __restrict__ counts,
+                                                            const SeqList seqs, int hq, int hkv, int nseg,
+                                                            float gamma) {
+  __shared__ uint32_t sx[PE_SMALL_ENT];
+  __shared__ uint32_t hc[PE_BUCKETS];
+  __shared__ __attribute__((aligned(16))) unsigned long long hm[PE_BUCKETS];
+  __shared__ float2 sn[PE_SMALL_NB];
+  __shared__ int seq_row[PE_SMALL_NB];
+  __shared__ PeCut sc;
+  __shared__ int s_ncand;
+  const int vh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (route[vh] != 0) return;
+  const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
+  const int nb = sp.nb, total = tri32(nb);
+  const int64_t hrow = sp.rows + (int64_t)(vh % hq) * nb;   // packed index of the head's row 0
+  const float* Ph = P + sp.tri + (int64_t)(vh % hq) * total;
+  float* Oh = pe_prob ? pe_prob + sp.tri + (int64_t)(vh % hq) * total : nullptr;
+  if (tid < nb) {
+    const float2 nrm = pe_row_norm(part + (hrow + tid) * nseg, tid, pe_seg(nb));
+    sn[tid] = nrm;
+    pnorm[hrow + tid] = nrm;
+  }
+  __syncthreads();
+  for (int e = tid; e < total; e += 1024) {
+    const uint32_t x = pe_p(Ph[e], sn[tri_row(e)]);
+    sx[e] = x;
+    if (Oh) Oh[e] = __uint_as_float(x);
+  }
+  PeCut c = cut[vh];   // as pool_q reset it
+  if (!c.active) return;   // uniform over the work-group
+  if (tid == 0) s_ncand = 0;
+  auto pass = [&](auto pc) {
+    constexpr int PASS = decltype(pc)::value;
+    constexpr int shift = pe_shift(PASS), width = pe_width(PASS), hi = shift + width;
+    constexpr uint32_t mask = (1u << width) - 1;
+    for (int i = tid; i < PE_BUCKETS; i += 1024) { hc[i] = 0; hm[i] = 0; }
+    __syncthreads();
+    int nm = 0;
+    for (int e = tid; e < total; e += 1024) {
+      const uint32_t x = sx[e];
+      if (PASS > 0 && (x >> hi) != (c.prefix >> hi)) continue;
+      const uint32_t b = (x >> shift) & mask;
+      atomicAdd(&hc[b], 1u);
+      atomicAdd(&hm[b], fx_mass(x));
+      ++nm;
+    }
+    if (PASS == 2 && nm) atomicAdd(&s_ncand, nm);
+    __syncthreads();
+    if (w == 0) {
+      pe_scan_wave<PASS>(c, hc, hm, gamma, lane);
+      if (lane == 0) sc = c;
+    }
+    __syncthreads();
+    c = sc;
+  };
+  pass(std::integral_constant<int, 0>{});
+  pass(std::integral_constant<int, 1>{});
+  pass(std::integral_constant<int, 2>{});
+  // per row: entries above the cut value and entries equal to it (a row holds
+  // at most 64 entries: one wave per row, one entry per lane)
+  for (int r = w; r < nb; r += 16) {
+    const bool valid = lane <= r;
+    const uint32_t x = valid ? sx[tri32(r) + lane] : 0u;
+    const int gt = __popcll(__ballot(valid && x > c.vstar));
+    const int eq = __popcll(__ballot(valid && x == c.vstar));
+    if (lane == 0) {
+      counts[hrow + r] = gt;
+      seq_row[r] = eq;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {   // eqrow: the row's equal count, or its exclusive flat-order scan when the cut splits the run
+    const int e = lane < nb ? seq_row[lane] : 0;
+    int v = e;
+    if (c.take < c.eq_cnt) {
+      int incl = e;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      v = incl - e;
+    }
+    if (lane < nb) eqrow[hrow + lane] = v;
+    if (lane == 0) {
+      c.ncand = s_ncand;
+      cut[vh] = c;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ lists
@@ -1595,23 +1714,28 @@ hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_ma
   pe_logits_kernel<<<std::min(pe_items, 2 * device_cu_count()), 256, 0, s>>>(
       b.qbar, b.kbar, b.route, b.P, (float2*)b.pepart, seqs, hq, hkv, nseg, 1.f / sqrtf((float)HD), b.peq, vh,
       pe_items);
-  // slice of the flat passes: PE_SLICE entries, fewer where the grid would not fill the device
-  int slice = PE_SLICE;
-  while (slice > 1024 && ((total_max + slice - 1) / slice) * vh < 2 * device_cu_count()) slice /= 2;
-  const dim3 gh((unsigned)((total_max + slice - 1) / slice), vh);
-  pe_flat_pass_kernel<0><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, b.pe_prob, cut,
-                                            b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
-  pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_flat_pass_kernel<1><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, nullptr, cut,
-                                            b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
-  pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  const int cap = pe_cand_limit(nb_max);
-  pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
-                                                                  (uint2*)b.cand, cap, seqs, hq, hkv);
-  pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
-  pe_count_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, (const uint2*)b.cand, cap, b.eqrow,
-                                               b.counts, seqs, hq, hkv);
-  pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
+  if (nb_max <= PE_SMALL_NB && pe_small_enabled()) {   // every sequence short: the whole cut in one launch
+    pe_cut_small_kernel<<<vh, 1024, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, b.pe_prob, cut,
+                                            b.eqrow, b.counts, seqs, hq, hkv, nseg, gamma);
+  } else {
+    // slice of the flat passes: PE_SLICE entries, fewer where the grid would not fill the device
+    int slice = PE_SLICE;
+    while (slice > 1024 && ((total_max + slice - 1) / slice) * vh < 2 * device_cu_count()) slice /= 2;
+    const dim3 gh((unsigned)((total_max + slice - 1) / slice), vh);
+    pe_flat_pass_kernel<0><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, b.pe_prob, cut,
+                                              b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
+    pe_scan_kernel<0><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    pe_flat_pass_kernel<1><<<gh, 256, 0, s>>>(b.route, b.P, (const float2*)b.pepart, (float2*)b.pnorm, nullptr, cut,
+                                              b.hcnt, b.hmass, seqs, hq, hkv, nseg, slice);
+    pe_scan_kernel<1><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    const int cap = pe_cand_limit(nb_max);
+    pe_last_pass_kernel<<<dim3((nb_max + 3) / 4, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, b.hcnt, b.hmass, b.eqrow, b.counts,
+                                                                    (uint2*)b.cand, cap, seqs, hq, hkv);
+    pe_scan_kernel<2><<<vh, 64, 0, s>>>(cut, b.hcnt, b.hmass, gamma);
+    pe_count_kernel<<<dim3(64, vh), 256, 0, s>>>(b.P, (const float2*)b.pnorm, cut, (const uint2*)b.cand, cap, b.eqrow,
+                                                 b.counts, seqs, hq, hkv);
+    pe_eq_scan_kernel<<<vh, 256, 0, s>>>(cut, b.eqrow, seqs, hq, hkv);
+  }
   const dim3 gl((nb_max + 3) / 4, vh);
   const size_t bm_bytes = 4 * ((nb_max + 31) / 32) * sizeof(uint32_t);
   list_kernel<false><<<gl, 256, bm_bytes, s>>>(b.route, b.sv, b.nv, b.ss, b.ns, b.P, (const float2*)b.pnorm, cut,

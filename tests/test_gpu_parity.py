@@ -271,13 +271,16 @@ def test_parameter_sweep_and_min_blocks():
 
 @pytest.mark.parametrize("case", ["llama", "zero_q"])
 def test_pe_cut_candidates_equal_full_read(case):
-    """The last radix pass counts each Pooled-Estimation row's entries above and
-    at the cut value from the few entries that share the cut's top 22 bits; a
-    head with more of them than the buffer holds reads its rows in full
-    instead.  CRISP_PE_CAND_CAP=0 sends every head to the full read: the
-    selection must be bitwise the same.  With Q = 0 every pooled row is uniform
-    (p = 1/(qb+1)), so the cut falls inside a run of equal values and only part
-    of it is taken (the flat-order tie rule)."""
+    """Three ways to the same gamma cut of the 64-block layer.  By default a
+    head of at most 64 blocks takes the whole cut in one work-group (LDS
+    histograms).  CRISP_PE_SMALL=0 sends it through the general passes, whose
+    last radix pass counts each row's entries above and at the cut value from
+    the few entries that share the cut's top 22 bits; with CRISP_PE_CAND_CAP=0
+    as well every head reads its rows in full instead.  The selection, the
+    pooled probabilities and the cut must be bitwise the same all three ways.
+    With Q = 0 every pooled row is uniform (p = 1/(qb+1)), so the cut falls
+    inside a run of equal values and only part of it is taken (the flat-order
+    tie rule)."""
     cfg = synth.custom_config("candcap", 8192, 8, 2, seed=51, conc_frac=0.5)
     spec = synth.make_spec(cfg)
     Q, K, V = synth.generate(spec)
@@ -285,23 +288,35 @@ def test_pe_cut_candidates_equal_full_read(case):
         Q[:] = 0
     q, k = P.to_device(spec, Q), P.to_device(spec, K)
     p = P.params_of(cfg, tau=2.0) if case == "zero_q" else P.params_of(cfg)   # tau 2: every head pooled
-    a = dsp.crisp_select(q, k, p, pe_prob=True)
-    torch.cuda.synchronize()
-    os.environ["CRISP_PE_CAND_CAP"] = "0"
-    try:
-        b = dsp.crisp_select(q, k, p, pe_prob=True)
-        torch.cuda.synchronize()
-    finally:
-        del os.environ["CRISP_PE_CAND_CAP"]
+
+    def select_with(env):
+        old = {key: os.environ.get(key) for key in env}
+        os.environ.update(env)
+        try:
+            sel = dsp.crisp_select(q, k, p, pe_prob=True)
+            torch.cuda.synchronize()
+        finally:
+            for key, v in old.items():
+                if v is None:
+                    del os.environ[key]
+                else:
+                    os.environ[key] = v
+        return sel
+
+    a = select_with({})
     route = a.route.cpu().numpy()
     P.log(f"[cand {case}] routes VS={int((route == 1).sum())} PE={int((route == 0).sum())}")
     assert (route == 0).any()
     if case == "zero_q":
         assert (route == 0).all()
-    for f in ("route", "c_struct", "row_ptr", "nv", "ns"):
-        assert torch.equal(getattr(a, f), getattr(b, f)), f
     n = int(a.row_ptr[-1])
-    assert torch.equal(a.col_idx[:n], b.col_idx[:n])
+    pe = np.repeat(route == 0, cfg.nb * (cfg.nb + 1) // 2)
+    for env in ({"CRISP_PE_SMALL": "0"}, {"CRISP_PE_SMALL": "0", "CRISP_PE_CAND_CAP": "0"}):
+        b = select_with(env)
+        for f in ("route", "c_struct", "row_ptr", "nv", "ns"):
+            assert torch.equal(getattr(a, f), getattr(b, f)), (env, f)
+        assert torch.equal(a.col_idx[:n], b.col_idx[:n]), env
+        assert np.array_equal(a.pe_prob.cpu().numpy()[pe], b.pe_prob.cpu().numpy()[pe]), env
     rep = P.check_decisions(a, cfg.hq, cfg.nb, p, name=f"candcap {case}")
     P.log(f"[cand {case}]", rep)
     assert rep["heads_checked"] + rep["pe_exempt"] + rep["vs_exempt"] + rep["route_ties"] == cfg.hq
