@@ -176,7 +176,12 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   const int chunk = blockIdx.x / (hkv * npg), rem = blockIdx.x % (hkv * npg);
   const int kvh = rem % hkv, hp = rem / hkv;
   const int h0 = kvh * G + PX_HEADS * hp, nh = min(PX_HEADS, G - PX_HEADS * hp);
-  const bool kbar_wg = hp == 0;        // block means of K, once per KV head
+  // block means of K, once per KV head: with two or more work-groups per KV
+  // head the first two take alternate tiles (tile kb by work-group kb % 2), so
+  // that the pair reading each K tile does equal work, stays in step and the
+  // second read of a tile finds it in L2
+  const int kbar_ways = npg > 1 ? 2 : 1;
+  auto kbar_owner = [&](int kb) __attribute__((always_inline)) { return hp == kb % kbar_ways; };
   const bool scores = hg < nh;         // this wave has a head
   const SeqPos sp = seq_pos(seqs, blockIdx.y, hq, hkv);
   const int nb = sp.nb;
@@ -254,12 +259,11 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
     // tile's copy is issued: the wait at the start of the next tile (which
     // counts stores too) then finds the store long completed
     if (pend_kb >= 0 && g == 0) ts[(int64_t)pend_kb * BLK + qrow] = pend;
-    if (kbar_wg) {
-      if (kb > kb0) kbar_final(kb - 1, par ^ 1);   // the last tile's partials were written before the barrier
-      if (hg == 1) {
-        kbar_partials(cur, par, 2 * wq);
-        kbar_partials(cur, par, 2 * wq + 1);
-      }
+    // the last tile's partials were written before the barrier
+    if (kb > kb0 && kbar_owner(kb - 1)) kbar_final(kb - 1, par ^ 1);
+    if (hg == 1 && kbar_owner(kb)) {
+      kbar_partials(cur, par, 2 * wq);
+      kbar_partials(cur, par, 2 * wq + 1);
     }
     if (!scores) return;
     const bool last = kb == nb - 1;
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(PX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4
   if (pend_kb >= 0 && g == 0) ts[(int64_t)pend_kb * BLK + qrow] = pend;
   if (scores && g == 0)
     stats[(((int64_t)blockIdx.y * hq + h0 + hg) * nchunk + chunk) * BLK + qrow] = make_float2(rM, rL);
-  if (kbar_wg) {
+  if (kbar_owner(kb1 - 1)) {
     __builtin_amdgcn_s_waitcnt(0);
     px_barrier();
     kbar_final(kb1 - 1, (kb1 - 1 - kb0) & 1);
