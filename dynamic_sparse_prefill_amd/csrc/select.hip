@@ -802,11 +802,13 @@ __device__ __forceinline__ void pe_logits_item(bf16 (&kt)[2][3][32 * KT_PITCH], 
 }
 
 // Persistent: gridDim.x work-groups (two per CU) take items from *queue
-// (zeroed by pool_q) until none is left.  Item it: virtual head it % nvh
+// (zeroed by pool_q) until none is left.  Item it: query head of the KV group
 // fastest, then segment, then row group from the top of the triangle (the
-// longest rows first); items of other routes or past a triangle are skipped.
-// The row groups of one head differ in work up to 8x, so a fixed grid left
-// whole XCDs idle at the end.
+// longest rows first), then the (virtual) KV group: the whole device works on
+// one KV group's K-bar (2 MB at 4096 blocks) at a time, which each XCD's L2
+// holds, instead of streaming every group's; items of other routes or past a
+// triangle are skipped.  The row groups of one head differ in work up to 8x,
+// so a fixed grid left whole XCDs idle at the end.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pe_logits_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, const int32_t* __restrict__ route,
     float* __restrict__ P, float2* __restrict__ part, const SeqList seqs, int hq, int hkv, int nseg, float scale,
@@ -820,9 +822,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int it = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item's indices stay scalar
     __syncthreads();   // read by every thread before the next item is fetched
     if (it >= nitems) break;
-    const int vh = it % nvh, rest = it / nvh;
+    const int G = hq / hkv, per = nitems / (nvh / G);   // items of one virtual KV group
+    const int rest = it % per, vh = (it / per) * G + rest % G;
     if (route[vh] != 0) continue;
-    pe_logits_item(kt, tileT, qbar, kbar, P, part, seqs, hq, hkv, nseg, scale, vh, rest / nseg, rest % nseg);
+    pe_logits_item(kt, tileT, qbar, kbar, P, part, seqs, hq, hkv, nseg, scale, vh, rest / (G * nseg),
+                   (rest / G) % nseg);
   }
 }
 
