@@ -272,6 +272,12 @@ SeqTable single_sequence(int nb, int hkv) {
   return t;
 }
 
+// A single sequence on the dense path (below the length gate, or N_b <= 2):
+// its selection is every causal block, so the prefill runs the dense kernel,
+// which gives the same output as the sparse kernel on those lists without
+// reading them.
+bool gated_dense(const crisp_shape* s, const crisp_params* p) { return seq_dense((int)(s->n / BLK), p->dense_below_n); }
+
 // vt_ready: the proxy launch of the same prefill has already re-laid out V
 // (prefill_vt_job) and cleared the work counters.
 int run_attn(const crisp_shape* s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
@@ -422,7 +428,8 @@ int crisp_prefill(const crisp_shape* shape, const void* q, const void* k, const 
   const VtJob vt = prefill_vt_job(shape, v, attn_ws_ptr);
   st = run_select(shape, q, k, params, sel, workspace, stream, vt);
   if (st) return st;
-  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, attn_ws_ptr, stream, nullptr, vt.V != nullptr);
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, gated_dense(shape, params), o, attn_ws_ptr, stream,
+                  nullptr, vt.V != nullptr);
 }
 
 size_t crisp_noalloc_scratch_bytes(void) { return CRISP_NOALLOC_SCRATCH_BYTES; }
@@ -444,8 +451,8 @@ int crisp_prefill_noalloc(const crisp_shape* shape, const void* q, const void* k
   const VtJob vt = prefill_vt_job(shape, v, (char*)ws + sel_bytes);
   st = run_select(shape, q, k, params, sel, ws, stream, vt);
   if (st) return st;
-  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, false, o, (char*)ws + sel_bytes, stream, nullptr,
-                  vt.V != nullptr);
+  return run_attn(shape, q, k, v, sel->row_ptr, sel->col_idx, gated_dense(shape, params), o, (char*)ws + sel_bytes,
+                  stream, nullptr, vt.V != nullptr);
 }
 
 int64_t crisp_varlen_col_capacity(const crisp_shape* shape, int32_t nseq, const int64_t* cu_seqlens) {
