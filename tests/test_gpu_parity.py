@@ -841,6 +841,56 @@ def test_varlen_fp32_and_gqa7():
             col0 += hq * nb * (nb + 1) // 2
 
 
+def test_pe_cut_small_varlen_equals_general():
+    """A packed batch of short sequences (13, 3, 64 and 1 blocks, every one at
+    most 64 blocks, so the gamma cut of each Pooled-Estimation head is taken in
+    one work-group) against the general radix passes (CRISP_PE_SMALL=0): the
+    whole selection, the pooled probabilities and the outputs are bitwise the
+    same.  The second sequence has Q = 0, so its pooled rows are uniform and
+    the cut splits a run of equal values."""
+    lens = [1664, 384, 8192, 128]
+    hq, hkv = 4, 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    parts = []
+    for i, n in enumerate(lens):
+        cfg = synth.custom_config(f"pesmall{i}", n, hq, hkv, seed=90 + i, conc_frac=0.25)
+        spec = synth.make_spec(cfg)
+        Q, K, V = synth.generate(spec)
+        if i == 1:
+            Q[:] = 0
+        parts.append((spec, Q, K, V))
+    spec0 = parts[0][0]
+    q = P.to_device(spec0, np.concatenate([p[1] for p in parts], axis=1))
+    k = P.to_device(spec0, np.concatenate([p[2] for p in parts], axis=1))
+    v = P.to_device(spec0, np.concatenate([p[3] for p in parts], axis=1))
+    params = P.params_of(spec0.cfg, tau=0.9)   # most heads pooled (uniform Q: C_struct = 256 / 384)
+    o, sel = dsp.crisp_prefill_varlen(q, k, v, cu, params, pe_prob=True)
+    torch.cuda.synchronize()
+    os.environ["CRISP_PE_SMALL"] = "0"
+    try:
+        o2, sel2 = dsp.crisp_prefill_varlen(q, k, v, cu, params, pe_prob=True)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["CRISP_PE_SMALL"]
+    route = sel.route.cpu().numpy()
+    P.log(f"[pe small varlen] routes {route.tolist()}")
+    assert (route == 0).sum() >= 4
+    for f in ("route", "c_struct", "row_ptr", "nv", "ns"):
+        assert torch.equal(getattr(sel, f), getattr(sel2, f)), f
+    n = int(sel.row_ptr[-1])
+    assert torch.equal(sel.col_idx[:n], sel2.col_idx[:n])
+    off = 0   # pooled probabilities of the Pooled-Estimation heads, sequence by sequence
+    for i, ln in enumerate(lens):
+        nb = ln // 128
+        tri = nb * (nb + 1) // 2
+        for h in range(hq):
+            if route[i * hq + h] == 0:
+                a, b = off + h * tri, off + (h + 1) * tri
+                assert torch.equal(sel.pe_prob[a:b], sel2.pe_prob[a:b]), (i, h)
+        off += hq * tri
+    assert torch.equal(o, o2)
+
+
 def test_varlen_multi_tile_row_scan():
     """A packed batch whose sequences need different numbers of 4096-row tiles
     in the row-pointer scan (hq * N_b = 4608, 160 and 2560 rows) and different
