@@ -237,7 +237,7 @@ int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_p
   b.router = (p->flags & CRISP_FLAG_ROUTE_JSD) ? 1 : 0;
   b.vs_budget = (p->flags & CRISP_FLAG_VS_MEDIAN) ? 1 : ((p->flags & CRISP_FLAG_VS_COVERAGE) ? 2 : 0);
   return status_of(launch_select(fp32, q, seqs, nb_max, s->hq, s->hkv, st, p->sink, p->local, p->tau, p->alpha,
-                                 p->gamma, p->min_blocks, p->dense_below_n, b, stream));
+                                 p->gamma, p->min_blocks, p->dense_below_n, b, vt, stream));
 }
 int run_select(const crisp_shape* s, const void* q, const void* k, const crisp_params* p, crisp_selection* out,
                void* ws, hipStream_t stream, const VtJob& vt = VtJob{}) {

@@ -145,9 +145,11 @@ struct SelectBufs {
   int router, vs_budget;
 };
 
-// nb_max: the longest sequence's N_b (grid extents, per-head scratch sizes)
+// nb_max: the longest sequence's N_b (grid extents, per-head scratch sizes).
+// vt: the V re-layout of a bf16 prefill, done here when every sequence is on
+// the dense path (the proxy launch, which does it otherwise, is then skipped).
 hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_max, int hq, int hkv,
                          const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
-                         int min_blocks, int dense_below_n, const SelectBufs& b, hipStream_t s);
+                         int min_blocks, int dense_below_n, const SelectBufs& b, const VtJob& vt, hipStream_t s);
 
 }  // namespace crisp

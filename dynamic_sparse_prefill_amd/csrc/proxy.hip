@@ -569,14 +569,15 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
   const int groups = hkv * ((G + hpw - 1) / hpw);
   const int chunks1 = proxy_chunks1(fp32, hq, hkv);
   const int nchunk = proxy_chunks(fp32, seqs, hq, hkv);
-  // every sequence on the dense path (below the length gate, or N_b <= 2):
-  // no scores are needed, only the V re-layout of a bf16 prefill
+  // every sequence on the dense path (below the length gate, or N_b <= 2): no
+  // scores are needed, and the selection launch does the V re-layout of a
+  // bf16 prefill beside writing the full lists
   bool all_dense = true;
   for (int i = 0; i < nseq; ++i) all_dense = all_dense && seq_dense(seqs.nb[i], dense_below_n);
-  const int nscore = all_dense ? 0 : nchunk * groups;
+  if (all_dense) return hipSuccess;
+  const int nscore = nchunk * groups;
   const dim3 grid((unsigned)nscore, (unsigned)nseq);
   if (fp32) {
-    if (all_dense) return hipSuccess;
     proxy_tiles_f32_kernel<<<grid, 256, 0, s>>>((const float*)Q, (const float*)K, (float4*)tstat, kbar,
                                                  (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h, st.k_n, w_sink,
                                                  w_local, dense_below_n, sl2, chunks1, nchunk);
@@ -585,12 +586,10 @@ hipError_t launch_proxy(int fp32, const void* Q, const void* K, const SeqList& s
     // the V re-layout's work-groups (two tiles each) spread over the grid's rows
     const int64_t vt_wgs = vt.V ? ((int64_t)vt.nb * hkv + 1) / 2 : 0;
     const dim3 g2((unsigned)(nscore + (vt_wgs + nseq - 1) / nseq), (unsigned)nseq);
-    if (g2.x > 0)
-      proxy_scores_bf16_kernel<<<g2, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
-                                                            (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
-                                                            st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
-                                                            nchunk, nscore, vt);
-    if (all_dense) return hipGetLastError();
+    proxy_scores_bf16_kernel<<<g2, PX_WAVES * 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (float4*)tstat, kbar,
+                                                          (float2*)stats, seqs, hq, hkv, st.q_h, st.q_n, st.k_h,
+                                                          st.k_n, w_sink, w_local, dense_below_n, sl2, chunks1,
+                                                          nchunk, nscore, vt);
   }
   const unsigned vheads = (unsigned)(nseq * hq);
   proxy_combine_kernel<<<vheads, BLK * CMB_GROUPS, 0, s>>>((const float2*)stats, (float2*)rowstat, seqs, hq, nchunk,

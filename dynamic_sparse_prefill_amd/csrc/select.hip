@@ -43,6 +43,7 @@
 #include "common.h"
 #include "lanes.h"
 #include "launch.h"
+#include "vt.h"
 
 namespace crisp {
 
@@ -1639,13 +1640,24 @@ __global__ void copy_sets_kernel(const int32_t* __restrict__ sv, const int32_t* 
 // sequence's CSR has the closed form h * N_b(N_b+1)/2 + qb(qb+1)/2.  Work-group
 // (0, vh) also writes the head's route (-1), C_struct (0), empty direction sets
 // and, when the JSD router is on, a zero divergence: what the general kernels
-// write for a dense sequence.
+// write for a dense sequence.  In a bf16 prefill the work-groups past the
+// first nrow_x columns of the grid re-lay V out for the attention, one tile
+// each (vt.h), and the first of them clears the attention's work counters.
 __global__ __launch_bounds__(256) void dense_selection_kernel(int32_t* __restrict__ route, float* __restrict__ c_struct,
                                                               int32_t* __restrict__ nv, int32_t* __restrict__ ns,
                                                               int32_t* nv_out, int32_t* ns_out, double* jsd,
                                                               int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
-                                                              const SeqList seqs, int hq, int hkv) {
+                                                              const SeqList seqs, int hq, int hkv, int nrow_x,
+                                                              VtJob vt) {
   const int qb = blockIdx.x, vh = blockIdx.y, tid = threadIdx.x;
+  if (qb >= nrow_x) {   // the V re-layout, numbered row after row of the grid
+    const int64_t tile = (int64_t)blockIdx.y * (gridDim.x - nrow_x) + (qb - nrow_x);   // tile = g * nb + kb
+    if (tile == 0 && tid < ATTN_QUEUE_INTS) vt.queue[tid] = 0;
+    if (tile < (int64_t)hkv * vt.nb)
+      vt_tile_bf16((const bf16*)vt.V, (bf16*)vt.Vt, vt.sv_h, vt.sv_n, vt.nb, (int)(tile % vt.nb), (int)(tile / vt.nb),
+                   tid);
+    return;
+  }
   const SeqPos sp = seq_pos(seqs, vh / hq, hq, hkv);
   const int nb = sp.nb, hl = vh % hq;
   if (qb == 0 && tid == 0) {
@@ -1671,15 +1683,17 @@ __global__ __launch_bounds__(256) void dense_selection_kernel(int32_t* __restric
 
 hipError_t launch_select(int fp32, const void* Q, const SeqList& seqs, int nb_max, int hq, int hkv,
                          const Strides& st, int w_sink, int w_local, float tau, float alpha, float gamma,
-                         int min_blocks, int dense_below_n, const SelectBufs& b, hipStream_t s) {
+                         int min_blocks, int dense_below_n, const SelectBufs& b, const VtJob& vt, hipStream_t s) {
   const unsigned vh = (unsigned)(seqs.nseq * hq);   // virtual heads: (sequence, query head)
   const bool jsd_on = b.router == 1;
   bool all_dense = true;
   for (int i = 0; i < seqs.nseq; ++i) all_dense = all_dense && seq_dense(seqs.nb[i], dense_below_n);
   if (all_dense) {
-    dense_selection_kernel<<<dim3(nb_max, vh), 256, 0, s>>>(b.route, b.c_struct, b.nv, b.ns, b.nv_out, b.ns_out,
-                                                            jsd_on ? b.jsd : nullptr, b.row_ptr, b.col_idx, seqs,
-                                                            hq, hkv);
+    const int64_t vt_tiles = (fp32 || !vt.V) ? 0 : (int64_t)hkv * vt.nb;
+    const dim3 g((unsigned)(nb_max + (vt_tiles + vh - 1) / vh), vh);
+    dense_selection_kernel<<<g, 256, 0, s>>>(b.route, b.c_struct, b.nv, b.ns, b.nv_out, b.ns_out,
+                                             jsd_on ? b.jsd : nullptr, b.row_ptr, b.col_idx, seqs, hq, hkv, nb_max,
+                                             vt);
     return hipGetLastError();
   }
   if (jsd_on) {
