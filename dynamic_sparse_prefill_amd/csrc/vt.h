@@ -1,6 +1,8 @@
 // Re-layout of V into per-block transposed tiles for the attention kernels'
 // O^T += V^T P^T products (bf16 and fp32), shared by the stand-alone re-layout
-// kernel and the proxy launch of a prefill (which does it beside the selection).
+// kernel, the proxy launch of a prefill (which does it beside the selection)
+// and the dense selection launch (a prefill with every sequence below the
+// length gate).
 //
 // V [hkv][n][d] (token stride sv_n, head stride sv_h) -> Vt [hkv][N_b][d][128]:
 // row d of tile (g, kb) holds V[g][128 kb + key][d] for the block's 128 keys.
