@@ -160,7 +160,10 @@ int crisp_dense_attn(const crisp_shape *shape, const void *q, const void *k, con
                      void *o, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* All four stages: crisp_select then crisp_sparse_attn, enqueued back to back
- * on `stream` with no host round trip.  `sel` receives the selection. */
+ * on `stream` with no host round trip.  `sel` receives the selection.  When
+ * the sequence is on the dense path (see crisp_select) the attention is
+ * crisp_dense_attn's kernel: the same output as crisp_sparse_attn on the full
+ * lists, bit for bit, without reading them. */
 int crisp_prefill(const crisp_shape *shape, const void *q, const void *k, const void *v,
                   const crisp_params *params, crisp_selection *sel, void *o,
                   void *workspace, size_t workspace_bytes, hipStream_t stream);
